@@ -1,15 +1,40 @@
 #!/usr/bin/env python3
-"""Benchmark of the dense linear-layer GEMM on one MI355X.
+"""Benchmark of the dense linear-layer GEMM C = A * B^T on one MI355X.
 
-Placeholder: formulas only (the timed driver is added with the GPU path).
+Default workload: bf16 M = N = K = 4096 (A, B ~ N(0, 0.02^2), B stored [N, K]
+and preshuffled once).  A step is one GEMM call through the C ABI with the
+tile chosen by select_tile; the preshuffle is a once-per-weight cost timed
+separately.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Measurement:
+  * W untimed warm-up calls, then exactly K calls bracketed by
+    torch.cuda.synchronize() on both sides, timed with HIP events on the
+    stream the kernels run on (torch's current stream).  Each call also gets
+    its own event pair, so the average kernel duration is measured live.
+  * The K calls rotate over enough copies of (A, Bs, C) to exceed twice the
+    256 MB Infinity Cache, so every call reads its operands from HBM.
+  * `roofline`: algorithmic flops (2MNK, "GEMM Optimization Guide" page,
+    section 8.1) or bytes per launch over the average kernel duration,
+    against MI355X's published dense peak or HBM bandwidth.
+  * `cpu_baseline`: the oracle (plain C fp64 triple loop) on a bounded sample
+    of the same workload -- whole rows of C -- timed on the host cores.
 """
 from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
 
 # --------------------------------------------------------------- formulas
 # Dense peaks and HBM bandwidth of one MI355X (AMD's published figures; dense,
 # no sparsity): 256 CUs at 2.4 GHz.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
 
 
 def flops(M: int, N: int, K: int) -> float:
@@ -43,3 +68,264 @@ def roofline_us(M: int, N: int, K: int, dtype: str) -> float:
     t_c = flops(M, N, K) / (PEAK_TFLOPS[dtype] * 1e12)
     t_m = alg_bytes(M, N, K, dtype) / (PEAK_HBM_GBPS * 1e9)
     return max(t_c, t_m) * 1e6
+
+
+# (M, N, K, dtype, dist A, sigma A, dist B, sigma B, seed config)
+WORKLOADS = {
+    "bf16_4096cube": (4096, 4096, 4096, "bf16", "normal", 0.02, "normal", 0.02, 2),
+    "bf16_llama_prefill": (597, 11008, 4096, "bf16", "normal", 1.0, "normal", 0.02, 3),
+    "bf16_llama_decode": (1, 11008, 4096, "bf16", "normal", 1.0, "normal", 0.02, 3),
+    "bf16_8x4096": (8, 4096, 4096, "bf16", "normal", 1.0, "normal", 1.0, 42),
+    "bf16_48x4096": (48, 4096, 4096, "bf16", "normal", 1.0, "normal", 1.0, 43),
+    "bf16_3402x4096x1024": (3402, 4096, 1024, "bf16", "normal", 1.0, "normal", 1.0, 44),
+    "bf16_lmhead_1024x50257x512": (1024, 50257, 512, "bf16", "normal", 1.0, "normal", 1.0, 45),
+    "bf16_2048x11007x1024": (2048, 11007, 1024, "bf16", "normal", 1.0, "normal", 1.0, 46),
+    "bf16_4095x4095x1024": (4095, 4095, 1024, "bf16", "normal", 1.0, "normal", 1.0, 47),
+    "bf16_528x528x1024": (528, 528, 1024, "bf16", "normal", 1.0, "normal", 1.0, 48),
+    "fp8_4096cube": (4096, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 5),
+    "fp8_32x4096": (32, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 51),
+}
+HEADLINE = "bf16_4096cube"
+DECODE = "bf16_llama_decode"
+
+
+def bound_of(M, N, K, dtype) -> str:
+    t_c = flops(M, N, K) / (PEAK_TFLOPS[dtype] * 1e12)
+    t_m = alg_bytes(M, N, K, dtype) / (PEAK_HBM_GBPS * 1e9)
+    return "mfma" if t_c >= t_m else "hbm"
+
+
+# ------------------------------------------------------------- GPU timing
+def make_inputs(name: str):
+    import numpy as np
+    import datagen
+    M, N, K, dt, da, sa, db, sb, cfg = WORKLOADS[name]
+    if dt == "bf16":
+        A, B = datagen.make_bf16_pair(M, N, K, da, db, cfg, sa, sb)
+        return A, B, 1.0, 1.0
+    A, B, s_a, s_b = datagen.make_e4m3_pair(M, N, K, cfg)
+    return A, B, s_a, s_b
+
+
+def gpu_setup(name: str, copies: int):
+    import numpy as np
+    import torch
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    A, B, s_a, s_b = make_inputs(name)
+    if dt == "bf16":
+        Ad = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).cuda()
+        Bd = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        Ad = torch.from_numpy(A).cuda()
+        Bd = torch.from_numpy(B).cuda()
+    # preshuffle, timed on its own
+    Bs0 = dg.shuffle_b(Bd, dtype=dt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = 5
+    for _ in range(reps):
+        dg.shuffle_b(Bd, dtype=dt, out=Bs0)
+    e1.record()
+    torch.cuda.synchronize()
+    shuffle_us = e0.elapsed_time(e1) * 1e3 / reps
+    sets = []
+    for i in range(copies):
+        a = Ad if i == 0 else Ad.clone()
+        bs = Bs0 if i == 0 else Bs0.clone()
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        sets.append((a, bs, c))
+    scales = (torch.tensor([s_a], dtype=torch.float32, device="cuda"),
+              torch.tensor([s_b], dtype=torch.float32, device="cuda"))
+    del Bd
+    return sets, scales, shuffle_us
+
+
+def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True):
+    import torch
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    if copies is None:   # enough operand sets to exceed twice the Infinity Cache
+        per_set = alg_bytes(M, N, K, dt)
+        copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
+    sets, (s_a, s_b), shuffle_us = gpu_setup(name, copies)
+    tile = dg.select_tile(M, N, K, dt)
+
+    def call(i):
+        a, bs, c = sets[i % copies]
+        if dt == "bf16":
+            dg.gemm_bf16(a, bs, N, out=c)
+        else:
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)] if per_launch else []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        if per_launch:
+            ev[i][0].record(stream)
+        call(i)
+        if per_launch:
+            ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    kern_us = [s.elapsed_time(e) * 1e3 for s, e in ev] if per_launch else []
+    return {
+        "total_ms": total_ms, "wall_s": wall, "kernel_us": kern_us, "tile": tile,
+        "shuffle_us": shuffle_us, "copies": copies,
+    }
+
+
+def run_graph(name: str, reps: int, copies: int):
+    """Decode-size kernels are shorter than a Python launch: time R launches
+    captured in one HIP graph (no memset nodes: the kernels write every output
+    element themselves)."""
+    import torch
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    sets, (s_a, s_b), shuffle_us = gpu_setup(name, copies)
+
+    def call(i):
+        a, bs, c = sets[i % copies]
+        if dt == "bf16":
+            dg.gemm_bf16(a, bs, N, out=c)
+        else:
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(reps):
+                call(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / reps, shuffle_us
+
+
+# ------------------------------------------------------------ CPU oracle
+def cpu_baseline(name: str, budget_s: float = 15.0):
+    """The oracle on whole rows of C of the same workload, scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    M, N, K, dt = WORKLOADS[name][:4]
+    A, B, s_a, s_b = make_inputs(name)
+    threads = min(16, os.cpu_count() or 1)
+    rows = threads
+    while True:
+        t = time.perf_counter()
+        if dt == "bf16":
+            oracle.gemm_bf16(A[:rows], B, threads=threads)
+        else:
+            oracle.gemm_e4m3(A[:rows], B, s_a, s_b, threads=threads)
+        el = time.perf_counter() - t
+        if el >= budget_s / 4 or rows >= M:
+            break
+        rows = min(M, max(rows * 2, int(rows * budget_s / 2 / max(el, 1e-3))))
+    val = flops(rows, N, K) / el / 1e12
+    return {"value": val, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} whole rows of C ({rows}x{N}x{K}, {rows * N * K / 1e9:.2f} G multiply-adds, "
+                      f"fp64 triple loop on {threads} threads) in {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the decode measurement")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the sharded design is described, not built).", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    name = args.workload
+    M, N, K, dt = WORKLOADS[name][:4]
+    r = run_timed(name, args.steps, args.warmup)
+    ms_per_step = r["total_ms"] / args.steps
+    kern = sorted(r["kernel_us"])
+    kern_avg = sum(kern) / len(kern)
+    bound = bound_of(M, N, K, dt)
+    if bound == "mfma":
+        achieved = flops(M, N, K) / (kern_avg * 1e-6) / 1e12
+        peak, unit_r = PEAK_TFLOPS[dt], "TFLOP/s"
+    else:
+        achieved = alg_bytes(M, N, K, dt) / (kern_avg * 1e-6) / 1e9
+        peak, unit_r = PEAK_HBM_GBPS, "GB/s"
+    value = flops(M, N, K) * args.steps / (r["total_ms"] * 1e-3) / 1e12
+    tile = r["tile"]
+    out = {
+        "metric": "GEMM TFLOP/s (2MNK/t) + % MFMA peak; HBM GB/s for M<=8 decode",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "tile": tile.name,
+                   "tile_eff": round(tile.tile_eff, 4), "wq_eff": round(tile.wq_eff, 4),
+                   "operand_copies_rotated": r["copies"], "pct_of_mfma_peak": None},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_r,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_us_avg": round(kern_avg, 3), "kernel_us_median": round(kern[len(kern) // 2], 3)},
+        "shuffle_b_us": round(r["shuffle_us"], 2),
+    }
+    if bound == "mfma":
+        out["config"]["pct_of_mfma_peak"] = round(100 * value / PEAK_TFLOPS[dt], 2)
+    if not args.no_secondary and name != DECODE:
+        dM, dN, dK, ddt = WORKLOADS[DECODE][:4]
+        us_cold, _ = run_graph(DECODE, reps=60, copies=6)
+        us_hot, _ = run_graph(DECODE, reps=60, copies=1)
+        gb = alg_bytes(dM, dN, dK, ddt)
+        out["secondary"] = {
+            "workload": DECODE, "M": dM, "N": dN, "K": dK,
+            "tile": dg_tile_name(dM, dN, dK, ddt),
+            "us_cold": round(us_cold, 3), "GBps_cold": round(gb / (us_cold * 1e-6) / 1e9, 1),
+            "frac_hbm_cold": round(gb / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "us_hot_mall": round(us_hot, 3), "GBps_hot_mall": round(gb / (us_hot * 1e-6) / 1e9, 1),
+            "timing": "hipGraph of 60 launches; cold = 6 rotated operand copies (541 MB)",
+        }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(name)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def dg_tile_name(M, N, K, dt):
+    import dense_gemm_linear_amd as dg
+    return dg.select_tile(M, N, K, dt).name
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,231 @@
+"""Python binding of the densegemm C ABI (``include/densegemm.h``).
+
+Argument marshalling only: tensors become device pointers, leading dimensions
+and the current HIP stream; every step of the computation runs in the HIP
+library ``libdensegemm.so``.  There is no fallback: if the library is missing
+the import of this package fails.
+
+Functions mirror the C entry points:
+
+  select_tile(M, N, K, dtype="bf16", num_cus=0) -> Tile
+  shuffle_b_bytes(N, K, dtype="bf16") -> int
+  shuffle_b(B, dtype=None, out=None) -> Bs (uint8 device tensor)
+  gemm_bf16(A, Bs, N, out=None, tile=None) -> C
+  gemm_fp8_scaled(A, Bs, N, scale_a, scale_b, out=None, tile=None) -> C
+  gemm_status_string(code) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdensegemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_VALUE = 1
+GEMM_ERR_UNSUPPORTED = 2
+GEMM_ERR_HIP = 3
+
+GEMM_BF16 = 0
+GEMM_FP8_E4M3 = 1
+
+GEMM_KERNEL_TILED = 0
+GEMM_KERNEL_SKINNY = 1
+
+EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
+           "gemm_status_string")
+
+
+class GemmTile(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("atom", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("k_split", ctypes.c_int32), ("lds_stages", ctypes.c_int32),
+                ("tile_eff", ctypes.c_float), ("wq_eff", ctypes.c_float),
+                ("predicted_us", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class Tile:
+    kernel: int
+    tile_m: int
+    tile_n: int
+    tile_k: int = 0
+    atom: int = 16
+    waves: int = 4
+    k_split: int = 1
+    lds_stages: int = 2
+    tile_eff: float = 0.0
+    wq_eff: float = 0.0
+    predicted_us: float = 0.0
+
+    @property
+    def name(self) -> str:
+        kind = "tiled" if self.kernel == GEMM_KERNEL_TILED else "skinny"
+        return f"{kind}{self.tile_m}x{self.tile_n}"
+
+    def to_c(self) -> GemmTile:
+        return GemmTile(self.kernel, self.tile_m, self.tile_n, self.tile_k, self.atom, self.waves,
+                        self.k_split, self.lds_stages, self.tile_eff, self.wq_eff, self.predicted_us)
+
+    @staticmethod
+    def from_c(t: GemmTile) -> "Tile":
+        return Tile(t.kernel, t.tile_m, t.tile_n, t.tile_k, t.atom, t.waves, t.k_split,
+                    t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
+
+
+def tiled(tm: int, tn: int) -> Tile:
+    return Tile(GEMM_KERNEL_TILED, tm, tn)
+
+
+def skinny(tm: int, tn: int) -> Tile:
+    return Tile(GEMM_KERNEL_SKINNY, tm, tn, k_split=4, lds_stages=0)
+
+
+TILED_LADDER = [(m, n) for m in (256, 128, 64, 32) for n in (256, 128, 64)]
+SKINNY_LADDER = [(m, n) for m in (16, 32, 48, 64) for n in (16, 32, 64)]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {gemm_status_string(code)}")
+        self.code = code
+
+
+def _load_lib():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g;"
+                          f" g.build()'` (hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.select_tile.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int32, ctypes.POINTER(GemmTile)]
+    lib.select_tile.restype = ctypes.c_int
+    lib.shuffle_b_bytes.argtypes = [I64, I64, ctypes.c_int]
+    lib.shuffle_b_bytes.restype = ctypes.c_size_t
+    lib.shuffle_b.argtypes = [P, I64, P, I64, I64, ctypes.c_int, P]
+    lib.shuffle_b.restype = ctypes.c_int
+    lib.gemm_bf16.argtypes = [P, I64, P, P, I64, I64, I64, I64, ctypes.POINTER(GemmTile), P]
+    lib.gemm_bf16.restype = ctypes.c_int
+    lib.gemm_fp8_scaled.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
+                                    ctypes.POINTER(GemmTile), P]
+    lib.gemm_fp8_scaled.restype = ctypes.c_int
+    lib.gemm_status_string.argtypes = [ctypes.c_int]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load_lib()
+
+
+def gemm_status_string(code: int) -> str:
+    return lib.gemm_status_string(int(code)).decode()
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("bf16", GEMM_BF16):
+        return GEMM_BF16
+    if dtype in ("fp8", "e4m3", GEMM_FP8_E4M3):
+        return GEMM_FP8_E4M3
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def select_tile(M: int, N: int, K: int, dtype="bf16", num_cus: int = 0) -> Tile:
+    t = GemmTile()
+    st = lib.select_tile(M, N, K, _dtype_code(dtype), num_cus, ctypes.byref(t))
+    if st != GEMM_OK:
+        raise GemmError("select_tile", st)
+    return Tile.from_c(t)
+
+
+def shuffle_b_bytes(N: int, K: int, dtype="bf16") -> int:
+    return int(lib.shuffle_b_bytes(N, K, _dtype_code(dtype)))
+
+
+# ------------------------------------------------------------ torch layer
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _tensor_dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return GEMM_BF16
+    if t.dtype in (torch.uint8, torch.int8, torch.float8_e4m3fn):
+        return GEMM_FP8_E4M3
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _check_rows(name: str, t):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def shuffle_b(B, dtype=None, out=None):
+    """Preshuffle the row-major weight B [N, K] (bf16 or e4m3) into a new (or
+    the given) uint8 device tensor of shuffle_b_bytes(N, K) bytes."""
+    torch = _torch()
+    _check_rows("B", B)
+    code = _tensor_dtype_code(B) if dtype is None else _dtype_code(dtype)
+    N, K = B.shape
+    nbytes = shuffle_b_bytes(N, K, code)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=B.device)
+    elif out.numel() * out.element_size() < nbytes:
+        raise ValueError("out is too small")
+    st = lib.shuffle_b(B.data_ptr(), B.stride(0), out.data_ptr(), N, K, code, _stream_ptr(B))
+    if st != GEMM_OK:
+        raise GemmError("shuffle_b", st)
+    return out
+
+
+def _out(A, N, out):
+    torch = _torch()
+    M = A.shape[0]
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _check_rows("out", out)
+    if tuple(out.shape) != (M, N) or out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("out must be a bf16 [M, N] view")
+    return out
+
+
+def _tile_ptr(tile):
+    if tile is None:
+        return None
+    return ctypes.byref(tile.to_c())
+
+
+def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None):
+    """C[M, N] = A[M, K] * B[N, K]^T with Bs = shuffle_b(B); returns C (bf16)."""
+    _check_rows("A", A)
+    C = _out(A, N, out)
+    M, K = A.shape
+    st = lib.gemm_bf16(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0), M, N,
+                       K, _tile_ptr(tile), _stream_ptr(A))
+    if st != GEMM_OK:
+        raise GemmError("gemm_bf16", st)
+    return C
+
+
+def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None = None):
+    """C = (A * B^T) * scale_a * scale_b for e4m3 A [M, K] and Bs = shuffle_b(B);
+    scale_a / scale_b are one-element float32 device tensors."""
+    _check_rows("A", A)
+    C = _out(A, N, out)
+    M, K = A.shape
+    st = lib.gemm_fp8_scaled(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
+                             scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
+                             _tile_ptr(tile), _stream_ptr(A))
+    if st != GEMM_OK:
+        raise GemmError("gemm_fp8_scaled", st)
+    return C

@@ -1,0 +1,200 @@
+// The C ABI (include/densegemm.h): argument checks, tile choice, launches.
+#include <string.h>
+
+#include <mutex>
+
+#include "internal.hpp"
+
+namespace dg {
+
+hipError_t launch_tiled_bf16(int tm, int tn, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled_fp8(int tm, int tn, const GemmArgs& a, hipStream_t s);
+void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out);
+
+hipError_t launch_tiled(int dt, int tm, int tn, const GemmArgs& a, hipStream_t s)
+{
+    return dt == DT_BF16 ? launch_tiled_bf16(tm, tn, a, s) : launch_tiled_fp8(tm, tn, a, s);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int checked = 0;
+    int gfx950 = 0;
+    int cus = 0;
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Current device: is it gfx950, and how many CUs.  Cached per device.
+gemm_status device_info(int* cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.checked) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return GEMM_ERR_HIP;
+        d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        d.checked = 1;
+    }
+    if (!d.gfx950)
+        return GEMM_ERR_UNSUPPORTED;
+    *cus = d.cus;
+    return GEMM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Is a forced tile usable for this shape?
+bool tile_feasible(const gemm_tile& t, int64_t M)
+{
+    if (t.kernel == GEMM_KERNEL_TILED)
+        return tiled_supported(t.tile_m, t.tile_n);
+    if (t.kernel == GEMM_KERNEL_SKINNY)
+        return skinny_supported(t.tile_m, t.tile_n) && M <= t.tile_m;
+    return false;
+}
+
+gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const float* sa,
+                     const float* sb, uint16_t* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                     const gemm_tile* tile, void* stream)
+{
+    const int e = dt == DT_BF16 ? 2 : 1;
+    // ---- argument checks (no HIP call before this block ends)
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    // With K == 0 neither A, Bs nor the scales are read (empty sum).
+    if (!C || (K > 0 && (!A || !Bs || (dt == DT_FP8 && (!sa || !sb)))))
+        return GEMM_ERR_INVALID_VALUE;
+    if (lda < K || ldc < N)
+        return GEMM_ERR_INVALID_VALUE;
+    if ((K > 0 && (!aligned16(A) || !aligned16(Bs) || (lda * e) % 16 != 0)) ||
+        ((uintptr_t)C & 1u) != 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (K % (dt == DT_BF16 ? 16 : 64) != 0)
+        return GEMM_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets: a tile of up to 256 rows of A or C, and one
+    // 16-column block of Bs, must stay below 2^31 bytes.
+    if (M > INT32_MAX || N > INT32_MAX || lda * e > (INT64_C(1) << 22) ||
+        ldc * 2 > (INT64_C(1) << 22) || K * e > (INT64_C(1) << 20))
+        return GEMM_ERR_UNSUPPORTED;
+    gemm_tile t;
+    if (tile) {
+        t = *tile;
+        if (!tile_feasible(t, M))
+            return GEMM_ERR_UNSUPPORTED;
+    }
+    // ---- device
+    int cus = 0;
+    gemm_status st = device_info(&cus);
+    if (st != GEMM_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0)
+        return launch_zero_c(C, ldc, M, N, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    if (!tile)
+        choose_tile(M, N, K, dt, cus, &t);
+    GemmArgs a;
+    memset(&a, 0, sizeof a);
+    a.A = static_cast<const uint8_t*>(A);
+    a.Bs = static_cast<const uint8_t*>(Bs);
+    a.C = C;
+    a.sa = sa;
+    a.sb = sb;
+    a.lda_b = lda * e;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.KA_b = (int)(K * e);
+    a.KB = (int)((K * e + 63) / 64);
+    a.nkt = (a.KB + 1) / 2;
+    a.tail = (a.KA_b % 128) != 0;
+    a.nblk = (int)((N + 15) / 16);
+    a.c_vec = (((uintptr_t)C & 15u) == 0) && (ldc % 8 == 0);
+    hipError_t err;
+    if (t.kernel == GEMM_KERNEL_SKINNY) {
+        err = launch_skinny(dt, t.tile_m, t.tile_n, a, s);
+    } else {
+        a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
+        a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
+        err = launch_tiled(dt, t.tile_m, t.tile_n, a, s);
+    }
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                      int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* stream)
+{
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, stream);
+}
+
+gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
+                            const float* scale_b, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                            int64_t K, const gemm_tile* tile, void* stream)
+{
+    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, stream);
+}
+
+size_t shuffle_b_bytes(int64_t N, int64_t K, gemm_dtype dtype)
+{
+    if (N < 0 || K < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return 0;
+    const int64_t e = dtype == GEMM_BF16 ? 2 : 1;
+    const int64_t kblocks = (K * e + 63) / 64;
+    return (size_t)((N + 15) / 16 * 16 * kblocks * 64);
+}
+
+gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K, gemm_dtype dtype,
+                      void* stream)
+{
+    if (N < 0 || K < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return GEMM_ERR_INVALID_VALUE;
+    if (N == 0 || K == 0)
+        return GEMM_OK;
+    if (!B || !Bs || ldb < K || !dg::aligned16(Bs))
+        return GEMM_ERR_INVALID_VALUE;
+    const int64_t e = dtype == GEMM_BF16 ? 2 : 1;
+    if (K % (dtype == GEMM_BF16 ? 16 : 64) != 0)
+        return GEMM_ERR_UNSUPPORTED;
+    int cus = 0;
+    gemm_status st = dg::device_info(&cus);
+    if (st != GEMM_OK)
+        return st;
+    const int aligned = dg::aligned16(B) && (ldb * e) % 16 == 0;
+    hipError_t err = dg::launch_shuffle_b(static_cast<const uint8_t*>(B), ldb * e,
+                                          static_cast<uint8_t*>(Bs), N, K * e, (K * e + 63) / 64,
+                                          aligned, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+const char* gemm_status_string(gemm_status status)
+{
+    switch (status) {
+    case GEMM_OK:
+        return "GEMM_OK";
+    case GEMM_ERR_INVALID_VALUE:
+        return "GEMM_ERR_INVALID_VALUE";
+    case GEMM_ERR_UNSUPPORTED:
+        return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_HIP:
+        return "GEMM_ERR_HIP";
+    }
+    return "GEMM_ERR_UNKNOWN";
+}
+
+}  // extern "C"

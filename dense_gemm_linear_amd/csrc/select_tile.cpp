@@ -1,0 +1,205 @@
+// select_tile: analytic choice of kernel and tile for an M x N x K GEMM.
+//
+// The model (pure host, deterministic):
+//   - tile quantization tile_eff = M*N / (M_pad*N_pad) and wave quantization
+//     wq_eff = tiles / (rounds * slots) as the TraceLens GEMM analysis page
+//     defines them ("Tile quantization efficiency", "Wave quantization
+//     efficiency"); the padding screen of the FlyDSL PR #1303 page rejects a
+//     tile whose padded output exceeds 1.25x the real one unless no other
+//     tile is feasible;
+//   - per-k-tile cost of a tiled workgroup = the largest of its MFMA issue
+//     time, its LDS traffic and its global-load traffic ("GEMM Optimization
+//     Guide" page, sections 1.5, 2.4, 8.3, 9.3), occupancy from the combined
+//     VGPR budget of section 10.2, LDS budget of 160 KiB per CU;
+//   - skinny (small M) candidates are priced as a stream of B at the HBM
+//     rate, derated when fewer workgroups than CUs are in flight;
+//   - the result is the candidate with the lowest predicted time; ties go to
+//     the earlier candidate in a fixed order.
+#include <math.h>
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace dg {
+
+namespace {
+
+struct Chip {
+    double clock_hz = 2.4e9;
+    double mfma_flop_per_clk_cu[2] = {4096.0, 8192.0};  // bf16, e4m3 dense
+    double lds_bytes_per_clk = 128.0;
+    double vmem_bytes_per_clk = 64.0;
+    double hbm_bytes_per_s = 8.0e12 * 0.85;              // sustained fraction
+    double cu_stream_bytes_per_clk = 48.0;               // one CU pulling from HBM
+    int lds_per_cu = 160 * 1024;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int align8(int v) { return (v + 7) / 8 * 8; }
+
+struct Cand {
+    gemm_tile t;
+    double us;
+    bool screened;  // fails the padding screen
+};
+
+void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt)
+{
+    memset(&t, 0, sizeof t);
+    t.kernel = kernel;
+    t.tile_m = tm;
+    t.tile_n = tn;
+    t.tile_k = dt == GEMM_BF16 ? 64 : 128;
+    t.atom = 16;
+    t.waves = 4;
+    t.k_split = kernel == GEMM_KERNEL_SKINNY ? 4 : 1;
+    t.lds_stages = kernel == GEMM_KERNEL_TILED ? 2 : 0;
+}
+
+bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, const Chip& c,
+                 Cand& out)
+{
+    const int lds = tiled_lds_bytes(tm, tn);
+    const int vgpr = tiled_vgpr_estimate(tm, tn);
+    if (lds < 0 || lds > c.lds_per_cu || vgpr > 512)
+        return false;
+    const int waves_per_simd = std::min(8, 512 / align8(vgpr));
+    const int occ = std::max(1, std::min(waves_per_simd, c.lds_per_cu / lds));
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    const int64_t nkt = cdiv(K * e, 128);
+    const int64_t tiles_m = cdiv(M, tm), tiles_n = cdiv(N, tn);
+    const int64_t tiles = tiles_m * tiles_n;
+    const double flop_tile_kt = 2.0 * tm * tn * (128.0 / e);
+    const double mfma = flop_tile_kt / c.mfma_flop_per_clk_cu[dt];
+    const double ldsc = (4.0 * tm * 128 + tm * 128) / c.lds_bytes_per_clk;
+    const double vmem = (double)(tm + tn) * 128 / c.vmem_bytes_per_clk;
+    const double per_kt = std::max(mfma, std::max(ldsc, vmem)) * (1.0 + 0.25 / occ);
+    const double epi = (double)tm * tn * 2 / c.vmem_bytes_per_clk + 600.0;
+    const double tile_cyc = nkt * per_kt + epi + 800.0;
+    const int64_t per_cu = cdiv(tiles, cus);
+    double us = per_cu * tile_cyc / c.clock_hz * 1e6;
+    const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
+    us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
+    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt);
+    const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
+    const int64_t rounds = cdiv(tiles, cus);
+    out.t.tile_eff = (float)te;
+    out.t.wq_eff = (float)((double)tiles / ((double)rounds * cus));
+    out.t.predicted_us = (float)us;
+    out.us = us;
+    out.screened = 1.0 / te > 1.25;
+    return true;
+}
+
+bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, const Chip& c,
+                  Cand& out)
+{
+    if (M > tm || tm - M >= 16)
+        return false;  // the smallest 16-row multiple that covers M
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    const int64_t nblk = cdiv(N, 16);
+    const int nb = tn / 16;
+    const int64_t nwg = cdiv(nblk, nb);
+    const double b_bytes = (double)nblk * 16 * K * e;
+    const double hbm = (b_bytes + (double)M * K * e + 2.0 * M * N);
+    const double fill = std::min(1.0, (double)nwg / cus);
+    double us = hbm / (c.hbm_bytes_per_s * fill) * 1e6;
+    const int64_t per_cu = cdiv(nwg, cus);
+    const double cu_bytes = per_cu * ((double)nb * 16 * K * e + (double)tm * K * e);
+    us = std::max(us, cu_bytes / (c.cu_stream_bytes_per_clk * c.clock_hz) * 1e6) + 3.0;
+    fill_common(out.t, GEMM_KERNEL_SKINNY, tm, tn, dt);
+    const double te = (double)M * N / ((double)tm * (double)nwg * tn);
+    out.t.tile_eff = (float)te;
+    const int64_t rounds = cdiv(nwg, cus);
+    out.t.wq_eff = (float)((double)nwg / ((double)rounds * cus));
+    out.t.predicted_us = (float)us;
+    out.us = us;
+    out.screened = false;
+    return true;
+}
+
+}  // namespace
+
+int tiled_vgpr_estimate(int tm, int tn)
+{
+    const int mr = tm / 16, nr = tn / 64;
+    const int acc = mr * nr * 4;
+    const int b = nr * 2 * 4 * 2;          // current and next k-tile of B
+    const int a_stage = (tm * 8 / 256) * 4;
+    const int a_frag = 8;
+    const int misc = 32;                   // addresses, offsets, loop state
+    return acc + b + a_stage + a_frag + misc;
+}
+
+bool tiled_supported(int tm, int tn)
+{
+    for (int m : kTiledTM)
+        for (int n : kTiledTN)
+            if (m == tm && n == tn)
+                return true;
+    return false;
+}
+
+bool skinny_supported(int tm, int tn)
+{
+    for (int m : kSkinnyTM)
+        for (int n : kSkinnyTN)
+            if (m == tm && n == tn)
+                return true;
+    return false;
+}
+
+// Pick the fastest candidate under the model; fill `out`.
+void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out)
+{
+    const Chip chip;
+    Cand best{}, best_screened{};
+    bool have = false, have_screened = false;
+    auto consider = [&](const Cand& cd) {
+        Cand& slot = cd.screened ? best_screened : best;
+        bool& h = cd.screened ? have_screened : have;
+        if (!h || cd.us < slot.us) {
+            slot = cd;
+            h = true;
+        }
+    };
+    if (M <= 64) {
+        for (int tm : kSkinnyTM)
+            for (int tn : kSkinnyTN) {
+                Cand cd;
+                if (price_skinny(M, N, K, dt, cus, tm, tn, chip, cd))
+                    consider(cd);
+            }
+    }
+    for (int tm : kTiledTM)
+        for (int tn : kTiledTN) {
+            Cand cd;
+            if (price_tiled(M, N, K, dt, cus, tm, tn, chip, cd))
+                consider(cd);
+        }
+    *out = have ? best.t : best_screened.t;
+}
+
+}  // namespace dg
+
+extern "C" gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                                   int32_t num_cus, gemm_tile* out)
+{
+    if (!out || M < 0 || N < 0 || K < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3) ||
+        num_cus < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (num_cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return GEMM_ERR_HIP;
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return GEMM_ERR_HIP;
+        num_cus = cus;
+    }
+    dg::choose_tile(std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), std::max<int64_t>(K, 1),
+                    (int)dtype, num_cus, out);
+    return GEMM_OK;
+}

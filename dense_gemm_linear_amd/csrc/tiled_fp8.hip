@@ -1,0 +1,4 @@
+#include "internal.hpp"
+#define DT_VALUE DT_FP8
+#define LAUNCH_NAME launch_tiled_fp8
+#include "tiled.inc"

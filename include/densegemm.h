@@ -1,0 +1,184 @@
+/*
+ * densegemm -- dense linear-layer GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the forward GEMM of an LLM linear layer: Y = X * W^T with
+ * the input flattened to X [M = batch * seq_len, K = d_model] and the weight
+ * W [N = d_ff, K] in nn.Linear (row-major [out, in]) layout, so that
+ *     C[m][n] = sum_k A[m][k] * B[n][k]
+ * (TraceLens GEMM analysis page, "Linear layers in LLMs", "Flattening for
+ * GEMM" and "Prefill versus decode": M = B*L for prefill, M = B for decode).
+ * In BLAS terms this is the (T, N) call on (W, X) of that page's "Linear
+ * layer" section; no BLAS is called here.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" must point to device memory of the current
+ *     HIP device; the library never dereferences them on the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without synchronising.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no per-call state and is safe to call from several host threads.
+ *   - Errors are reported by return value; nothing throws across this ABI.
+ *     Argument checks run before any HIP call, so invalid arguments are
+ *     rejected without touching the device.
+ *   - Matrices are row-major with unit stride in the last dimension; the
+ *     leading dimension (lda, ldb, ldc) is in elements.  A non-unit inner
+ *     stride is not representable: callers pass contiguous rows, and nothing
+ *     is copied behind their back (TraceLens page, "Edge cases").
+ */
+#ifndef DENSEGEMM_H
+#define DENSEGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1, /* null pointer, negative size, bad leading dim, misalignment */
+    GEMM_ERR_UNSUPPORTED = 2,   /* K granularity, forced tile infeasible, device not gfx950 */
+    GEMM_ERR_HIP = 3            /* a HIP runtime call or kernel launch failed */
+} gemm_status;
+
+typedef enum {
+    GEMM_BF16 = 0,     /* bfloat16 A and B, fp32 accumulation, bf16 C             */
+    GEMM_FP8_E4M3 = 1  /* OCP e4m3 (max 448) A and B, fp32 accumulation, bf16 C  */
+} gemm_dtype;
+
+typedef enum {
+    GEMM_KERNEL_TILED = 0,  /* block tiles, A double-buffered in LDS, B straight to VGPRs */
+    GEMM_KERNEL_SKINNY = 1  /* M <= 64: B streamed once, waves split K, LDS reduction    */
+} gemm_kernel;
+
+/*
+ * One launch configuration.  Inputs to the kernels: kernel, tile_m, tile_n
+ * (and for the skinny kernel k_split).  The remaining fields are reported by
+ * select_tile for information and ignored when a tile is forced.
+ *
+ *   tiled:  tile_m in {32, 64, 128, 256}, tile_n in {64, 128, 256}; 4 waves of
+ *           64 lanes split tile_n ("GEMM Optimization Guide" page, sections
+ *           1.1 and 1.4); tile_k is 128 bytes of K (64 bf16 or 128 e4m3).
+ *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering
+ *           M), tile_n in {16, 32, 64} (16-column blocks per workgroup),
+ *           k_split = waves that split K in one workgroup (4).
+ */
+typedef struct {
+    int32_t kernel;      /* gemm_kernel */
+    int32_t tile_m;
+    int32_t tile_n;
+    int32_t tile_k;      /* elements of K per pipeline stage (informational) */
+    int32_t atom;        /* MFMA block edge: 16 (informational) */
+    int32_t waves;       /* waves per workgroup (informational) */
+    int32_t k_split;     /* skinny: waves splitting K */
+    int32_t lds_stages;  /* 2 = ping-pong A buffers (informational) */
+    float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */
+    float wq_eff;        /* tiles / (ceil(tiles / CUs) * CUs) */
+    float predicted_us;  /* cost model estimate (informational) */
+} gemm_tile;
+
+/*
+ * select_tile -- choose a launch configuration for an M x N x K GEMM.
+ *
+ * Pure host function: deterministic, no device access unless num_cus == 0,
+ * in which case the current device's compute-unit count is queried.  Weighs
+ * tile quantization (padding) and wave quantization (last-round fill) as the
+ * TraceLens page defines them ("GEMM dimension efficiency"), drops tiles that
+ * pad the output past 1.25x its real area unless nothing else fits (FlyDSL
+ * PR #1303 page, autotuner changes), checks the LDS and register budget
+ * ("GEMM Optimization Guide" page, sections 2.4 and 10), and routes small M
+ * to the skinny kernel.  Ties are broken by a fixed order.
+ *
+ * Returns GEMM_ERR_INVALID_VALUE for out == NULL or negative sizes,
+ * GEMM_ERR_HIP when num_cus == 0 and the device query fails.
+ */
+gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
+                        gemm_tile* out);
+
+/*
+ * shuffle_b_bytes -- size in bytes of the preshuffled weight for N x K.
+ *
+ * Layout ("GEMM Optimization Guide" page, sections 1.4 and 12.1, read in
+ * bytes): [ceil(N/16)][Kp/kb][4][16][kp] elements, kp = 16 / element_bytes
+ * (16 bytes, one 16-byte load per lane), kb = 4 * kp (64 bytes of K), Kp = K
+ * rounded up to kb.  For e4m3 this is exactly (N/16, K/64, 4, 16, 16); for
+ * bf16 (N/16, K/32, 4, 16, 8).  Returns 0 for negative sizes.
+ */
+size_t shuffle_b_bytes(int64_t N, int64_t K, gemm_dtype dtype);
+
+/*
+ * shuffle_b -- rewrite a row-major weight B [N, ldb] (device, bf16 bits or
+ * e4m3 codes) into the preshuffled layout Bs (device, shuffle_b_bytes(N, K)
+ * bytes, 16-byte aligned):
+ *     Bs[n0][k0][g][nl][j] = B[16*n0 + nl][kb*k0 + kp*g + j]
+ * with zero in every position whose row is >= N or whose column is >= K.
+ * One memory-bound kernel; done once per weight and reused by every GEMM call
+ * (page section 12.2).  The "16" index is the MFMA column a lane holds and
+ * the "4" index the lane group, so a 64-lane wave reads one contiguous 1 KiB
+ * block per load.
+ *
+ * Errors: INVALID_VALUE for null pointers with N, K > 0, negative sizes,
+ * ldb < K, Bs not 16-byte aligned; UNSUPPORTED when K is not a multiple of 16
+ * (bf16) or 64 (e4m3); HIP on launch failure.  N == 0 or K == 0: no work.
+ */
+gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K, gemm_dtype dtype,
+                      void* stream);
+
+/*
+ * gemm_bf16 -- C[m][n] = bf16( sum_k A[m][k] * B[n][k] ), fp32 accumulation,
+ * C overwritten (no alpha/beta, no bias).
+ *
+ *   A   device, bf16 bits, row-major [M, lda], lda >= K, base 16-byte aligned,
+ *       lda * 2 a multiple of 16 bytes.
+ *   Bs  device, the weight B [N, K] preshuffled by shuffle_b(..., GEMM_BF16).
+ *   C   device, bf16 bits, row-major [M, ldc], ldc >= N, 2-byte aligned; only
+ *       the M x N region is written (columns N..ldc-1 are untouched).
+ *   tile  NULL = select_tile(M, N, K, GEMM_BF16, <device CUs>); otherwise a
+ *         forced configuration, validated against the shape.
+ *
+ * The fp32 sum is rounded to bf16 to nearest, ties to even ("GEMM
+ * Optimization Guide" page, section 7.1, direct-store epilogue: the
+ * accumulator is truncated to the output type).  Ragged M and N are served by
+ * buffer descriptors bounded at the real rows (loads past them read zero,
+ * stores past them are dropped) and a column predicate on the C store
+ * (FlyDSL PR #1303 page).
+ *
+ * Errors: INVALID_VALUE (null pointer with M, N > 0; negative size; lda < K;
+ * ldc < N; misalignment), UNSUPPORTED (K % 16 != 0; infeasible forced tile;
+ * device is not gfx950; a row offset that does not fit 31 bits), HIP.
+ * M == 0 or N == 0: GEMM_OK, no launch.  K == 0: C := 0 (empty sum); A and
+ * Bs are not read then and may be NULL (no alignment or lda requirement).
+ */
+gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                      int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* stream);
+
+/*
+ * gemm_fp8_scaled -- C[m][n] = bf16( (sum_k a[m][k] * b[n][k]) * sa * sb ).
+ *
+ * a, b are OCP e4m3 codes; sa, sb the per-tensor fp32 dequant multipliers,
+ * each one float in device memory (so a graph can replay with new scales).
+ * The epilogue multiplies the fp32 accumulator by sa, then by sb, in fp32,
+ * and rounds to bf16 to nearest even ("GEMM Optimization Guide" page,
+ * section 7.1).
+ *
+ *   A   device, e4m3 [M, lda], lda >= K, base 16-byte aligned, lda % 16 == 0.
+ *   Bs  device, shuffle_b(..., GEMM_FP8_E4M3) of B [N, K]: (N/16, K/64, 4, 16, 16).
+ *   C   as for gemm_bf16.
+ *
+ * Errors as for gemm_bf16 with K % 64 != 0 -> UNSUPPORTED and null scale
+ * pointers (K > 0) -> INVALID_VALUE.
+ */
+gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
+                            const float* scale_b, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                            int64_t K, const gemm_tile* tile, void* stream);
+
+/* Static, human-readable name of a status code ("GEMM_OK", ...). */
+const char* gemm_status_string(gemm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSEGEMM_H */

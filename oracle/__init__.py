@@ -77,7 +77,7 @@ def _c(a, dtype):
 
 
 def default_threads() -> int:
-    return os.cpu_count() or 1
+    return min(16, os.cpu_count() or 1)
 
 
 # ----------------------------------------------------------------- codecs

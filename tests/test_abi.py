@@ -1,0 +1,144 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every entry
+point include/densegemm.h declares, rejects bad arguments before touching the
+device, and its pure-host parts (select_tile, shuffle_b_bytes) agree with the
+oracle's definitions.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dense_gemm_linear_amd as dg
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "densegemm.h")
+
+CONFIG_SHAPES = [(128, 256, 128), (4096, 4096, 4096), (597, 11008, 4096), (1, 11008, 4096),
+                 (8, 4096, 4096), (48, 4096, 4096), (3402, 4096, 1024), (1024, 50257, 512),
+                 (2048, 11007, 1024), (4095, 4095, 1024), (528, 528, 1024), (32, 4096, 4096)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dg.EXPORTS)
+    raw = ctypes.CDLL(dg.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings():
+    assert dg.gemm_status_string(0) == "GEMM_OK"
+    assert dg.gemm_status_string(1) == "GEMM_ERR_INVALID_VALUE"
+    assert dg.gemm_status_string(2) == "GEMM_ERR_UNSUPPORTED"
+    assert dg.gemm_status_string(3) == "GEMM_ERR_HIP"
+    assert dg.gemm_status_string(99) == "GEMM_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("N,K,dt,e", [(16, 64, "bf16", 2), (17, 48, "bf16", 2), (11008, 4096, "bf16", 2),
+                                      (50257, 512, "bf16", 2), (4096, 4096, "fp8", 1), (33, 128, "fp8", 1),
+                                      (0, 64, "bf16", 2), (5, 0, "fp8", 1)])
+def test_shuffle_b_bytes_matches_oracle(N, K, dt, e):
+    assert dg.shuffle_b_bytes(N, K, dt) == oracle.shuffle_b_bytes(N, K, e)
+
+
+def test_shuffle_b_bytes_fp8_layout_size():
+    # (N/16, K/64, 4, 16, 16) bytes for the fp8 workload
+    assert dg.shuffle_b_bytes(4096, 4096, "fp8") == (4096 // 16) * (4096 // 64) * 4 * 16 * 16
+    assert dg.shuffle_b_bytes(-1, 64, "bf16") == 0
+
+
+@pytest.mark.parametrize("M,N,K", CONFIG_SHAPES)
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_select_tile_metrics_match_oracle(M, N, K, dt):
+    t = dg.select_tile(M, N, K, dt, num_cus=256)
+    assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY)
+    if t.kernel == dg.GEMM_KERNEL_TILED:
+        assert (t.tile_m, t.tile_n) in dg.TILED_LADDER
+        tiles, te, we, de = oracle.dim_eff(M, N, t.tile_m, t.tile_n, 256)
+        assert abs(t.tile_eff - te) < 1e-6 and abs(t.wq_eff - we) < 1e-6
+        # padding screen: padded output at most 1.25x the real one when any tile passes
+        assert 1.0 / t.tile_eff <= 1.25 + 1e-6
+    else:
+        assert (t.tile_m, t.tile_n) in dg.SKINNY_LADDER
+        assert M <= t.tile_m < M + 16
+    assert t.predicted_us > 0
+    assert dg.select_tile(M, N, K, dt, num_cus=256) == t       # deterministic
+
+
+def test_select_tile_routes_small_m_to_skinny():
+    for M in (1, 8, 16):
+        assert dg.select_tile(M, 11008, 4096, "bf16", 256).kernel == dg.GEMM_KERNEL_SKINNY
+    assert dg.select_tile(4096, 4096, 4096, "bf16", 256).kernel == dg.GEMM_KERNEL_TILED
+
+
+def test_select_tile_errors():
+    t = dg.GemmTile()
+    assert dg.lib.select_tile(-1, 4, 4, 0, 256, ctypes.byref(t)) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.lib.select_tile(4, 4, 4, 7, 256, ctypes.byref(t)) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.lib.select_tile(4, 4, 4, 0, 256, None) == dg.GEMM_ERR_INVALID_VALUE
+
+
+# Fake device addresses: argument checks must reject before any HIP call.
+PA = 0x10000
+PB = 0x20000
+PC = 0x30000
+
+
+def _bf16(A, lda, Bs, C, ldc, M, N, K, tile=None):
+    return dg.lib.gemm_bf16(A, lda, Bs, C, ldc, M, N, K, tile, None)
+
+
+def test_gemm_bf16_argument_checks():
+    E = dg.GEMM_ERR_INVALID_VALUE
+    U = dg.GEMM_ERR_UNSUPPORTED
+    assert _bf16(PA, 64, PB, PC, 64, 0, 64, 64) == dg.GEMM_OK        # empty: no launch
+    assert _bf16(PA, 64, PB, PC, 64, 64, 0, 64) == dg.GEMM_OK
+    assert _bf16(None, 64, None, None, 64, 0, 64, 64) == dg.GEMM_OK
+    assert _bf16(PA, 64, PB, PC, 64, -1, 64, 64) == E
+    assert _bf16(PA, 64, PB, PC, 64, 64, 64, -16) == E
+    assert _bf16(None, 64, PB, PC, 64, 64, 64, 64) == E
+    assert _bf16(PA, 64, None, PC, 64, 64, 64, 64) == E
+    assert _bf16(PA, 64, PB, None, 64, 64, 64, 64) == E
+    assert _bf16(PA, 32, PB, PC, 64, 64, 64, 64) == E                 # lda < K
+    assert _bf16(PA, 64, PB, PC, 63, 64, 64, 64) == E                 # ldc < N
+    assert _bf16(PA + 8, 64, PB, PC, 64, 64, 64, 64) == E             # A not 16-byte aligned
+    assert _bf16(PA, 64, PB + 4, PC, 64, 64, 64, 64) == E             # Bs not 16-byte aligned
+    assert _bf16(PA, 68, PB, PC, 64, 64, 64, 64) == E                 # lda*2 % 16 != 0
+    assert _bf16(PA, 64, PB, PC + 1, 64, 64, 64, 64) == E             # C odd address
+    assert _bf16(PA, 64, PB, PC, 64, 64, 64, 40) == U                 # K % 16 != 0
+    assert _bf16(None, 0, None, None, 64, 64, 64, 0) == E              # K = 0 still needs C
+    bad = dg.tiled(100, 64).to_c()
+    assert _bf16(PA, 64, PB, PC, 64, 64, 64, 64, ctypes.byref(bad)) == U
+    bad = dg.skinny(16, 16).to_c()
+    assert _bf16(PA, 64, PB, PC, 64, 17, 64, 64, ctypes.byref(bad)) == U   # M > skinny rows
+
+
+def test_gemm_fp8_argument_checks():
+    E = dg.GEMM_ERR_INVALID_VALUE
+    U = dg.GEMM_ERR_UNSUPPORTED
+    f = dg.lib.gemm_fp8_scaled
+    assert f(PA, 128, PB, 0x40000, 0x40010, PC, 64, 0, 64, 128, None, None) == dg.GEMM_OK
+    assert f(PA, 128, PB, None, 0x40010, PC, 64, 8, 64, 128, None, None) == E
+    assert f(PA, 128, PB, 0x40000, None, PC, 64, 8, 64, 128, None, None) == E
+    assert f(PA, 136, PB, 0x40000, 0x40010, PC, 64, 8, 64, 128, None, None) == E   # lda % 16
+    assert f(PA, 128, PB, 0x40000, 0x40010, PC, 64, 8, 64, 96, None, None) == U    # K % 64
+
+
+def test_shuffle_b_argument_checks():
+    f = dg.lib.shuffle_b
+    assert f(PA, 64, PB, 0, 64, 0, None) == dg.GEMM_OK
+    assert f(PA, 64, PB, 16, 0, 0, None) == dg.GEMM_OK
+    assert f(None, 64, PB, 16, 64, 0, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert f(PA, 32, PB, 16, 64, 0, None) == dg.GEMM_ERR_INVALID_VALUE      # ldb < K
+    assert f(PA, 64, PB + 8, 16, 64, 0, None) == dg.GEMM_ERR_INVALID_VALUE  # Bs alignment
+    assert f(PA, 64, PB, -16, 64, 0, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert f(PA, 96, PB, 16, 96, 1, None) == dg.GEMM_ERR_UNSUPPORTED        # fp8 K % 64
+    assert f(PA, 64, PB, 16, 40, 0, None) == dg.GEMM_ERR_UNSUPPORTED        # bf16 K % 16

@@ -1,0 +1,93 @@
+"""e4m3 GEMM with per-tensor scales on the GPU against the oracle (C ABI).
+
+Inputs: N(0, 1) quantised per tensor to amax 448 (the fp8 workloads), and a
+small-integer variant whose values are exact e4m3 codes: with scales 1 and
+with the power-of-two scales 2^-3, 2^2 the output is bit-exact.  The general
+bound is 3e-2 relative Frobenius against the oracle on the same e4m3 bytes
+with the scales applied, plus the per-element bound of parity.py.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import dense_gemm_linear_amd as dg
+from parity import (abs_bits, check_close, check_exact, oracle_full, oracle_lines, run,
+                    sample_lines)
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = {"cfg5_4096cube": (4096, 4096, 4096, 5), "cfg5_32x4096": (32, 4096, 4096, 51)}
+SMALL_SHAPES = [(128, 256, 128), (33, 65, 64), (1, 16, 64), (263, 270, 192), (597, 600, 256)]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes_full(shape):
+    M, N, K = shape
+    A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=M + 3 * N)
+    C, ok = run("fp8", A, B, sa=sa, sb=sb)
+    assert ok
+    check_close("fp8", C, oracle_full("fp8", A, B, sa, sb),
+                oracle_full("fp8", abs_bits("fp8", A), abs_bits("fp8", B)), K, scale=sa * sb,
+                what=str(shape))
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=M + 3 * N, smallint=True)
+    for (s1, s2) in ((1.0, 1.0), (2.0 ** -3, 2.0 ** 2)):
+        C, ok = run("fp8", A, B, sa=s1, sb=s2)
+        assert ok
+        check_exact(C, oracle_full("fp8", A, B, s1, s2), f"{shape} smallint scales {s1},{s2}")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("smallint", [False, True], ids=["general", "smallint"])
+def test_workload_shapes_sampled(name, smallint):
+    M, N, K, cfg = WORKLOADS[name]
+    A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=cfg, smallint=smallint)
+    if smallint:
+        sa, sb = 2.0 ** -3, 2.0 ** 2
+    print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint} tile="
+          f"{dg.select_tile(M, N, K, 'fp8').name}]", flush=True)
+    C, ok = run("fp8", A, B, sa=sa, sb=sb)
+    assert ok
+    rows, cols = sample_lines(M), sample_lines(N)
+    ms, ns, vals, absv = oracle_lines("fp8", A, B, rows, cols, scale=sa * sb)
+    got = C[ms, ns]
+    if smallint:
+        check_exact(got[None, :], vals[None, :], name)
+    else:
+        check_close("fp8", got[None, :], vals[None, :], absv[None, :], K, scale=sa * sb, what=name)
+
+
+@pytest.mark.parametrize("tm,tn", dg.TILED_LADDER)
+def test_every_tiled_tile(tm, tn):
+    M, N, K = 263, 270, 192
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=19, smallint=True)
+    C, ok = run("fp8", A, B, tile=dg.tiled(tm, tn), sa=0.5, sb=4.0)
+    assert ok
+    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"tiled{tm}x{tn}")
+
+
+@pytest.mark.parametrize("tm,tn", dg.SKINNY_LADDER)
+def test_every_skinny_tile(tm, tn):
+    M, N, K = tm - 3, 270, 320
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=20 + tm, smallint=True)
+    C, ok = run("fp8", A, B, tile=dg.skinny(tm, tn))
+    assert ok
+    check_exact(C, oracle_full("fp8", A, B), f"skinny{tm}x{tn}")
+
+
+@pytest.mark.parametrize("K", [64, 192, 320])
+def test_k_tails(K):
+    M, N = 40, 90
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=K, smallint=True)
+    for tile in (None, dg.tiled(64, 64), dg.tiled(128, 256), dg.skinny(48, 32)):
+        C, ok = run("fp8", A, B, tile=tile)
+        assert ok
+        check_exact(C, oracle_full("fp8", A, B), f"K={K} {tile}")
+
+
+def test_guard_band_odd_ldc():
+    M, N, K = 75, 333, 128
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=3, smallint=True)
+    for ldc, col0 in ((N, 0), (N + 9, 2), (N + 16, 8)):
+        C, ok = run("fp8", A, B, ldc=ldc, col0=col0)
+        assert ok
+        check_exact(C, oracle_full("fp8", A, B), f"ldc={ldc} col0={col0}")
