@@ -224,7 +224,7 @@ def run_graph(name: str, reps: int, copies: int):
 
 
 # ------------------------------------------------------------ CPU oracle
-def cpu_baseline(name: str, budget_s: float = 15.0):
+def cpu_baseline(name: str, budget_s: float = 20.0):
     """The oracle on whole rows of C of the same workload, scaled to TFLOP/s."""
     import numpy as np
     import oracle
@@ -239,7 +239,7 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
         else:
             oracle.gemm_e4m3(A[:rows], B, s_a, s_b, threads=threads)
         el = time.perf_counter() - t
-        if el >= budget_s / 4 or rows >= M:
+        if el >= budget_s / 2 or rows >= M:
             break
         rows = min(M, max(rows * 2, int(rows * budget_s / 2 / max(el, 1e-3))))
     val = flops(rows, N, K) / el / 1e12

@@ -94,6 +94,14 @@ class GemmError(RuntimeError):
 
 
 def _load_lib():
+    # Load torch's HIP runtime first.  torch ships its own libamdhip64 (soname
+    # libamdhip64.so.7); once it is mapped, this library's dependency on that
+    # soname resolves to the same copy, so the memory and streams torch hands
+    # us belong to the runtime our kernels launch on.  Loading this library
+    # first would map /opt/rocm's runtime as well: two HIP runtimes in one
+    # process, and launches on torch's streams fail.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g;"
                           f" g.build()'` (hipcc, gfx950). There is no fallback implementation.")

@@ -142,3 +142,12 @@ def test_shuffle_b_argument_checks():
     assert f(PA, 64, PB, -16, 64, 0, None) == dg.GEMM_ERR_INVALID_VALUE
     assert f(PA, 96, PB, 16, 96, 1, None) == dg.GEMM_ERR_UNSUPPORTED        # fp8 K % 64
     assert f(PA, 64, PB, 16, 40, 0, None) == dg.GEMM_ERR_UNSUPPORTED        # bf16 K % 16
+
+
+def test_one_hip_runtime_in_process():
+    """The binding must bind to the HIP runtime torch already loaded: exactly
+    one libamdhip64 mapped in this process."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {line.split()[-1] for line in maps if "libamdhip64" in line and "/" in line}
+    assert len(libs) == 1, libs
