@@ -142,22 +142,47 @@ def gpu_setup(name: str, copies: int):
     return sets, scales, shuffle_us
 
 
-def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True):
+def parse_tile(spec: str | None):
+    """'tiled:256x128', 'tiled:256x256w8', 'ab:256x256w8' or 'skinny:16x32' -> Tile;
+    None -> select_tile."""
+    if spec is None:
+        return None
+    import dense_gemm_linear_amd as dg
+    kind, dims = spec.split(":")
+    waves = 4
+    if "w" in dims:
+        dims, w = dims.split("w")
+        waves = int(w)
+    tm, tn = (int(x) for x in dims.split("x"))
+    if kind == "tiled":
+        return dg.tiled(tm, tn, waves)
+    if kind == "ab":
+        return dg.tiled_ab(tm, tn, waves)
+    return dg.skinny(tm, tn)
+
+
+def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True,
+              tile=None, setup=None):
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
     if copies is None:   # enough operand sets to exceed twice the Infinity Cache
         per_set = alg_bytes(M, N, K, dt)
         copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
-    sets, (s_a, s_b), shuffle_us = gpu_setup(name, copies)
-    tile = dg.select_tile(M, N, K, dt)
+    if setup is None:
+        setup = gpu_setup(name, copies)
+    sets, (s_a, s_b), shuffle_us = setup
+    copies = len(sets)
+    forced = tile
+    if tile is None:
+        tile = dg.select_tile(M, N, K, dt)
 
     def call(i):
         a, bs, c = sets[i % copies]
         if dt == "bf16":
-            dg.gemm_bf16(a, bs, N, out=c)
+            dg.gemm_bf16(a, bs, N, out=c, tile=forced)
         else:
-            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c)
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, tile=forced)
 
     for i in range(warmup):
         call(i)
@@ -256,6 +281,10 @@ def main(argv=None):
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--tile", default=None, help="force a tile, e.g. tiled:256x256 or skinny:16x32")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every tile of the ladder on the workload (one JSON line each) and the "
+                         "selector's pick; reports the selector's regret")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
@@ -267,7 +296,9 @@ def main(argv=None):
         return 2
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
-    r = run_timed(name, args.steps, args.warmup)
+    if args.sweep:
+        return sweep(name, args.steps, args.warmup)
+    r = run_timed(name, args.steps, args.warmup, tile=parse_tile(args.tile))
     ms_per_step = r["total_ms"] / args.steps
     kern = sorted(r["kernel_us"])
     kern_avg = sum(kern) / len(kern)
@@ -319,6 +350,32 @@ def main(argv=None):
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(name)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def sweep(name: str, steps: int, warmup: int) -> int:
+    """Every feasible tile on one workload; prints a line per tile and a summary
+    with the selector's regret (its pick's time over the best time)."""
+    import torch
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    per_set = alg_bytes(M, N, K, dt)
+    copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
+    setup = gpu_setup(name, copies)
+    tiles = dg.all_tiles(M)
+    res = {}
+    for t in tiles:
+        r = run_timed(name, steps, warmup, tile=t, setup=setup)
+        us = sorted(r["kernel_us"])[len(r["kernel_us"]) // 2]
+        res[t.name] = us
+        print(json.dumps({"sweep": name, "tile": t.name, "kernel_us_median": round(us, 3),
+                          "tflops": round(flops(M, N, K) / (us * 1e-6) / 1e12, 1),
+                          "gbps": round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)}), flush=True)
+    pick = dg.select_tile(M, N, K, dt)
+    best = min(res, key=res.get)
+    print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
+                      "best": best, "best_us": round(res[best], 3),
+                      "regret": round(res[pick.name] / res[best], 4)}), flush=True)
     return 0
 
 

@@ -33,6 +33,7 @@ GEMM_FP8_E4M3 = 1
 
 GEMM_KERNEL_TILED = 0
 GEMM_KERNEL_SKINNY = 1
+GEMM_KERNEL_TILED_AB = 2
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_status_string")
@@ -62,8 +63,11 @@ class Tile:
 
     @property
     def name(self) -> str:
-        kind = "tiled" if self.kernel == GEMM_KERNEL_TILED else "skinny"
-        return f"{kind}{self.tile_m}x{self.tile_n}"
+        if self.kernel == GEMM_KERNEL_TILED:
+            return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}")
+        if self.kernel == GEMM_KERNEL_TILED_AB:
+            return f"ab{self.tile_m}x{self.tile_n}w{self.waves}"
+        return f"skinny{self.tile_m}x{self.tile_n}"
 
     def to_c(self) -> GemmTile:
         return GemmTile(self.kernel, self.tile_m, self.tile_n, self.tile_k, self.atom, self.waves,
@@ -75,16 +79,31 @@ class Tile:
                     t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
 
 
-def tiled(tm: int, tn: int) -> Tile:
-    return Tile(GEMM_KERNEL_TILED, tm, tn)
+def tiled(tm: int, tn: int, waves: int = 4) -> Tile:
+    return Tile(GEMM_KERNEL_TILED, tm, tn, waves=waves)
+
+
+def tiled_ab(tm: int, tn: int, waves: int = 4) -> Tile:
+    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, waves=waves)
 
 
 def skinny(tm: int, tn: int) -> Tile:
     return Tile(GEMM_KERNEL_SKINNY, tm, tn, k_split=4, lds_stages=0)
 
 
-TILED_LADDER = [(m, n) for m in (256, 128, 64, 32) for n in (256, 128, 64)]
+# (tile_m, tile_n, waves): 8-wave rungs arrange the waves 2 (M) x 4 (N)
+TILED_LADDER = [(256, 256, 8), (256, 128, 8), (128, 256, 8), (128, 128, 8)] + \
+    [(m, n, 4) for m in (256, 128, 64, 32) for n in (256, 128, 64) if (m, n) != (256, 256)]
+AB_LADDER = [(256, 256, 8), (256, 256, 4), (256, 128, 4), (128, 256, 4), (128, 128, 4)]
 SKINNY_LADDER = [(m, n) for m in (16, 32, 48, 64) for n in (16, 32, 64)]
+
+
+def all_tiles(M: int):
+    """Every rung usable for a GEMM with M rows."""
+    t = [tiled(m, n, w) for m, n, w in TILED_LADDER] + [tiled_ab(m, n, w) for m, n, w in AB_LADDER]
+    if M <= 64:
+        t += [skinny(m, n) for m, n in SKINNY_LADDER if M <= m < M + 16]
+    return t
 
 
 class GemmError(RuntimeError):

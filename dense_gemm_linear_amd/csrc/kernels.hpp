@@ -27,11 +27,35 @@
 // and stays in L2); partial sums are reduced in LDS in a fixed order.
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace dg {
 
 enum { DT_BF16 = 0, DT_FP8 = 1 };
+
+// Depth of the tiled kernel's load pipeline (k-tiles in LDS / registers):
+// 3 for 4-wave tiles (one wave per SIMD hides its own latency), 2 for 8-wave
+// tiles (two waves per SIMD share 512 registers and hide each other's).
+#ifndef DG_STAGES_4WAVE
+#define DG_STAGES_4WAVE 3
+#endif
+#ifndef DG_STAGES_8WAVE
+#define DG_STAGES_8WAVE 2
+#endif
+// Tile rows per raster group, and whether workgroups are renumbered per XCD.
+#ifndef DG_GROUP_M
+#define DG_GROUP_M 4
+#endif
+// A fragments read from LDS ahead of the MFMAs that consume them.
+#ifndef DG_LDS_AHEAD
+#define DG_LDS_AHEAD 2
+#endif
+#ifndef DG_XCD_REMAP
+#define DG_XCD_REMAP 1
+#endif
+constexpr int tiled_stages(int waves) { return waves == 8 ? DG_STAGES_8WAVE : DG_STAGES_4WAVE; }
 
 struct GemmArgs {
     const uint8_t* A;     // [M, lda] elements, row-major
@@ -60,9 +84,12 @@ template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn)
 {
     const int G = tiles_m * tiles_n;
-    const int x = wg & 7, j = wg >> 3;
-    const int q = G >> 3, r = G & 7;
-    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    int t = wg;
+    if (DG_XCD_REMAP) {
+        const int x = wg & 7, j = wg >> 3;
+        const int q = G >> 3, r = G & 7;
+        t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    }
     const int per_group = GROUP_M * tiles_n;
     const int grp = t / per_group;
     const int first = grp * GROUP_M;
@@ -72,170 +99,53 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
     tn = in / gm;
 }
 
-template <int TM, int TN>
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int TM, int TN, int WM, int ST>
 struct TiledShape {
-    static constexpr int MR = TM / 16;            // 16-row MFMA blocks per wave
+    static constexpr int WAVES = 4 * WM;          // WM rows x 4 columns of waves
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int MR = TM / WM / 16;       // 16-row MFMA blocks per wave
     static constexpr int NR = TN / 64;            // 16-column blocks per wave
-    static constexpr int A_LOADS = TM * 8 / 256;  // 16-byte A chunks per thread per k-tile
-    static constexpr int A_BUF = TM * 128;        // bytes of one A buffer
+    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
+    static constexpr int A_BUF = TM * 128;        // bytes of one A stage
+    static constexpr int LOADS = A_DMA + 2 * NR;  // vector-memory ops per wave per k-tile
     static constexpr int WCOLS = TN / 4;          // C columns per wave
     static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
     static constexpr int fit_ch()
     {
         int ch = MR;
-        while (ch > 1 && (4 * ch * 16 * SROW > 2 * A_BUF || MR % ch != 0))
+        while (ch > 1 && (WAVES * ch * 16 * SROW > ST * A_BUF || MR % ch != 0))
             --ch;
         return ch;
     }
     static constexpr int CH = fit_ch();           // 16-row blocks per epilogue pass
-    static constexpr int LDS = (2 * A_BUF > 4 * CH * 16 * SROW) ? 2 * A_BUF : 4 * CH * 16 * SROW;
-    static_assert(TM % 32 == 0 && TN % 64 == 0, "tile shape");
+    static constexpr int LDS = (ST * A_BUF > WAVES * CH * 16 * SROW) ? ST * A_BUF
+                                                                     : WAVES * CH * 16 * SROW;
+    static_assert(TM % (32 * WM) == 0 && TN % 64 == 0 && A_DMA >= 1, "tile shape");
+    static_assert(ST >= 2 && (ST - 2) * LOADS <= 63, "pipeline depth");
 };
 
-template <int DT, int TM, int TN>
-__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs p)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Epilogue shared by the tiled kernels: scale (e4m3), round to bf16, stage a
+// wave's (MR*16) x (NR*16) accumulator block through its private LDS region
+// CH row blocks at a time, and store 16-byte row pieces ("GEMM Optimization
+// Guide" page, section 7.2).  Rows past M fall outside the C descriptor; the
+// column predicate keeps a row's padding and the next row intact, and odd
+// leading dimensions or an unaligned C take 2-byte stores.
+template <int DT, int MR, int NR, int CH, int SROW, int WCOLS>
+__device__ __forceinline__ void store_c_tile(const GemmArgs& p, const f32x4 (&acc)[MR][NR],
+                                             uint8_t* stage, int m0, int rows, int col_w, int row0,
+                                             int lane, float scale_a, float scale_b)
 {
-    using S = TiledShape<TM, TN>;
-    constexpr int MR = S::MR, NR = S::NR, A_LOADS = S::A_LOADS, A_BUF = S::A_BUF;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    int tm, tn;
-    tile_coords<4>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * TM;
-    const int n0 = tn * TN;
-    const int rows = min(TM, p.M - m0);
-
-    // Descriptors rebased at this tile: rows past M and 16-column blocks past
-    // ceil(N/16) fall outside and read as zero.
-    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
-                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
-    const int nb0 = n0 >> 4;
-    const int nbv = min(TN / 16, p.nblk - nb0);
-    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
-                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
-
-    // A chunk c of a k-tile: row c / 8, 16-byte column c % 8.
-    uint32_t a_goff[A_LOADS], a_soff[A_LOADS], a_col[A_LOADS];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-        const uint32_t c = tid + 256 * i;
-        const uint32_t row = c >> 3, col = c & 7;
-        a_goff[i] = row * (uint32_t)p.lda_b + col * 16;
-        a_soff[i] = row * 128 + ((col ^ ((row >> 1) & 7)) << 4);
-        a_col[i] = col * 16;
-    }
-    const uint32_t b_base = (uint32_t)(wave * NR) * (uint32_t)p.KB * 1024u + lane * 16;
     const int r16 = lane & 15, g4 = lane >> 4;
-    const uint32_t swz = (r16 >> 1) & 7;
-
-    i32x4 areg[A_LOADS];
-    i32x4 bcur[NR][2], bnext[NR][2];
-    f32x4 acc[MR][NR];
-#pragma unroll
-    for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-        for (int j = 0; j < NR; ++j)
-            acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load_a = [&](int kt, bool mask) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            uint32_t off = a_goff[i] + (uint32_t)kt * 128;
-            if (mask && (int)((uint32_t)kt * 128 + a_col[i]) >= p.KA_b)
-                off = kOOB;
-            areg[i] = load16(ra, off);
-        }
-    };
-    auto load_b = [&](i32x4 (&dst)[NR][2], int kt, bool mask) {
-#pragma unroll
-        for (int j = 0; j < NR; ++j)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int kb = kt * 2 + c;
-                uint32_t off = b_base + (uint32_t)(j * p.KB + kb) * 1024u;
-                if (mask && kb >= p.KB)
-                    off = kOOB;
-                dst[j][c] = load16(rb, off);
-            }
-    };
-    auto store_a = [&](uint8_t* buf) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            *reinterpret_cast<i32x4*>(buf + a_soff[i]) = areg[i];
-    };
-    auto lds_a = [&](const uint8_t* buf, int mi, int col16) -> i32x4 {
-        const uint32_t off = (uint32_t)(mi * 16 + r16) * 128 + (((uint32_t)col16 ^ swz) << 4);
-        return *reinterpret_cast<const i32x4*>(buf + off);
-    };
-    auto compute = [&](const uint8_t* buf) {
-        if constexpr (DT == DT_BF16) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int mi = 0; mi < MR; ++mi) {
-                    const i32x4 a = lds_a(buf, mi, 4 * s + g4);
-#pragma unroll
-                    for (int j = 0; j < NR; ++j)
-                        acc[mi][j] = mfma_bf16(a, bcur[j][s], acc[mi][j]);
-                }
-        } else {
-#pragma unroll
-            for (int mi = 0; mi < MR; ++mi) {
-                const i32x8 a = cat(lds_a(buf, mi, g4), lds_a(buf, mi, 4 + g4));
-#pragma unroll
-                for (int j = 0; j < NR; ++j)
-                    acc[mi][j] = mfma_fp8(a, cat(bcur[j][0], bcur[j][1]), acc[mi][j]);
-            }
-        }
-    };
-
-    // Prologue: k-tile 0 into buffer 0 and registers.
-    {
-        const bool m = p.tail && p.nkt == 1;
-        load_a(0, m);
-        load_b(bcur, 0, m);
-        store_a(lds);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < p.nkt; ++kt) {
-        uint8_t* cur = lds + (kt & 1) * A_BUF;
-        uint8_t* nxt = lds + ((kt & 1) ^ 1) * A_BUF;
-        const bool has_next = kt + 1 < p.nkt;
-        if (has_next) {
-            const bool m = p.tail && kt + 2 == p.nkt;
-            load_a(kt + 1, m);
-            load_b(bnext, kt + 1, m);
-        }
-        compute(cur);
-        if (has_next)
-            store_a(nxt);
-        __syncthreads();
-        if (has_next) {
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                bcur[j][0] = bnext[j][0];
-                bcur[j][1] = bnext[j][1];
-            }
-        }
-    }
-
-    // Epilogue: scale, round, stage through LDS, store 16-byte row pieces.
-    float scale_a = 1.f, scale_b = 1.f;
-    if constexpr (DT == DT_FP8) {
-        scale_a = *p.sa;
-        scale_b = *p.sb;
-    }
     const rsrc_t rc = make_rsrc(p.C + (int64_t)m0 * p.ldc,
                                 (uint32_t)(((int64_t)(rows - 1) * p.ldc + p.N) * 2));
-    constexpr int CH = S::CH, SROW = S::SROW, WCOLS = S::WCOLS;
     constexpr int PPR = WCOLS / 8;                 // 16-byte pieces per staged row
     constexpr int PIECES = CH * 16 * PPR;
-    uint8_t* stage = lds + wave * (CH * 16 * SROW);
-    const int col_w = n0 + wave * WCOLS;           // first C column of this wave
 #pragma unroll
     for (int cc = 0; cc < MR / CH; ++cc) {
 #pragma unroll
@@ -258,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs p)
             if (PIECES % 64 == 0 || q < PIECES) {
                 const int prow = q / PPR, pc = q % PPR;
                 const i32x4 v = *reinterpret_cast<const i32x4*>(stage + prow * SROW + pc * 16);
-                const int trow = cc * CH * 16 + prow;       // row within the tile
+                const int trow = row0 + cc * CH * 16 + prow;   // row within the tile
                 const int gcol = col_w + pc * 8;
                 const uint32_t off = (uint32_t)(((int64_t)trow * p.ldc + gcol) * 2);
                 if (p.c_vec && gcol + 8 <= p.N) {
@@ -273,6 +183,434 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs p)
         }
         __syncthreads();
     }
+}
+
+
+
+template <int DT, int TM, int TN, int WM, int ST>
+__global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
+{
+    using S = TiledShape<TM, TN, WM, ST>;
+    constexpr int MR = S::MR, NR = S::NR, A_DMA = S::A_DMA, A_BUF = S::A_BUF;
+    constexpr int WAVES = S::WAVES;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;     // wave row (M) and column (N)
+    int tm, tn;
+    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+
+    // Descriptors rebased at this tile: rows past M and 16-column blocks past
+    // ceil(N/16) fall outside and read as zero.
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
+
+    // A: global -> LDS without registers (16-byte LDS DMA per lane).  One
+    // load of a wave fills one 1 KiB chunk = 8 rows of 128 bytes; lane l
+    // lands at chunk + 16*l, i.e. row l/8, 16-byte slot l%8.  The XOR swizzle
+    // ("GEMM Optimization Guide" page, section 3) is applied on the global
+    // side: the slot holds the column (slot ^ ((row >> 1) & 7)).  Wave w
+    // fills chunks w, w + WAVES, ...
+    uint32_t a_goff[A_DMA], a_col[A_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const uint32_t row = 8 * (wave + WAVES * i) + (lane >> 3);
+        const uint32_t col = (lane & 7) ^ ((row >> 1) & 7);
+        a_goff[i] = row * (uint32_t)p.lda_b + col * 16;
+        a_col[i] = col * 16;
+    }
+    const uint32_t b_base = (uint32_t)(wn * NR) * (uint32_t)p.KB * 1024u + lane * 16;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const uint32_t swz = (r16 >> 1) & 7;
+    const uint32_t row0 = (uint32_t)(wm * (TM / WM));   // first A row of this wave
+
+    i32x4 breg[ST][NR][2];
+    f32x4 acc[MR][NR];
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // A k-tile past the real K (kt >= nkt, or the K tail of the last one)
+    // loads through out-of-range offsets: zeros, and no memory traffic.
+    const int last_full = p.tail ? p.nkt - 1 : p.nkt;   // first k-tile that needs masking
+    auto load_a = [&](int kt, int stage) __attribute__((always_inline)) {
+        const bool mask = kt >= last_full;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            uint32_t off = a_goff[i] + (uint32_t)kt * 128;
+            if (mask && (int)((uint32_t)kt * 128 + a_col[i]) >= p.KA_b)
+                off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void*)(lds + stage * A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    auto load_b = [&](i32x4 (&dst)[NR][2], int kt) __attribute__((always_inline)) {
+        const bool mask = kt >= last_full;
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int kb = kt * 2 + c;
+                uint32_t off = b_base + (uint32_t)(j * p.KB + kb) * 1024u;
+                if (mask && kb >= p.KB)
+                    off = kOOB;
+                dst[j][c] = load16(rb, off);
+            }
+    };
+    auto lds_a = [&](int stage, int mi, int col16) __attribute__((always_inline)) -> i32x4 {
+        const uint32_t off = (uint32_t)(stage * A_BUF) + (row0 + (uint32_t)(mi * 16 + r16)) * 128 +
+                             (((uint32_t)col16 ^ swz) << 4);
+        return *reinterpret_cast<const i32x4*>(lds + off);
+    };
+    // MFMAs of one k-tile.  The group barriers fix the issue order: the LDS
+    // reads of the first DG_LDS_AHEAD A fragments, then for every fragment its
+    // NR MFMAs followed by the read of the fragment DG_LDS_AHEAD places ahead,
+    // so that many reads are in flight while MFMAs issue (instead of all reads
+    // up front, which costs registers the pipeline needs, or one at a time,
+    // which exposes the LDS latency).
+    auto compute = [&](int stage, const i32x4 (&b)[NR][2]) __attribute__((always_inline)) {
+        constexpr int F = DT == DT_BF16 ? 2 * MR : MR;        // A fragments per k-tile
+        constexpr int RPF = DT == DT_BF16 ? 1 : 2;             // reads per fragment
+        constexpr int D = DG_LDS_AHEAD < F ? DG_LDS_AHEAD : F;
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int mi = 0; mi < MR; ++mi) {
+                    const i32x4 a = lds_a(stage, mi, 4 * s + g4);
+#pragma unroll
+                    for (int j = 0; j < NR; ++j)
+                        acc[mi][j] = mfma_bf16(a, b[j][s], acc[mi][j]);
+                }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < MR; ++mi) {
+                const i32x8 a = cat(lds_a(stage, mi, g4), lds_a(stage, mi, 4 + g4));
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    acc[mi][j] = mfma_fp8(a, cat(b[j][0], b[j][1]), acc[mi][j]);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, D * RPF, 0);
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
+            if (f + D < F)
+                __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
+        }
+    };
+    // Barrier without the workgroup memory fence of __syncthreads (which would
+    // drain every outstanding load, prefetches included); the explicit
+    // vmcnt wait before it is what makes the next stage visible.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: k-tiles 0 .. ST-2 in flight, wait for k-tile 0.
+#pragma unroll
+    for (int t = 0; t < ST - 1; ++t) {
+        load_a(t, t);
+        load_b(breg[t], t);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
+    barrier();
+
+    // Phase t multiplies k-tile t out of stage t % ST while k-tile t + ST - 1
+    // streams into the stage that phase t - 1 just finished with.  At the end
+    // of the phase, k-tile t + 1 must have landed: at most the ST - 2 newer
+    // k-tiles' loads may still be in flight.  Loads past nkt read zeros.
+    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int pre = (s + ST - 1) % ST;
+        load_a(t + ST - 1, pre);
+        load_b(breg[pre], t + ST - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s, breg[s]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
+        barrier();
+    };
+    // Steady state: ST unconditional phases per trip (no control-flow merges
+    // inside the loop, so the accumulators keep their registers); the last
+    // nkt % ST k-tiles run after it.
+    static_assert(ST <= 4, "phases are spelled out for up to 4 stages");
+    int kt = 0;
+    for (; kt + ST <= p.nkt; kt += ST) {
+        phase(kt, std::integral_constant<int, 0>{});
+        phase(kt + 1, std::integral_constant<int, 1>{});
+        if constexpr (ST > 2)
+            phase(kt + 2, std::integral_constant<int, 2>{});
+        if constexpr (ST > 3)
+            phase(kt + 3, std::integral_constant<int, 3>{});
+    }
+    if (kt < p.nkt)
+        phase(kt, std::integral_constant<int, 0>{});
+    if constexpr (ST > 2) {
+        if (kt + 1 < p.nkt)
+            phase(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (ST > 3) {
+        if (kt + 2 < p.nkt)
+            phase(kt + 2, std::integral_constant<int, 2>{});
+    }
+    // The zero prefetches past nkt still target LDS: drain them everywhere
+    // before the epilogue reuses it.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+
+    float scale_a = 1.f, scale_b = 1.f;
+    if constexpr (DT == DT_FP8) {
+        scale_a = *p.sa;
+        scale_b = *p.sb;
+    }
+    store_c_tile<DT, MR, NR, S::CH, S::SROW, S::WCOLS>(p, acc, lds + wave * (S::CH * 16 * S::SROW),
+                                                      m0, rows, n0 + wn * S::WCOLS, (int)row0,
+                                                      lane, scale_a, scale_b);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel with A and B both staged in LDS ("AB" kernel).
+//
+// Loading a B fragment straight into the registers of every wave that needs
+// it (the kernel above) moves it from L2 once per wave row; measured on
+// MI355X, the L2 -> CU path, not the MFMA, bounds both kernels once the tile
+// is large.  Here each k-tile of A *and* B enters the workgroup once, by
+// 16-byte LDS DMA, and the WM x WN waves read their fragments from LDS.  The
+// preshuffled B blocks (1 KiB = one MFMA operand per 64 lanes) land in LDS
+// unchanged, so B fragment reads are contiguous 1 KiB ds_read_b128s.
+// Per k-tile and stage: [A: TM rows x 128 B, XOR-swizzled][B: TN/16 blocks x
+// 2 halves x 1 KiB].
+template <int TM, int TN, int WM, int WN, int ST>
+struct ABShape {
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int MR = TM / WM / 16;       // 16-row MFMA blocks per wave
+    static constexpr int NR = TN / WN / 16;       // 16-column blocks per wave
+    static constexpr int A_BUF = TM * 128;
+    static constexpr int B_BUF = TN * 128;
+    static constexpr int STAGE = A_BUF + B_BUF;
+    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
+    static constexpr int B_DMA = TN / 8 / WAVES;  // 1 KiB B loads per wave per k-tile
+    static constexpr int LOADS = A_DMA + B_DMA;
+    static constexpr int WCOLS = TN / WN;         // C columns per wave
+    static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
+    static constexpr int fit_ch()
+    {
+        int ch = MR;
+        while (ch > 1 && (WAVES * ch * 16 * SROW > ST * STAGE || MR % ch != 0))
+            --ch;
+        return ch;
+    }
+    static constexpr int CH = fit_ch();
+    static constexpr int LDS = (ST * STAGE > WAVES * CH * 16 * SROW) ? ST * STAGE
+                                                                     : WAVES * CH * 16 * SROW;
+    static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * 8 * WAVES == TM && B_DMA * 8 * WAVES == TN,
+                  "DMA split");
+    static_assert(ST >= 2 && ST <= 4 && (ST - 2) * LOADS <= 63, "pipeline depth");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int DT, int TM, int TN, int WM, int WN, int ST>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
+{
+    using S = ABShape<TM, TN, WM, WN, ST>;
+    constexpr int MR = S::MR, NR = S::NR, A_BUF = S::A_BUF, STAGE = S::STAGE;
+    constexpr int WAVES = S::WAVES, A_DMA = S::A_DMA, B_DMA = S::B_DMA;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
+
+    // A chunk w + WAVES*i: rows 8c .. 8c+7 (swizzled on the global side as in
+    // the kernel above).  B chunk w + WAVES*i: block b / 2, half b % 2.
+    uint32_t a_goff[A_DMA], a_col[A_DMA], b_goff[B_DMA], b_half[B_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const uint32_t row = 8 * (wave + WAVES * i) + (lane >> 3);
+        const uint32_t col = (lane & 7) ^ ((row >> 1) & 7);
+        a_goff[i] = row * (uint32_t)p.lda_b + col * 16;
+        a_col[i] = col * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const uint32_t b = wave + WAVES * i;
+        b_goff[i] = ((b >> 1) * (uint32_t)p.KB + (b & 1)) * 1024u + lane * 16;
+        b_half[i] = b & 1;
+    }
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const uint32_t swz = (r16 >> 1) & 7;
+    const uint32_t row0 = (uint32_t)(wm * (TM / WM));
+    const uint32_t bblk0 = (uint32_t)(wn * NR);          // first B block of this wave
+
+    f32x4 acc[MR][NR];
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int last_full = p.tail ? p.nkt - 1 : p.nkt;
+    auto load = [&](int kt, int stage) __attribute__((always_inline)) {
+        const bool mask = kt >= last_full;
+        uint8_t* base = lds + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            uint32_t off = a_goff[i] + (uint32_t)kt * 128;
+            if (mask && (int)((uint32_t)kt * 128 + a_col[i]) >= p.KA_b)
+                off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i) {
+            uint32_t off = b_goff[i] + (uint32_t)kt * 2048u;
+            if (mask && kt * 2 + (int)b_half[i] >= p.KB)
+                off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    auto lds_a = [&](int stage, int mi, int col16) __attribute__((always_inline)) -> i32x4 {
+        const uint32_t off = (uint32_t)(stage * STAGE) + (row0 + (uint32_t)(mi * 16 + r16)) * 128 +
+                             (((uint32_t)col16 ^ swz) << 4);
+        return *reinterpret_cast<const i32x4*>(lds + off);
+    };
+    auto lds_b = [&](int stage, int j, int half) __attribute__((always_inline)) -> i32x4 {
+        const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) +
+                             (((bblk0 + (uint32_t)j) * 2 + (uint32_t)half) << 10) + lane * 16;
+        return *reinterpret_cast<const i32x4*>(lds + off);
+    };
+    // One k-tile: per K step the NR B fragments, then the A fragments streamed
+    // DG_LDS_AHEAD ahead of their NR MFMAs each.
+    auto compute = [&](int stage) __attribute__((always_inline)) {
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x4 bf[NR];
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    bf[j] = lds_b(stage, j, s);
+#pragma unroll
+                for (int mi = 0; mi < MR; ++mi) {
+                    const i32x4 a = lds_a(stage, mi, 4 * s + g4);
+#pragma unroll
+                    for (int j = 0; j < NR; ++j)
+                        acc[mi][j] = mfma_bf16(a, bf[j], acc[mi][j]);
+                }
+            }
+            constexpr int D = DG_LDS_AHEAD < MR ? DG_LDS_AHEAD : MR;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x100, NR + D, 0);
+#pragma unroll
+                for (int f = 0; f < MR; ++f) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
+                    if (f + D < MR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+        } else {
+            i32x8 bf[NR];
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+                bf[j] = cat(lds_b(stage, j, 0), lds_b(stage, j, 1));
+#pragma unroll
+            for (int mi = 0; mi < MR; ++mi) {
+                const i32x8 a = cat(lds_a(stage, mi, g4), lds_a(stage, mi, 4 + g4));
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    acc[mi][j] = mfma_fp8(a, bf[j], acc[mi][j]);
+            }
+            constexpr int D = DG_LDS_AHEAD < MR ? DG_LDS_AHEAD : MR;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR + 2 * D, 0);
+#pragma unroll
+            for (int f = 0; f < MR; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
+                if (f + D < MR)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
+    };
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int pre = (s + ST - 1) % ST;
+        load(t + ST - 1, pre);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
+        barrier();
+    };
+
+#pragma unroll
+    for (int t = 0; t < ST - 1; ++t)
+        load(t, t);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
+    barrier();
+
+    int kt = 0;
+    for (; kt + ST <= p.nkt; kt += ST) {
+        phase(kt, std::integral_constant<int, 0>{});
+        phase(kt + 1, std::integral_constant<int, 1>{});
+        if constexpr (ST > 2)
+            phase(kt + 2, std::integral_constant<int, 2>{});
+        if constexpr (ST > 3)
+            phase(kt + 3, std::integral_constant<int, 3>{});
+    }
+    if (kt < p.nkt)
+        phase(kt, std::integral_constant<int, 0>{});
+    if constexpr (ST > 2) {
+        if (kt + 1 < p.nkt)
+            phase(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (ST > 3) {
+        if (kt + 2 < p.nkt)
+            phase(kt + 2, std::integral_constant<int, 2>{});
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+
+    float scale_a = 1.f, scale_b = 1.f;
+    if constexpr (DT == DT_FP8) {
+        scale_a = *p.sa;
+        scale_b = *p.sb;
+    }
+    store_c_tile<DT, MR, NR, S::CH, S::SROW, S::WCOLS>(p, acc, lds + wave * (S::CH * 16 * S::SROW),
+                                                      m0, rows, n0 + wn * S::WCOLS, (int)row0,
+                                                      lane, scale_a, scale_b);
 }
 
 // Skinny kernel: NB 16-column blocks per workgroup, MR 16-row blocks cover M.

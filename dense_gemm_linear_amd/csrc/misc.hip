@@ -65,13 +65,20 @@ hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStre
                            dim3(256), args, 0, s);
 }
 
-int tiled_lds_bytes(int tm, int tn)
+int ab_lds_bytes(int tm, int tn, int waves)
 {
-#define DG_CASE(M_, N_) if (tm == M_ && tn == N_) return TiledShape<M_, N_>::LDS;
-    DG_CASE(256, 256) DG_CASE(256, 128) DG_CASE(256, 64)
-    DG_CASE(128, 256) DG_CASE(128, 128) DG_CASE(128, 64)
-    DG_CASE(64, 256) DG_CASE(64, 128) DG_CASE(64, 64)
-    DG_CASE(32, 256) DG_CASE(32, 128) DG_CASE(32, 64)
+#define DG_CASE(M_, N_, WM_, WN_, ST_) \
+    if (tm == M_ && tn == N_ && waves == WM_ * WN_) return ABShape<M_, N_, WM_, WN_, ST_>::LDS;
+    DG_AB_LADDER(DG_CASE)
+#undef DG_CASE
+    return -1;
+}
+
+int tiled_lds_bytes(int tm, int tn, int waves)
+{
+#define DG_CASE(M_, N_, W_) \
+    if (tm == M_ && tn == N_ && waves == W_) return TiledShape<M_, N_, W_ / 4, tiled_stages(W_)>::LDS;
+    DG_TILED_LADDER(DG_CASE)
 #undef DG_CASE
     return -1;
 }

@@ -44,7 +44,7 @@ struct Cand {
     bool screened;  // fails the padding screen
 };
 
-void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt)
+void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4)
 {
     memset(&t, 0, sizeof t);
     t.kernel = kernel;
@@ -52,28 +52,31 @@ void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt)
     t.tile_n = tn;
     t.tile_k = dt == GEMM_BF16 ? 64 : 128;
     t.atom = 16;
-    t.waves = 4;
+    t.waves = waves;
     t.k_split = kernel == GEMM_KERNEL_SKINNY ? 4 : 1;
     t.lds_stages = kernel == GEMM_KERNEL_TILED ? 2 : 0;
 }
 
-bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, const Chip& c,
-                 Cand& out)
+bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, int waves,
+                 const Chip& c, Cand& out)
 {
-    const int lds = tiled_lds_bytes(tm, tn);
-    const int vgpr = tiled_vgpr_estimate(tm, tn);
+    const int lds = tiled_lds_bytes(tm, tn, waves);
+    const int vgpr = tiled_vgpr_estimate(tm, tn, waves);
     if (lds < 0 || lds > c.lds_per_cu || vgpr > 512)
         return false;
     const int waves_per_simd = std::min(8, 512 / align8(vgpr));
-    const int occ = std::max(1, std::min(waves_per_simd, c.lds_per_cu / lds));
+    // workgroups per CU: each puts waves/4 waves on every SIMD
+    const int occ = std::max(1, std::min(waves_per_simd / (waves / 4), c.lds_per_cu / lds));
     const int e = dt == GEMM_BF16 ? 2 : 1;
     const int64_t nkt = cdiv(K * e, 128);
     const int64_t tiles_m = cdiv(M, tm), tiles_n = cdiv(N, tn);
     const int64_t tiles = tiles_m * tiles_n;
     const double flop_tile_kt = 2.0 * tm * tn * (128.0 / e);
     const double mfma = flop_tile_kt / c.mfma_flop_per_clk_cu[dt];
-    const double ldsc = (4.0 * tm * 128 + tm * 128) / c.lds_bytes_per_clk;
-    const double vmem = (double)(tm + tn) * 128 / c.vmem_bytes_per_clk;
+    // every wave reads its rows of A from LDS once per k-tile (the 4 wave
+    // columns share rows); B is read by every wave row
+    const double ldsc = (4.0 * tm * 128) / c.lds_bytes_per_clk;
+    const double vmem = (double)(tm + tn * (waves / 4)) * 128 / c.vmem_bytes_per_clk;
     const double per_kt = std::max(mfma, std::max(ldsc, vmem)) * (1.0 + 0.25 / occ);
     const double epi = (double)tm * tn * 2 / c.vmem_bytes_per_clk + 600.0;
     const double tile_cyc = nkt * per_kt + epi + 800.0;
@@ -81,11 +84,51 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int t
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt);
+    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves);
     const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
     const int64_t rounds = cdiv(tiles, cus);
     out.t.tile_eff = (float)te;
     out.t.wq_eff = (float)((double)tiles / ((double)rounds * cus));
+    out.t.predicted_us = (float)us;
+    out.us = us;
+    out.screened = 1.0 / te > 1.25;
+    return true;
+}
+
+// A and B staged in LDS: each k-tile enters the workgroup once; waves read
+// their A and B fragments from LDS.
+bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r, const Chip& c,
+              Cand& out)
+{
+    const int waves = r.wm * r.wn;
+    const int lds = ab_lds_bytes(r.tm, r.tn, waves);
+    if (lds < 0 || lds > c.lds_per_cu)
+        return false;
+    const int mr = r.tm / r.wm / 16, nr = r.tn / r.wn / 16;
+    const int vgpr = mr * nr * 4 + nr * 8 + 16 + 40;
+    const int waves_per_simd = std::min(8, 512 / align8(vgpr));
+    const int occ = std::max(1, std::min(waves_per_simd / std::max(1, waves / 4), c.lds_per_cu / lds));
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    const int64_t nkt = cdiv(K * e, 128);
+    const int64_t tiles_m = cdiv(M, r.tm), tiles_n = cdiv(N, r.tn);
+    const int64_t tiles = tiles_m * tiles_n;
+    const double flop_tile_kt = 2.0 * r.tm * r.tn * (128.0 / e);
+    const double mfma = flop_tile_kt / c.mfma_flop_per_clk_cu[dt];
+    const double ldsc = ((double)r.wn * r.tm * 128 + (double)r.wm * r.tn * 128) / c.lds_bytes_per_clk;
+    const double vmem = (double)(r.tm + r.tn) * 128 / c.vmem_bytes_per_clk;
+    const double per_kt = std::max(mfma, std::max(ldsc, vmem)) * (1.0 + 0.25 / occ);
+    const double epi = (double)r.tm * r.tn * 2 / c.vmem_bytes_per_clk + 600.0;
+    const double tile_cyc = nkt * per_kt + epi + 800.0;
+    const int64_t per_cu = cdiv(tiles, cus);
+    double us = per_cu * tile_cyc / c.clock_hz * 1e6;
+    const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
+    us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
+    fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves);
+    const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
+    const int64_t rounds = cdiv(tiles, cus);
+    out.t.tile_eff = (float)te;
+    out.t.wq_eff = (float)((double)tiles / ((double)rounds * cus));
+    out.t.lds_stages = r.st;
     out.t.predicted_us = (float)us;
     out.us = us;
     out.screened = 1.0 / te > 1.25;
@@ -121,23 +164,29 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int 
 
 }  // namespace
 
-int tiled_vgpr_estimate(int tm, int tn)
+int tiled_vgpr_estimate(int tm, int tn, int waves)
 {
-    const int mr = tm / 16, nr = tn / 64;
+    const int mr = tm / (waves / 4) / 16, nr = tn / 64;
     const int acc = mr * nr * 4;
-    const int b = nr * 2 * 4 * 2;          // current and next k-tile of B
-    const int a_stage = (tm * 8 / 256) * 4;
+    const int b = nr * 2 * 4 * tiled_stages(waves);  // B k-tiles in flight
     const int a_frag = 8;
-    const int misc = 32;                   // addresses, offsets, loop state
-    return acc + b + a_stage + a_frag + misc;
+    const int misc = 40;                      // addresses, offsets, loop state
+    return acc + b + a_frag + misc;
 }
 
-bool tiled_supported(int tm, int tn)
+bool tiled_supported(int tm, int tn, int waves)
 {
-    for (int m : kTiledTM)
-        for (int n : kTiledTN)
-            if (m == tm && n == tn)
-                return true;
+    for (const TiledRung& r : kTiledLadder)
+        if (r.tm == tm && r.tn == tn && r.waves == waves)
+            return true;
+    return false;
+}
+
+bool ab_supported(int tm, int tn, int waves)
+{
+    for (const ABRung& r : kABLadder)
+        if (r.tm == tm && r.tn == tn && r.wm * r.wn == waves)
+            return true;
     return false;
 }
 
@@ -172,12 +221,16 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
                     consider(cd);
             }
     }
-    for (int tm : kTiledTM)
-        for (int tn : kTiledTN) {
-            Cand cd;
-            if (price_tiled(M, N, K, dt, cus, tm, tn, chip, cd))
-                consider(cd);
-        }
+    for (const TiledRung& r : kTiledLadder) {
+        Cand cd;
+        if (price_tiled(M, N, K, dt, cus, r.tm, r.tn, r.waves, chip, cd))
+            consider(cd);
+    }
+    for (const ABRung& r : kABLadder) {
+        Cand cd;
+        if (price_ab(M, N, K, dt, cus, r, chip, cd))
+            consider(cd);
+    }
     *out = have ? best.t : best_screened.t;
 }
 

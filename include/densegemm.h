@@ -49,8 +49,9 @@ typedef enum {
 } gemm_dtype;
 
 typedef enum {
-    GEMM_KERNEL_TILED = 0,  /* block tiles, A double-buffered in LDS, B straight to VGPRs */
-    GEMM_KERNEL_SKINNY = 1  /* M <= 64: B streamed once, waves split K, LDS reduction    */
+    GEMM_KERNEL_TILED = 0,    /* block tiles, A pipelined through LDS, B straight to VGPRs */
+    GEMM_KERNEL_SKINNY = 1,   /* M <= 64: B streamed once, waves split K, LDS reduction    */
+    GEMM_KERNEL_TILED_AB = 2  /* block tiles, A and B both pipelined through LDS           */
 } gemm_kernel;
 
 /*
@@ -58,9 +59,15 @@ typedef enum {
  * (and for the skinny kernel k_split).  The remaining fields are reported by
  * select_tile for information and ignored when a tile is forced.
  *
- *   tiled:  tile_m in {32, 64, 128, 256}, tile_n in {64, 128, 256}; 4 waves of
- *           64 lanes split tile_n ("GEMM Optimization Guide" page, sections
- *           1.1 and 1.4); tile_k is 128 bytes of K (64 bf16 or 128 e4m3).
+ *   tiled:  (tile_m, tile_n, waves) in {256x128, 256x64, 128x256, 128x128,
+ *           128x64, 64x256, 64x128, 64x64, 32x256, 32x128, 32x64} with 4 waves
+ *           of 64 lanes splitting tile_n ("GEMM Optimization Guide" page,
+ *           sections 1.1 and 1.4), or {256x256, 256x128, 128x256, 128x128}
+ *           with 8 waves (2 rows x 4 columns); tile_k is 128 bytes of K (64
+ *           bf16 or 128 e4m3).
+ *   tiled_ab: (tile_m, tile_n, waves) in {256x256 x 8, 256x256 x 4,
+ *           256x128 x 4, 128x256 x 4, 128x128 x 4}; the waves form a 2 x
+ *           (waves/2) grid and A and B are both staged in LDS.
  *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering
  *           M), tile_n in {16, 32, 64} (16-column blocks per workgroup),
  *           k_split = waves that split K in one workgroup (4).
@@ -71,7 +78,7 @@ typedef struct {
     int32_t tile_n;
     int32_t tile_k;      /* elements of K per pipeline stage (informational) */
     int32_t atom;        /* MFMA block edge: 16 (informational) */
-    int32_t waves;       /* waves per workgroup (informational) */
+    int32_t waves;       /* waves per workgroup (selects the rung of a ladder) */
     int32_t k_split;     /* skinny: waves splitting K */
     int32_t lds_stages;  /* 2 = ping-pong A buffers (informational) */
     float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */

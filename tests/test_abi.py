@@ -60,8 +60,9 @@ def test_shuffle_b_bytes_fp8_layout_size():
 def test_select_tile_metrics_match_oracle(M, N, K, dt):
     t = dg.select_tile(M, N, K, dt, num_cus=256)
     assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY)
-    if t.kernel == dg.GEMM_KERNEL_TILED:
-        assert (t.tile_m, t.tile_n) in dg.TILED_LADDER
+    if t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB):
+        ladder = dg.TILED_LADDER if t.kernel == dg.GEMM_KERNEL_TILED else dg.AB_LADDER
+        assert (t.tile_m, t.tile_n, t.waves) in ladder
         tiles, te, we, de = oracle.dim_eff(M, N, t.tile_m, t.tile_n, 256)
         assert abs(t.tile_eff - te) < 1e-6 and abs(t.wq_eff - we) < 1e-6
         # padding screen: padded output at most 1.25x the real one when any tile passes
@@ -116,6 +117,8 @@ def test_gemm_bf16_argument_checks():
     assert _bf16(PA, 64, PB, PC, 64, 64, 64, 40) == U                 # K % 16 != 0
     assert _bf16(None, 0, None, None, 64, 64, 64, 0) == E              # K = 0 still needs C
     bad = dg.tiled(100, 64).to_c()
+    assert _bf16(PA, 64, PB, PC, 64, 64, 64, 64, ctypes.byref(bad)) == U
+    bad = dg.tiled(64, 64, 8).to_c()                                     # not a rung
     assert _bf16(PA, 64, PB, PC, 64, 64, 64, 64, ctypes.byref(bad)) == U
     bad = dg.skinny(16, 16).to_c()
     assert _bf16(PA, 64, PB, PC, 64, 17, 64, 64, ctypes.byref(bad)) == U   # M > skinny rows

@@ -92,10 +92,27 @@ def test_workload_shapes_sampled(name, smallint):
 EVERY_SHAPE = (263, 270, 176)   # divides no tile in M, N or the 64-element k-tile
 
 
-@pytest.mark.parametrize("tm,tn", dg.TILED_LADDER)
-def test_every_tiled_tile(tm, tn):
+@pytest.mark.parametrize("tm,tn,waves", dg.TILED_LADDER)
+def test_every_tiled_tile(tm, tn, waves):
     M, N, K = EVERY_SHAPE
-    tile = dg.tiled(tm, tn)
+    tile = dg.tiled(tm, tn, waves)
+    for smallint in (False, True):
+        A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
+                                      "smallint" if smallint else "normal", config=9)
+        C, ok = run("bf16", A, B, tile=tile)
+        assert ok, "guard band written"
+        Cref = oracle_full("bf16", A, B)
+        if smallint:
+            check_exact(C, Cref, tile.name)
+        else:
+            check_close("bf16", C, Cref, oracle_full("bf16", abs_bits("bf16", A), abs_bits("bf16", B)),
+                        K, what=tile.name)
+
+
+@pytest.mark.parametrize("tm,tn,waves", dg.AB_LADDER)
+def test_every_ab_tile(tm, tn, waves):
+    M, N, K = EVERY_SHAPE
+    tile = dg.tiled_ab(tm, tn, waves)
     for smallint in (False, True):
         A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
                                       "smallint" if smallint else "normal", config=9)
@@ -122,8 +139,10 @@ def test_every_skinny_tile(tm, tn, M):
 
 
 @pytest.mark.parametrize("K", [16, 48, 80, 144, 64, 128])
-@pytest.mark.parametrize("tile", [None, dg.tiled(64, 64), dg.tiled(256, 256), dg.skinny(32, 16)],
-                         ids=["auto", "t64x64", "t256x256", "s32x16"])
+@pytest.mark.parametrize("tile", [None, dg.tiled(64, 64), dg.tiled(256, 128), dg.tiled(256, 256, 8),
+                                  dg.tiled_ab(256, 256, 8), dg.tiled_ab(128, 128, 4), dg.skinny(32, 16)],
+                         ids=["auto", "t64x64", "t256x128", "t256x256w8", "ab256x256w8", "ab128x128",
+                              "s32x16"])
 def test_k_tails(K, tile):
     M, N = 30, 100
     A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=K)
