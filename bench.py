@@ -282,6 +282,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode measurement")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. tiled:256x256 or skinny:16x32")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
+                         "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
@@ -294,6 +297,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
@@ -376,6 +381,22 @@ def sweep(name: str, steps: int, warmup: int) -> int:
     print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
                       "best": best, "best_us": round(res[best], 3),
                       "regret": round(res[pick.name] / res[best], 4)}), flush=True)
+    return 0
+
+
+def copy_calibration(mib: int) -> int:
+    """Five device-to-device copies of a known size: under rocprofv3 --pmc the
+    copy kernel's FETCH_SIZE and WRITE_SIZE per dispatch, against mib MiB,
+    give the factor that turns those counters into HBM bytes."""
+    import torch
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
     return 0
 
 
