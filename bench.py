@@ -143,21 +143,25 @@ def gpu_setup(name: str, copies: int):
 
 
 def parse_tile(spec: str | None):
-    """'tiled:256x128', 'tiled:256x256w8', 'ab:256x256w8' or 'skinny:16x32' -> Tile;
-    None -> select_tile."""
+    """'tiled:256x128', 'tiled:256x256w8', 'ab:256x256w8a32' or 'skinny:16x32' -> Tile
+    (an 'a32' suffix selects the 32 x 32 MFMA atom); None -> select_tile."""
     if spec is None:
         return None
     import dense_gemm_linear_amd as dg
     kind, dims = spec.split(":")
+    atom = 16
+    if "a" in dims:
+        dims, a = dims.split("a")
+        atom = int(a)
     waves = 4
     if "w" in dims:
         dims, w = dims.split("w")
         waves = int(w)
     tm, tn = (int(x) for x in dims.split("x"))
     if kind == "tiled":
-        return dg.tiled(tm, tn, waves)
+        return dg.tiled(tm, tn, waves, atom)
     if kind == "ab":
-        return dg.tiled_ab(tm, tn, waves)
+        return dg.tiled_ab(tm, tn, waves, atom)
     return dg.skinny(tm, tn)
 
 

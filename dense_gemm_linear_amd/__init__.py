@@ -63,10 +63,11 @@ class Tile:
 
     @property
     def name(self) -> str:
+        atom = "" if self.atom in (0, 16) else f"a{self.atom}"
         if self.kernel == GEMM_KERNEL_TILED:
-            return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}")
+            return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}") + atom
         if self.kernel == GEMM_KERNEL_TILED_AB:
-            return f"ab{self.tile_m}x{self.tile_n}w{self.waves}"
+            return f"ab{self.tile_m}x{self.tile_n}w{self.waves}" + atom
         return f"skinny{self.tile_m}x{self.tile_n}"
 
     def to_c(self) -> GemmTile:
@@ -79,28 +80,34 @@ class Tile:
                     t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
 
 
-def tiled(tm: int, tn: int, waves: int = 4) -> Tile:
-    return Tile(GEMM_KERNEL_TILED, tm, tn, waves=waves)
+def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16) -> Tile:
+    return Tile(GEMM_KERNEL_TILED, tm, tn, atom=atom, waves=waves)
 
 
-def tiled_ab(tm: int, tn: int, waves: int = 4) -> Tile:
-    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, waves=waves)
+def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16) -> Tile:
+    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, atom=atom, waves=waves)
 
 
 def skinny(tm: int, tn: int) -> Tile:
     return Tile(GEMM_KERNEL_SKINNY, tm, tn, k_split=4, lds_stages=0)
 
 
-# (tile_m, tile_n, waves): 8-wave rungs arrange the waves 2 (M) x 4 (N)
-TILED_LADDER = [(256, 256, 8), (256, 128, 8), (128, 256, 8), (128, 128, 8)] + \
-    [(m, n, 4) for m in (256, 128, 64, 32) for n in (256, 128, 64) if (m, n) != (256, 256)]
-AB_LADDER = [(256, 256, 8), (256, 256, 4), (256, 128, 4), (128, 256, 4), (128, 128, 4)]
+# (tile_m, tile_n, waves, atom): 8-wave tiled rungs arrange the waves 2 (M) x 4 (N)
+TILED_LADDER = [(256, 128, 8, 16), (128, 256, 8, 16), (128, 128, 8, 16)] + \
+    [(m, n, 4, 16) for m in (256, 128, 64, 32) for n in (256, 128, 64) if (m, n) != (256, 256)] + \
+    [(256, 256, 8, 32), (256, 128, 8, 32), (128, 256, 8, 32), (128, 128, 8, 32),
+     (256, 128, 4, 32), (128, 256, 4, 32), (128, 128, 4, 32), (64, 256, 4, 32), (64, 128, 4, 32)]
+# (tile_m, tile_n, waves, atom): 8 waves form 2 x 4, 4 waves 2 x 2
+AB_LADDER = [(256, 128, 4, 16), (128, 256, 4, 16), (128, 128, 4, 16),
+             (256, 256, 8, 32), (256, 256, 4, 32), (256, 128, 8, 32), (256, 128, 4, 32),
+             (128, 256, 4, 32), (128, 128, 4, 32)]
 SKINNY_LADDER = [(m, n) for m in (16, 32, 48, 64) for n in (16, 32, 64)]
 
 
 def all_tiles(M: int):
     """Every rung usable for a GEMM with M rows."""
-    t = [tiled(m, n, w) for m, n, w in TILED_LADDER] + [tiled_ab(m, n, w) for m, n, w in AB_LADDER]
+    t = [tiled(m, n, w, a) for m, n, w, a in TILED_LADDER] + \
+        [tiled_ab(m, n, w, a) for m, n, w, a in AB_LADDER]
     if M <= 64:
         t += [skinny(m, n) for m, n in SKINNY_LADDER if M <= m < M + 16]
     return t

@@ -9,15 +9,16 @@ namespace dg {
 
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out);
 
-hipError_t launch_ab(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s)
+hipError_t launch_ab(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s)
 {
-    return dt == DT_BF16 ? launch_ab_bf16(tm, tn, waves, a, s) : launch_ab_fp8(tm, tn, waves, a, s);
+    return dt == DT_BF16 ? launch_ab_bf16(tm, tn, waves, atom, a, s)
+                         : launch_ab_fp8(tm, tn, waves, atom, a, s);
 }
 
-hipError_t launch_tiled(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s)
+hipError_t launch_tiled(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s)
 {
-    return dt == DT_BF16 ? launch_tiled_bf16(tm, tn, waves, a, s)
-                         : launch_tiled_fp8(tm, tn, waves, a, s);
+    return dt == DT_BF16 ? launch_tiled_bf16(tm, tn, waves, atom, a, s)
+                         : launch_tiled_fp8(tm, tn, waves, atom, a, s);
 }
 
 namespace {
@@ -57,15 +58,17 @@ gemm_status device_info(int* cus)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Is a forced tile usable for this shape?
-bool tile_feasible(const gemm_tile& t, int64_t M)
+// Is a forced tile usable for this shape?  (atom 0 means 16.)
+bool tile_feasible(gemm_tile& t, int64_t M)
 {
+    if (t.atom == 0)
+        t.atom = 16;
     if (t.kernel == GEMM_KERNEL_TILED)
-        return tiled_supported(t.tile_m, t.tile_n, t.waves);
+        return tiled_supported(t.tile_m, t.tile_n, t.waves, t.atom);
     if (t.kernel == GEMM_KERNEL_SKINNY)
         return skinny_supported(t.tile_m, t.tile_n) && M <= t.tile_m;
     if (t.kernel == GEMM_KERNEL_TILED_AB)
-        return ab_supported(t.tile_m, t.tile_n, t.waves);
+        return ab_supported(t.tile_m, t.tile_n, t.waves, t.atom);
     return false;
 }
 
@@ -133,8 +136,9 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     } else {
         a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
         a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
-        err = t.kernel == GEMM_KERNEL_TILED_AB ? launch_ab(dt, t.tile_m, t.tile_n, t.waves, a, s)
-                                               : launch_tiled(dt, t.tile_m, t.tile_n, t.waves, a, s);
+        err = t.kernel == GEMM_KERNEL_TILED_AB
+                  ? launch_ab(dt, t.tile_m, t.tile_n, t.waves, t.atom, a, s)
+                  : launch_tiled(dt, t.tile_m, t.tile_n, t.waves, t.atom, a, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

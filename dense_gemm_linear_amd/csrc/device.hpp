@@ -9,6 +9,7 @@ namespace dg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -69,6 +70,24 @@ __device__ __forceinline__ f32x4 mfma_bf16(i32x4 a, i32x4 b, f32x4 c)
 __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] * B[16x32].  Lane l holds
+// row (A) / column (B) l % 32 and the (l / 32)-th group of 8 K values; the
+// result lane l holds column l % 32 and, in element e, row
+// 8*(e/4) + 4*(l/32) + e%4.
+__device__ __forceinline__ f32x16 mfma_bf16_32(i32x4 a, i32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 operands, no block scales:
+// D[32x32] += A[32x64] * B[64x32], 32 K bytes per lane, lanes 32..63 holding
+// the second half of K.  Output layout as for mfma_bf16_32.
+__device__ __forceinline__ f32x16 mfma_fp8_32(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi)

@@ -11,51 +11,56 @@
 
 namespace dg {
 
-// Tiled ladder: (tile_m, tile_n, waves).  X(M, N, W) is applied to every rung.
+// Tiled ladder: (tile_m, tile_n, waves, atom).  X(M, N, W, R) is applied to
+// every rung.  8-wave rungs arrange the waves 2 (M) x 4 (N).
 #define DG_TILED_LADDER(X)                                                              \
-    X(256, 256, 8) X(256, 128, 8) X(128, 256, 8) X(128, 128, 8)                        \
-    X(256, 128, 4) X(256, 64, 4)                                                       \
-    X(128, 256, 4) X(128, 128, 4) X(128, 64, 4)                                        \
-    X(64, 256, 4) X(64, 128, 4) X(64, 64, 4)                                           \
-    X(32, 256, 4) X(32, 128, 4) X(32, 64, 4)
+    X(256, 128, 8, 16) X(128, 256, 8, 16) X(128, 128, 8, 16)                           \
+    X(256, 128, 4, 16) X(256, 64, 4, 16)                                               \
+    X(128, 256, 4, 16) X(128, 128, 4, 16) X(128, 64, 4, 16)                            \
+    X(64, 256, 4, 16) X(64, 128, 4, 16) X(64, 64, 4, 16)                               \
+    X(32, 256, 4, 16) X(32, 128, 4, 16) X(32, 64, 4, 16)                               \
+    X(256, 256, 8, 32) X(256, 128, 8, 32) X(128, 256, 8, 32) X(128, 128, 8, 32)        \
+    X(256, 128, 4, 32) X(128, 256, 4, 32) X(128, 128, 4, 32)                           \
+    X(64, 256, 4, 32) X(64, 128, 4, 32)
 
-// A+B-in-LDS ladder: (tile_m, tile_n, wave rows, wave columns, stages).
+// A+B-in-LDS ladder: (tile_m, tile_n, wave rows, wave columns, stages, atom).
 #define DG_AB_LADDER(X)                                                                 \
-    X(256, 256, 2, 4, 2) X(256, 256, 2, 2, 2) X(256, 128, 2, 2, 3) X(128, 256, 2, 2, 3)  \
-    X(128, 128, 2, 2, 3)
+    X(256, 128, 2, 2, 3, 16) X(128, 256, 2, 2, 3, 16) X(128, 128, 2, 2, 3, 16)          \
+    X(256, 256, 2, 4, 2, 32) X(256, 256, 2, 2, 2, 32) X(256, 128, 2, 4, 3, 32)          \
+    X(256, 128, 2, 2, 3, 32) X(128, 256, 2, 2, 3, 32) X(128, 128, 2, 2, 3, 32)
 
 struct ABRung {
-    int tm, tn, wm, wn, st;
+    int tm, tn, wm, wn, st, atom;
 };
 constexpr ABRung kABLadder[] = {
-#define DG_ABR(M_, N_, WM_, WN_, ST_) {M_, N_, WM_, WN_, ST_},
+#define DG_ABR(M_, N_, WM_, WN_, ST_, R_) {M_, N_, WM_, WN_, ST_, R_},
     DG_AB_LADDER(DG_ABR)
 #undef DG_ABR
 };
 
 struct TiledRung {
-    int tm, tn, waves;
+    int tm, tn, waves, atom;
 };
 constexpr TiledRung kTiledLadder[] = {
-#define DG_RUNG(M_, N_, W_) {M_, N_, W_},
+#define DG_RUNG(M_, N_, W_, R_) {M_, N_, W_, R_},
     DG_TILED_LADDER(DG_RUNG)
 #undef DG_RUNG
 };
 constexpr int kSkinnyTM[] = {16, 32, 48, 64};
 constexpr int kSkinnyTN[] = {16, 32, 64};
 
-bool tiled_supported(int tm, int tn, int waves);
-bool ab_supported(int tm, int tn, int waves);
+bool tiled_supported(int tm, int tn, int waves, int atom);
+bool ab_supported(int tm, int tn, int waves, int atom);
 bool skinny_supported(int tm, int tn);
 
 // Launchers: return hipSuccess or the launch error.  Grids are computed from
 // the arguments; shapes are validated by the caller.
-hipError_t launch_tiled(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_bf16(int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_fp8(int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_bf16(int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_fp8(int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled_bf16(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled_fp8(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab_bf16(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab_fp8(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int dt, int tm, int tn, const GemmArgs& a, hipStream_t s);
 hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
@@ -72,8 +77,8 @@ inline hipError_t launch_args(F* kernel, dim3 grid, dim3 block, const GemmArgs& 
 }
 
 // Resource model of the tiled kernel (used by select_tile's feasibility check).
-int tiled_lds_bytes(int tm, int tn, int waves);
-int ab_lds_bytes(int tm, int tn, int waves);
-int tiled_vgpr_estimate(int tm, int tn, int waves);
+int tiled_lds_bytes(int tm, int tn, int waves, int atom);
+int ab_lds_bytes(int tm, int tn, int waves, int atom);
+int tiled_vgpr_estimate(int tm, int tn, int waves, int atom);
 
 }  // namespace dg

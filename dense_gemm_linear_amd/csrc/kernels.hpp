@@ -103,49 +103,130 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int TM, int TN, int WM, int ST>
-struct TiledShape {
-    static constexpr int WAVES = 4 * WM;          // WM rows x 4 columns of waves
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int MR = TM / WM / 16;       // 16-row MFMA blocks per wave
-    static constexpr int NR = TN / 64;            // 16-column blocks per wave
-    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
-    static constexpr int A_BUF = TM * 128;        // bytes of one A stage
-    static constexpr int LOADS = A_DMA + 2 * NR;  // vector-memory ops per wave per k-tile
-    static constexpr int WCOLS = TN / 4;          // C columns per wave
-    static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
-    static constexpr int fit_ch()
+// ---------------------------------------------------------------------------
+// MFMA atoms.  An atom is one R x R block of C computed by one MFMA per K
+// step.  A k-tile (128 bytes of K) takes STEPS MFMAs along K, and for each
+// one every lane supplies P 16-byte pieces of A and P of B.  Piece p of step
+// s holds the same K bytes of the k-tile in the A operand and in the B
+// operand, which is all the sum over K needs to pair A[m][k] with B[n][k]:
+//   A: row (lane % R) of the atom in the LDS A tile, 16-byte chunk a_chunk;
+//   B: column (lane % R) of the atom, in the 64-byte half b_half of the
+//      k-tile (one 1 KiB block of the preshuffled B) and lane group b_group.
+// Output element e of lane l sits at row out_row(e, l), column l % R.
+//
+// The 16 x 16 atoms are the pages' choice ("GEMM Optimization Guide" page,
+// section 6.1).  On MI355X the 32 x 32 bf16 MFMA sustains the full dense
+// rate with its accumulators in ordinary VGPRs, while back-to-back 16 x 16 x
+// 32 bf16 MFMAs accumulating in VGPRs issue at roughly half of it (measured),
+// so the large tiles use 32 x 32 atoms.
+template <int DT, int R>
+struct Atom;
+
+template <>
+struct Atom<DT_BF16, 16> {   // v_mfma_f32_16x16x32_bf16
+    static constexpr int R = 16, STEPS = 2, P = 1, NACC = 4;
+    using acc_t = f32x4;
+    static __device__ __forceinline__ int a_chunk(int s, int l, int) { return 4 * s + (l >> 4); }
+    static __device__ __forceinline__ int b_half(int s, int) { return s; }
+    static __device__ __forceinline__ int b_group(int, int l, int) { return l >> 4; }
+    static __device__ __forceinline__ int out_row(int e, int l) { return 4 * (l >> 4) + e; }
+    static __device__ __forceinline__ acc_t mma(const i32x4 (&a)[P], const i32x4 (&b)[P], acc_t c)
     {
-        int ch = MR;
-        while (ch > 1 && (WAVES * ch * 16 * SROW > ST * A_BUF || MR % ch != 0))
-            --ch;
-        return ch;
+        return mfma_bf16(a[0], b[0], c);
     }
-    static constexpr int CH = fit_ch();           // 16-row blocks per epilogue pass
-    static constexpr int LDS = (ST * A_BUF > WAVES * CH * 16 * SROW) ? ST * A_BUF
-                                                                     : WAVES * CH * 16 * SROW;
-    static_assert(TM % (32 * WM) == 0 && TN % 64 == 0 && A_DMA >= 1, "tile shape");
-    static_assert(ST >= 2 && (ST - 2) * LOADS <= 63, "pipeline depth");
 };
+
+template <>
+struct Atom<DT_BF16, 32> {   // v_mfma_f32_32x32x16_bf16
+    static constexpr int R = 32, STEPS = 4, P = 1, NACC = 16;
+    using acc_t = f32x16;
+    static __device__ __forceinline__ int a_chunk(int s, int l, int) { return 2 * s + (l >> 5); }
+    static __device__ __forceinline__ int b_half(int s, int) { return s >> 1; }
+    static __device__ __forceinline__ int b_group(int s, int l, int) { return 2 * (s & 1) + (l >> 5); }
+    static __device__ __forceinline__ int out_row(int e, int l) { return 8 * (e >> 2) + 4 * (l >> 5) + (e & 3); }
+    static __device__ __forceinline__ acc_t mma(const i32x4 (&a)[P], const i32x4 (&b)[P], acc_t c)
+    {
+        return mfma_bf16_32(a[0], b[0], c);
+    }
+};
+
+template <>
+struct Atom<DT_FP8, 16> {    // v_mfma_scale_f32_16x16x128_f8f6f4
+    static constexpr int R = 16, STEPS = 1, P = 2, NACC = 4;
+    using acc_t = f32x4;
+    static __device__ __forceinline__ int a_chunk(int, int l, int p) { return 4 * p + (l >> 4); }
+    static __device__ __forceinline__ int b_half(int, int p) { return p; }
+    static __device__ __forceinline__ int b_group(int, int l, int) { return l >> 4; }
+    static __device__ __forceinline__ int out_row(int e, int l) { return 4 * (l >> 4) + e; }
+    static __device__ __forceinline__ acc_t mma(const i32x4 (&a)[P], const i32x4 (&b)[P], acc_t c)
+    {
+        return mfma_fp8(cat(a[0], a[1]), cat(b[0], b[1]), c);
+    }
+};
+
+template <>
+struct Atom<DT_FP8, 32> {    // v_mfma_scale_f32_32x32x64_f8f6f4
+    static constexpr int R = 32, STEPS = 2, P = 2, NACC = 16;
+    using acc_t = f32x16;
+    static __device__ __forceinline__ int a_chunk(int s, int l, int p) { return 4 * s + 2 * (l >> 5) + p; }
+    static __device__ __forceinline__ int b_half(int s, int) { return s; }
+    static __device__ __forceinline__ int b_group(int, int l, int p) { return 2 * (l >> 5) + p; }
+    static __device__ __forceinline__ int out_row(int e, int l) { return 8 * (e >> 2) + 4 * (l >> 5) + (e & 3); }
+    static __device__ __forceinline__ acc_t mma(const i32x4 (&a)[P], const i32x4 (&b)[P], acc_t c)
+    {
+        return mfma_fp8_32(cat(a[0], a[1]), cat(b[0], b[1]), c);
+    }
+};
+
+template <class AT>
+__device__ __forceinline__ typename AT::acc_t zero_acc()
+{
+    typename AT::acc_t z;
+#pragma unroll
+    for (int e = 0; e < AT::NACC; ++e)
+        z[e] = 0.f;
+    return z;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The A tile of one k-tile in LDS: TM rows of 128 bytes, the 16-byte chunk c
+// of row r stored at slot c ^ ((r >> 1) & 7) ("GEMM Optimization Guide"
+// page, section 3: an XOR swizzle at 16-byte granularity, applied on both
+// the write and the read side).  The global -> LDS copy is a 16-byte LDS DMA
+// per lane (page section 11: 16 bytes per op on gfx950): one wave load fills
+// one 1 KiB chunk = 8 rows, lane l landing at row l / 8, slot l % 8, so the
+// swizzle is applied to the global address instead.
+struct ADma {
+    uint32_t goff;   // byte offset of this lane's 16 bytes in the A slab (k-tile 0)
+    uint32_t col;    // its K byte within the k-tile (for the K-tail mask)
+};
+
+__device__ __forceinline__ ADma a_dma_lane(int chunk, int lane, int64_t lda_b)
+{
+    const uint32_t row = 8 * (uint32_t)chunk + (uint32_t)(lane >> 3);
+    const uint32_t col = (uint32_t)(lane & 7) ^ ((row >> 1) & 7);
+    return {row * (uint32_t)lda_b + col * 16, col * 16};
+}
+
 // Epilogue shared by the tiled kernels: scale (e4m3), round to bf16, stage a
-// wave's (MR*16) x (NR*16) accumulator block through its private LDS region
-// CH row blocks at a time, and store 16-byte row pieces ("GEMM Optimization
+// wave's (MR*R) x (NR*R) accumulator block through its private LDS region
+// CH atom rows at a time, and store 16-byte row pieces ("GEMM Optimization
 // Guide" page, section 7.2).  Rows past M fall outside the C descriptor; the
 // column predicate keeps a row's padding and the next row intact, and odd
 // leading dimensions or an unaligned C take 2-byte stores.
-template <int DT, int MR, int NR, int CH, int SROW, int WCOLS>
-__device__ __forceinline__ void store_c_tile(const GemmArgs& p, const f32x4 (&acc)[MR][NR],
+template <int DT, class AT, int MR, int NR, int CH, int SROW, int WCOLS>
+__device__ __forceinline__ void store_c_tile(const GemmArgs& p,
+                                             const typename AT::acc_t (&acc)[MR][NR],
                                              uint8_t* stage, int m0, int rows, int col_w, int row0,
                                              int lane, float scale_a, float scale_b)
 {
-    const int r16 = lane & 15, g4 = lane >> 4;
+    constexpr int R = AT::R;
     const rsrc_t rc = make_rsrc(p.C + (int64_t)m0 * p.ldc,
                                 (uint32_t)(((int64_t)(rows - 1) * p.ldc + p.N) * 2));
     constexpr int PPR = WCOLS / 8;                 // 16-byte pieces per staged row
-    constexpr int PIECES = CH * 16 * PPR;
+    constexpr int PIECES = CH * R * PPR;
+    const int lc = lane % R;
 #pragma unroll
     for (int cc = 0; cc < MR / CH; ++cc) {
 #pragma unroll
@@ -153,12 +234,12 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p, const f32x4 (&ac
 #pragma unroll
             for (int j = 0; j < NR; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = acc[cc * CH + ml][j][i];
+                for (int e = 0; e < AT::NACC; ++e) {
+                    float v = acc[cc * CH + ml][j][e];
                     if constexpr (DT == DT_FP8)
                         v = (v * scale_a) * scale_b;
-                    const int row = ml * 16 + 4 * g4 + i;
-                    const int col = j * 16 + r16;
+                    const int row = ml * R + AT::out_row(e, lane);
+                    const int col = j * R + lc;
                     *reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2) = bf16_rne(v);
                 }
         __syncthreads();
@@ -168,7 +249,7 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p, const f32x4 (&ac
             if (PIECES % 64 == 0 || q < PIECES) {
                 const int prow = q / PPR, pc = q % PPR;
                 const i32x4 v = *reinterpret_cast<const i32x4*>(stage + prow * SROW + pc * 16);
-                const int trow = row0 + cc * CH * 16 + prow;   // row within the tile
+                const int trow = row0 + cc * CH * R + prow;   // row within the tile
                 const int gcol = col_w + pc * 8;
                 const uint32_t off = (uint32_t)(((int64_t)trow * p.ldc + gcol) * 2);
                 if (p.c_vec && gcol + 8 <= p.N) {
@@ -185,14 +266,86 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p, const f32x4 (&ac
     }
 }
 
+// Largest CH dividing MR whose staging (WAVES regions of CH*R rows) fits in
+// `avail` bytes of LDS.
+constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
+{
+    int ch = MR;
+    while (ch > 1 && (WAVES * ch * R * SROW > avail || MR % ch != 0))
+        --ch;
+    return ch;
+}
 
+// Barrier without the workgroup memory fence of __syncthreads (which would
+// drain every outstanding load, prefetches included); an explicit vmcnt wait
+// before it is what makes the next stage visible.
+__device__ __forceinline__ void stage_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-template <int DT, int TM, int TN, int WM, int ST>
+// Issue order of one k-tile's LDS reads and MFMAs: the reads of step 0, then
+// the MFMAs of each step with the next step's reads spread between them, so
+// that reads are in flight while MFMAs issue.
+template <int STEPS, int MF, int RD>
+__device__ __forceinline__ void schedule_ktile()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        if (s + 1 < STEPS) {
+#pragma unroll
+            for (int i = 0; i < MF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < RD)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (RD > MF)
+                __builtin_amdgcn_sched_group_barrier(0x100, RD > MF ? RD - MF : 1, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel ("GEMM Optimization Guide" page, sections 1, 2, 3, 4, 6, 7):
+// WM x 4 waves, the 4 wave columns splitting tile_n (section 1.1); A through
+// LDS (ST-stage ring fed by LDS DMA), B straight from the preshuffled layout
+// into VGPRs (section 4.2), ST - 1 k-tiles ahead.
+template <int TM, int TN, int WM, int ST, int R>
+struct TiledShape {
+    static constexpr int WAVES = 4 * WM;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int MR = TM / WM / R;        // atoms per wave along M
+    static constexpr int NR = TN / 4 / R;         // atoms per wave along N
+    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
+    static constexpr int A_BUF = TM * 128;        // bytes of one A stage
+    static constexpr int B_LOADS = TN / 32;       // 16-byte B loads per lane per k-tile
+    static constexpr int LOADS = A_DMA + B_LOADS; // vector-memory ops per wave per k-tile
+    static constexpr int WCOLS = TN / 4;          // C columns per wave
+    static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
+    static constexpr int CH = fit_stage_rows(MR, WAVES, R, SROW, ST * A_BUF);
+    static constexpr int LDS = (ST * A_BUF > WAVES * CH * R * SROW) ? ST * A_BUF
+                                                                    : WAVES * CH * R * SROW;
+    static_assert(MR >= 1 && NR >= 1 && MR * WM * R == TM && NR * 4 * R == TN, "tile shape");
+    static_assert(A_DMA >= 1 && A_DMA * 8 * WAVES == TM, "A DMA split");
+    static_assert(ST >= 2 && ST <= 4 && (ST - 2) * LOADS <= 63, "pipeline depth");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int DT, int TM, int TN, int WM, int ST, int R>
 __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 {
-    using S = TiledShape<TM, TN, WM, ST>;
+    using S = TiledShape<TM, TN, WM, ST, R>;
+    using AT = Atom<DT, R>;
+    using acc_t = typename AT::acc_t;
     constexpr int MR = S::MR, NR = S::NR, A_DMA = S::A_DMA, A_BUF = S::A_BUF;
-    constexpr int WAVES = S::WAVES;
+    constexpr int WAVES = S::WAVES, STEPS = AT::STEPS, P = AT::P;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
 
     const int tid = threadIdx.x;
@@ -214,32 +367,24 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
                                 (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 
-    // A: global -> LDS without registers (16-byte LDS DMA per lane).  One
-    // load of a wave fills one 1 KiB chunk = 8 rows of 128 bytes; lane l
-    // lands at chunk + 16*l, i.e. row l/8, 16-byte slot l%8.  The XOR swizzle
-    // ("GEMM Optimization Guide" page, section 3) is applied on the global
-    // side: the slot holds the column (slot ^ ((row >> 1) & 7)).  Wave w
-    // fills chunks w, w + WAVES, ...
-    uint32_t a_goff[A_DMA], a_col[A_DMA];
+    ADma ad[A_DMA];
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        const uint32_t row = 8 * (wave + WAVES * i) + (lane >> 3);
-        const uint32_t col = (lane & 7) ^ ((row >> 1) & 7);
-        a_goff[i] = row * (uint32_t)p.lda_b + col * 16;
-        a_col[i] = col * 16;
-    }
-    const uint32_t b_base = (uint32_t)(wn * NR) * (uint32_t)p.KB * 1024u + lane * 16;
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const uint32_t swz = (r16 >> 1) & 7;
+    for (int i = 0; i < A_DMA; ++i)
+        ad[i] = a_dma_lane(wave + WAVES * i, lane, p.lda_b);
+    const int lr = lane % R;                       // row / column of this lane in an atom
+    const uint32_t swz = (uint32_t)((lane & 15) >> 1) & 7;
     const uint32_t row0 = (uint32_t)(wm * (TM / WM));   // first A row of this wave
+    // 16-column block of this lane's column in atom 0 of this wave
+    const uint32_t bblk = (uint32_t)(wn * NR * (R / 16) + (lr >> 4));
+    const uint32_t b_lane = bblk * (uint32_t)p.KB * 1024u + (uint32_t)(lane & 15) * 16;
 
-    i32x4 breg[ST][NR][2];
-    f32x4 acc[MR][NR];
+    i32x4 breg[ST][NR][STEPS][P];
+    acc_t acc[MR][NR];
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
         for (int j = 0; j < NR; ++j)
-            acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[mi][j] = zero_acc<AT>();
 
     // A k-tile past the real K (kt >= nkt, or the K tail of the last one)
     // loads through out-of-range offsets: zeros, and no memory traffic.
@@ -248,77 +393,54 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         const bool mask = kt >= last_full;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            uint32_t off = a_goff[i] + (uint32_t)kt * 128;
-            if (mask && (int)((uint32_t)kt * 128 + a_col[i]) >= p.KA_b)
+            uint32_t off = ad[i].goff + (uint32_t)kt * 128;
+            if (mask && (int)((uint32_t)kt * 128 + ad[i].col) >= p.KA_b)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(lds + stage * A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
         }
     };
-    auto load_b = [&](i32x4 (&dst)[NR][2], int kt) __attribute__((always_inline)) {
+    auto load_b = [&](i32x4 (&dst)[NR][STEPS][P], int kt) __attribute__((always_inline)) {
         const bool mask = kt >= last_full;
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int kb = kt * 2 + c;
-                uint32_t off = b_base + (uint32_t)(j * p.KB + kb) * 1024u;
-                if (mask && kb >= p.KB)
-                    off = kOOB;
-                dst[j][c] = load16(rb, off);
+            for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+                for (int q = 0; q < P; ++q) {
+                    const int kb = kt * 2 + AT::b_half(s, q);
+                    uint32_t off = b_lane + (uint32_t)(j * (R / 16) * p.KB + kb) * 1024u +
+                                   ((uint32_t)AT::b_group(s, lane, q) << 8);
+                    if (mask && kb >= p.KB)
+                        off = kOOB;
+                    dst[j][s][q] = load16(rb, off);
+                }
+    };
+    auto read_a = [&](int stage, int s, i32x4 (&dst)[MR][P]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const uint32_t row = row0 + (uint32_t)(mi * R + lr);
+                const uint32_t off = (uint32_t)(stage * A_BUF) + row * 128 +
+                                     (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+                dst[mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
     };
-    auto lds_a = [&](int stage, int mi, int col16) __attribute__((always_inline)) -> i32x4 {
-        const uint32_t off = (uint32_t)(stage * A_BUF) + (row0 + (uint32_t)(mi * 16 + r16)) * 128 +
-                             (((uint32_t)col16 ^ swz) << 4);
-        return *reinterpret_cast<const i32x4*>(lds + off);
-    };
-    // MFMAs of one k-tile.  The group barriers fix the issue order: the LDS
-    // reads of the first DG_LDS_AHEAD A fragments, then for every fragment its
-    // NR MFMAs followed by the read of the fragment DG_LDS_AHEAD places ahead,
-    // so that many reads are in flight while MFMAs issue (instead of all reads
-    // up front, which costs registers the pipeline needs, or one at a time,
-    // which exposes the LDS latency).
-    auto compute = [&](int stage, const i32x4 (&b)[NR][2]) __attribute__((always_inline)) {
-        constexpr int F = DT == DT_BF16 ? 2 * MR : MR;        // A fragments per k-tile
-        constexpr int RPF = DT == DT_BF16 ? 1 : 2;             // reads per fragment
-        constexpr int D = DG_LDS_AHEAD < F ? DG_LDS_AHEAD : F;
-        if constexpr (DT == DT_BF16) {
+    auto compute = [&](int stage, const i32x4 (&b)[NR][STEPS][P]) __attribute__((always_inline)) {
+        i32x4 af[2][MR][P];
+        read_a(stage, 0, af[0]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < STEPS; ++s) {
+            if (s + 1 < STEPS)
+                read_a(stage, s + 1, af[(s + 1) & 1]);
 #pragma unroll
-                for (int mi = 0; mi < MR; ++mi) {
-                    const i32x4 a = lds_a(stage, mi, 4 * s + g4);
-#pragma unroll
-                    for (int j = 0; j < NR; ++j)
-                        acc[mi][j] = mfma_bf16(a, b[j][s], acc[mi][j]);
-                }
-        } else {
-#pragma unroll
-            for (int mi = 0; mi < MR; ++mi) {
-                const i32x8 a = cat(lds_a(stage, mi, g4), lds_a(stage, mi, 4 + g4));
+            for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
-                    acc[mi][j] = mfma_fp8(a, cat(b[j][0], b[j][1]), acc[mi][j]);
-            }
+                    acc[mi][j] = AT::mma(af[s & 1][mi], b[j][s], acc[mi][j]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, D * RPF, 0);
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
-            if (f + D < F)
-                __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
-        }
-    };
-    // Barrier without the workgroup memory fence of __syncthreads (which would
-    // drain every outstanding load, prefetches included); the explicit
-    // vmcnt wait before it is what makes the next stage visible.
-    auto barrier = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
+        schedule_ktile<STEPS, MR * NR, MR * P>();
     };
 
     // Prologue: k-tiles 0 .. ST-2 in flight, wait for k-tile 0.
@@ -328,7 +450,7 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         load_b(breg[t], t);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-    barrier();
+    stage_barrier();
 
     // Phase t multiplies k-tile t out of stage t % ST while k-tile t + ST - 1
     // streams into the stage that phase t - 1 just finished with.  At the end
@@ -342,12 +464,11 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         __builtin_amdgcn_sched_barrier(0);
         compute(s, breg[s]);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-        barrier();
+        stage_barrier();
     };
     // Steady state: ST unconditional phases per trip (no control-flow merges
     // inside the loop, so the accumulators keep their registers); the last
     // nkt % ST k-tiles run after it.
-    static_assert(ST <= 4, "phases are spelled out for up to 4 stages");
     int kt = 0;
     for (; kt + ST <= p.nkt; kt += ST) {
         phase(kt, std::integral_constant<int, 0>{});
@@ -377,9 +498,9 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    store_c_tile<DT, MR, NR, S::CH, S::SROW, S::WCOLS>(p, acc, lds + wave * (S::CH * 16 * S::SROW),
-                                                      m0, rows, n0 + wn * S::WCOLS, (int)row0,
-                                                      lane, scale_a, scale_b);
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+        p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
+        scale_a, scale_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -387,19 +508,19 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 //
 // Loading a B fragment straight into the registers of every wave that needs
 // it (the kernel above) moves it from L2 once per wave row; measured on
-// MI355X, the L2 -> CU path, not the MFMA, bounds both kernels once the tile
+// MI355X, the L2 -> CU path, not the MFMA, bounds that kernel once the tile
 // is large.  Here each k-tile of A *and* B enters the workgroup once, by
 // 16-byte LDS DMA, and the WM x WN waves read their fragments from LDS.  The
-// preshuffled B blocks (1 KiB = one MFMA operand per 64 lanes) land in LDS
-// unchanged, so B fragment reads are contiguous 1 KiB ds_read_b128s.
-// Per k-tile and stage: [A: TM rows x 128 B, XOR-swizzled][B: TN/16 blocks x
-// 2 halves x 1 KiB].
-template <int TM, int TN, int WM, int WN, int ST>
+// preshuffled B blocks (1 KiB = 16 columns x 64 K bytes) land in LDS
+// unchanged, so a B fragment read is a run of 256 contiguous bytes per 16
+// lanes.  Per stage: [A: TM rows x 128 B, XOR-swizzled][B: TN/16 blocks x 2
+// halves x 1 KiB].
+template <int TM, int TN, int WM, int WN, int ST, int R>
 struct ABShape {
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int MR = TM / WM / 16;       // 16-row MFMA blocks per wave
-    static constexpr int NR = TN / WN / 16;       // 16-column blocks per wave
+    static constexpr int MR = TM / WM / R;        // atoms per wave along M
+    static constexpr int NR = TN / WN / R;        // atoms per wave along N
     static constexpr int A_BUF = TM * 128;
     static constexpr int B_BUF = TN * 128;
     static constexpr int STAGE = A_BUF + B_BUF;
@@ -408,28 +529,25 @@ struct ABShape {
     static constexpr int LOADS = A_DMA + B_DMA;
     static constexpr int WCOLS = TN / WN;         // C columns per wave
     static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
-    static constexpr int fit_ch()
-    {
-        int ch = MR;
-        while (ch > 1 && (WAVES * ch * 16 * SROW > ST * STAGE || MR % ch != 0))
-            --ch;
-        return ch;
-    }
-    static constexpr int CH = fit_ch();
-    static constexpr int LDS = (ST * STAGE > WAVES * CH * 16 * SROW) ? ST * STAGE
-                                                                     : WAVES * CH * 16 * SROW;
+    static constexpr int CH = fit_stage_rows(MR, WAVES, R, SROW, ST * STAGE);
+    static constexpr int LDS = (ST * STAGE > WAVES * CH * R * SROW) ? ST * STAGE
+                                                                    : WAVES * CH * R * SROW;
+    static_assert(MR >= 1 && NR >= 1 && MR * WM * R == TM && NR * WN * R == TN, "tile shape");
     static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * 8 * WAVES == TM && B_DMA * 8 * WAVES == TN,
                   "DMA split");
     static_assert(ST >= 2 && ST <= 4 && (ST - 2) * LOADS <= 63, "pipeline depth");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int WN, int ST>
+template <int DT, int TM, int TN, int WM, int WN, int ST, int R>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 {
-    using S = ABShape<TM, TN, WM, WN, ST>;
+    using S = ABShape<TM, TN, WM, WN, ST, R>;
+    using AT = Atom<DT, R>;
+    using acc_t = typename AT::acc_t;
     constexpr int MR = S::MR, NR = S::NR, A_BUF = S::A_BUF, STAGE = S::STAGE;
     constexpr int WAVES = S::WAVES, A_DMA = S::A_DMA, B_DMA = S::B_DMA;
+    constexpr int STEPS = AT::STEPS, P = AT::P;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
 
     const int tid = threadIdx.x;
@@ -448,33 +566,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
                                 (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 
-    // A chunk w + WAVES*i: rows 8c .. 8c+7 (swizzled on the global side as in
-    // the kernel above).  B chunk w + WAVES*i: block b / 2, half b % 2.
-    uint32_t a_goff[A_DMA], a_col[A_DMA], b_goff[B_DMA], b_half[B_DMA];
+    // A chunk w + WAVES*i: rows 8c .. 8c+7.  B chunk w + WAVES*i: 16-column
+    // block b / 2, 64-byte half b % 2 of the k-tile.
+    ADma ad[A_DMA];
+    uint32_t b_goff[B_DMA], b_half[B_DMA];
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        const uint32_t row = 8 * (wave + WAVES * i) + (lane >> 3);
-        const uint32_t col = (lane & 7) ^ ((row >> 1) & 7);
-        a_goff[i] = row * (uint32_t)p.lda_b + col * 16;
-        a_col[i] = col * 16;
-    }
+    for (int i = 0; i < A_DMA; ++i)
+        ad[i] = a_dma_lane(wave + WAVES * i, lane, p.lda_b);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
         const uint32_t b = wave + WAVES * i;
         b_goff[i] = ((b >> 1) * (uint32_t)p.KB + (b & 1)) * 1024u + lane * 16;
         b_half[i] = b & 1;
     }
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const uint32_t swz = (r16 >> 1) & 7;
+    const int lr = lane % R;
+    const uint32_t swz = (uint32_t)((lane & 15) >> 1) & 7;
     const uint32_t row0 = (uint32_t)(wm * (TM / WM));
-    const uint32_t bblk0 = (uint32_t)(wn * NR);          // first B block of this wave
+    // LDS byte offset (within a stage's B region) of this lane's column in
+    // atom 0 of this wave, group 0, half 0.
+    const uint32_t b_lds = (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * 2048 + (lane & 15) * 16);
 
-    f32x4 acc[MR][NR];
+    acc_t acc[MR][NR];
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
         for (int j = 0; j < NR; ++j)
-            acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[mi][j] = zero_acc<AT>();
 
     const int last_full = p.tail ? p.nkt - 1 : p.nkt;
     auto load = [&](int kt, int stage) __attribute__((always_inline)) {
@@ -482,8 +599,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         uint8_t* base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            uint32_t off = a_goff[i] + (uint32_t)kt * 128;
-            if (mask && (int)((uint32_t)kt * 128 + a_col[i]) >= p.KA_b)
+            uint32_t off = ad[i].goff + (uint32_t)kt * 128;
+            if (mask && (int)((uint32_t)kt * 128 + ad[i].col) >= p.KA_b)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -497,73 +614,42 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
                 rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
         }
     };
-    auto lds_a = [&](int stage, int mi, int col16) __attribute__((always_inline)) -> i32x4 {
-        const uint32_t off = (uint32_t)(stage * STAGE) + (row0 + (uint32_t)(mi * 16 + r16)) * 128 +
-                             (((uint32_t)col16 ^ swz) << 4);
-        return *reinterpret_cast<const i32x4*>(lds + off);
+    auto read_frags = [&](int stage, int s, i32x4 (&af)[MR][P], i32x4 (&bf)[NR][P])
+                          __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) + b_lds +
+                                     (uint32_t)(j * (R / 16) * 2048) +
+                                     ((uint32_t)AT::b_half(s, q) << 10) +
+                                     ((uint32_t)AT::b_group(s, lane, q) << 8);
+                bf[j][q] = *reinterpret_cast<const i32x4*>(lds + off);
+            }
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const uint32_t row = row0 + (uint32_t)(mi * R + lr);
+                const uint32_t off = (uint32_t)(stage * STAGE) + row * 128 +
+                                     (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+                af[mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
+            }
     };
-    auto lds_b = [&](int stage, int j, int half) __attribute__((always_inline)) -> i32x4 {
-        const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) +
-                             (((bblk0 + (uint32_t)j) * 2 + (uint32_t)half) << 10) + lane * 16;
-        return *reinterpret_cast<const i32x4*>(lds + off);
-    };
-    // One k-tile: per K step the NR B fragments, then the A fragments streamed
-    // DG_LDS_AHEAD ahead of their NR MFMAs each.
     auto compute = [&](int stage) __attribute__((always_inline)) {
-        if constexpr (DT == DT_BF16) {
+        i32x4 af[2][MR][P], bf[2][NR][P];
+        read_frags(stage, 0, af[0], bf[0]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                i32x4 bf[NR];
+        for (int s = 0; s < STEPS; ++s) {
+            if (s + 1 < STEPS)
+                read_frags(stage, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
 #pragma unroll
-                for (int j = 0; j < NR; ++j)
-                    bf[j] = lds_b(stage, j, s);
-#pragma unroll
-                for (int mi = 0; mi < MR; ++mi) {
-                    const i32x4 a = lds_a(stage, mi, 4 * s + g4);
-#pragma unroll
-                    for (int j = 0; j < NR; ++j)
-                        acc[mi][j] = mfma_bf16(a, bf[j], acc[mi][j]);
-                }
-            }
-            constexpr int D = DG_LDS_AHEAD < MR ? DG_LDS_AHEAD : MR;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x100, NR + D, 0);
-#pragma unroll
-                for (int f = 0; f < MR; ++f) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
-                    if (f + D < MR)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-        } else {
-            i32x8 bf[NR];
-#pragma unroll
-            for (int j = 0; j < NR; ++j)
-                bf[j] = cat(lds_b(stage, j, 0), lds_b(stage, j, 1));
-#pragma unroll
-            for (int mi = 0; mi < MR; ++mi) {
-                const i32x8 a = cat(lds_a(stage, mi, g4), lds_a(stage, mi, 4 + g4));
+            for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
-                    acc[mi][j] = mfma_fp8(a, bf[j], acc[mi][j]);
-            }
-            constexpr int D = DG_LDS_AHEAD < MR ? DG_LDS_AHEAD : MR;
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR + 2 * D, 0);
-#pragma unroll
-            for (int f = 0; f < MR; ++f) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
-                if (f + D < MR)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
+                    acc[mi][j] = AT::mma(af[s & 1][mi], bf[s & 1][j], acc[mi][j]);
         }
-    };
-    auto barrier = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
+        schedule_ktile<STEPS, MR * NR, (MR + NR) * P>();
     };
     auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
         constexpr int s = decltype(sc)::value;
@@ -572,14 +658,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         __builtin_amdgcn_sched_barrier(0);
         compute(s);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-        barrier();
+        stage_barrier();
     };
 
 #pragma unroll
     for (int t = 0; t < ST - 1; ++t)
         load(t, t);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-    barrier();
+    stage_barrier();
 
     int kt = 0;
     for (; kt + ST <= p.nkt; kt += ST) {
@@ -608,9 +694,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    store_c_tile<DT, MR, NR, S::CH, S::SROW, S::WCOLS>(p, acc, lds + wave * (S::CH * 16 * S::SROW),
-                                                      m0, rows, n0 + wn * S::WCOLS, (int)row0,
-                                                      lane, scale_a, scale_b);
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+        p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
+        scale_a, scale_b);
 }
 
 // Skinny kernel: NB 16-column blocks per workgroup, MR 16-row blocks cover M.

@@ -44,24 +44,35 @@ struct Cand {
     bool screened;  // fails the padding screen
 };
 
-void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4)
+// Sustained MFMA issue rate of an atom relative to the dense peak, measured
+// on MI355X with independent accumulators in VGPRs: the 16 x 16 x 32 bf16
+// MFMA issues at about 0.57 of the peak there, the others at about 0.98.
+double atom_rate(int dt, int atom)
+{
+    if (dt == GEMM_BF16 && atom == 16)
+        return 0.57;
+    return 0.98;
+}
+
+void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4, int atom = 16)
 {
     memset(&t, 0, sizeof t);
     t.kernel = kernel;
     t.tile_m = tm;
     t.tile_n = tn;
     t.tile_k = dt == GEMM_BF16 ? 64 : 128;
-    t.atom = 16;
+    t.atom = atom;
     t.waves = waves;
     t.k_split = kernel == GEMM_KERNEL_SKINNY ? 4 : 1;
     t.lds_stages = kernel == GEMM_KERNEL_TILED ? 2 : 0;
 }
 
-bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, int waves,
+bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, const TiledRung& r,
                  const Chip& c, Cand& out)
 {
-    const int lds = tiled_lds_bytes(tm, tn, waves);
-    const int vgpr = tiled_vgpr_estimate(tm, tn, waves);
+    const int tm = r.tm, tn = r.tn, waves = r.waves;
+    const int lds = tiled_lds_bytes(tm, tn, waves, r.atom);
+    const int vgpr = tiled_vgpr_estimate(tm, tn, waves, r.atom);
     if (lds < 0 || lds > c.lds_per_cu || vgpr > 512)
         return false;
     const int waves_per_simd = std::min(8, 512 / align8(vgpr));
@@ -72,7 +83,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int t
     const int64_t tiles_m = cdiv(M, tm), tiles_n = cdiv(N, tn);
     const int64_t tiles = tiles_m * tiles_n;
     const double flop_tile_kt = 2.0 * tm * tn * (128.0 / e);
-    const double mfma = flop_tile_kt / c.mfma_flop_per_clk_cu[dt];
+    const double mfma = flop_tile_kt / (c.mfma_flop_per_clk_cu[dt] * atom_rate(dt, r.atom));
     // every wave reads its rows of A from LDS once per k-tile (the 4 wave
     // columns share rows); B is read by every wave row
     const double ldsc = (4.0 * tm * 128) / c.lds_bytes_per_clk;
@@ -84,7 +95,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int t
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves);
+    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves, r.atom);
     const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
     const int64_t rounds = cdiv(tiles, cus);
     out.t.tile_eff = (float)te;
@@ -101,11 +112,13 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r,
               Cand& out)
 {
     const int waves = r.wm * r.wn;
-    const int lds = ab_lds_bytes(r.tm, r.tn, waves);
+    const int lds = ab_lds_bytes(r.tm, r.tn, waves, r.atom);
     if (lds < 0 || lds > c.lds_per_cu)
         return false;
-    const int mr = r.tm / r.wm / 16, nr = r.tn / r.wn / 16;
-    const int vgpr = mr * nr * 4 + nr * 8 + 16 + 40;
+    // accumulators + two sets of fragments + addresses
+    const int acc = r.tm * r.tn / (waves * 64);
+    const int frag = 2 * (r.tm / r.wm + r.tn / r.wn) / r.atom * 4 * (dt == GEMM_BF16 ? 1 : 2);
+    const int vgpr = acc + frag + 40;
     const int waves_per_simd = std::min(8, 512 / align8(vgpr));
     const int occ = std::max(1, std::min(waves_per_simd / std::max(1, waves / 4), c.lds_per_cu / lds));
     const int e = dt == GEMM_BF16 ? 2 : 1;
@@ -113,7 +126,7 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r,
     const int64_t tiles_m = cdiv(M, r.tm), tiles_n = cdiv(N, r.tn);
     const int64_t tiles = tiles_m * tiles_n;
     const double flop_tile_kt = 2.0 * r.tm * r.tn * (128.0 / e);
-    const double mfma = flop_tile_kt / c.mfma_flop_per_clk_cu[dt];
+    const double mfma = flop_tile_kt / (c.mfma_flop_per_clk_cu[dt] * atom_rate(dt, r.atom));
     const double ldsc = ((double)r.wn * r.tm * 128 + (double)r.wm * r.tn * 128) / c.lds_bytes_per_clk;
     const double vmem = (double)(r.tm + r.tn) * 128 / c.vmem_bytes_per_clk;
     const double per_kt = std::max(mfma, std::max(ldsc, vmem)) * (1.0 + 0.25 / occ);
@@ -123,7 +136,7 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r,
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves);
+    fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves, r.atom);
     const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
     const int64_t rounds = cdiv(tiles, cus);
     out.t.tile_eff = (float)te;
@@ -164,28 +177,28 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int 
 
 }  // namespace
 
-int tiled_vgpr_estimate(int tm, int tn, int waves)
+int tiled_vgpr_estimate(int tm, int tn, int waves, int atom)
 {
-    const int mr = tm / (waves / 4) / 16, nr = tn / 64;
-    const int acc = mr * nr * 4;
-    const int b = nr * 2 * 4 * tiled_stages(waves);  // B k-tiles in flight
+    (void)atom;
+    const int acc = tm * tn / (waves * 64);          // fp32 accumulators per lane
+    const int b = tn / 32 * 4 * tiled_stages(waves);  // B k-tiles in flight
     const int a_frag = 8;
     const int misc = 40;                      // addresses, offsets, loop state
     return acc + b + a_frag + misc;
 }
 
-bool tiled_supported(int tm, int tn, int waves)
+bool tiled_supported(int tm, int tn, int waves, int atom)
 {
     for (const TiledRung& r : kTiledLadder)
-        if (r.tm == tm && r.tn == tn && r.waves == waves)
+        if (r.tm == tm && r.tn == tn && r.waves == waves && r.atom == atom)
             return true;
     return false;
 }
 
-bool ab_supported(int tm, int tn, int waves)
+bool ab_supported(int tm, int tn, int waves, int atom)
 {
     for (const ABRung& r : kABLadder)
-        if (r.tm == tm && r.tn == tn && r.wm * r.wn == waves)
+        if (r.tm == tm && r.tn == tn && r.wm * r.wn == waves && r.atom == atom)
             return true;
     return false;
 }
@@ -223,7 +236,7 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
     }
     for (const TiledRung& r : kTiledLadder) {
         Cand cd;
-        if (price_tiled(M, N, K, dt, cus, r.tm, r.tn, r.waves, chip, cd))
+        if (price_tiled(M, N, K, dt, cus, r, chip, cd))
             consider(cd);
     }
     for (const ABRung& r : kABLadder) {

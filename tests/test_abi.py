@@ -59,10 +59,10 @@ def test_shuffle_b_bytes_fp8_layout_size():
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 def test_select_tile_metrics_match_oracle(M, N, K, dt):
     t = dg.select_tile(M, N, K, dt, num_cus=256)
-    assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY)
+    assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY, dg.GEMM_KERNEL_TILED_AB)
     if t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB):
         ladder = dg.TILED_LADDER if t.kernel == dg.GEMM_KERNEL_TILED else dg.AB_LADDER
-        assert (t.tile_m, t.tile_n, t.waves) in ladder
+        assert (t.tile_m, t.tile_n, t.waves, t.atom) in ladder
         tiles, te, we, de = oracle.dim_eff(M, N, t.tile_m, t.tile_n, 256)
         assert abs(t.tile_eff - te) < 1e-6 and abs(t.wq_eff - we) < 1e-6
         # padding screen: padded output at most 1.25x the real one when any tile passes
@@ -77,7 +77,8 @@ def test_select_tile_metrics_match_oracle(M, N, K, dt):
 def test_select_tile_routes_small_m_to_skinny():
     for M in (1, 8, 16):
         assert dg.select_tile(M, 11008, 4096, "bf16", 256).kernel == dg.GEMM_KERNEL_SKINNY
-    assert dg.select_tile(4096, 4096, 4096, "bf16", 256).kernel == dg.GEMM_KERNEL_TILED
+    assert dg.select_tile(4096, 4096, 4096, "bf16", 256).kernel in (dg.GEMM_KERNEL_TILED,
+                                                                    dg.GEMM_KERNEL_TILED_AB)
 
 
 def test_select_tile_errors():

@@ -92,10 +92,10 @@ def test_workload_shapes_sampled(name, smallint):
 EVERY_SHAPE = (263, 270, 176)   # divides no tile in M, N or the 64-element k-tile
 
 
-@pytest.mark.parametrize("tm,tn,waves", dg.TILED_LADDER)
-def test_every_tiled_tile(tm, tn, waves):
+@pytest.mark.parametrize("tm,tn,waves,atom", dg.TILED_LADDER)
+def test_every_tiled_tile(tm, tn, waves, atom):
     M, N, K = EVERY_SHAPE
-    tile = dg.tiled(tm, tn, waves)
+    tile = dg.tiled(tm, tn, waves, atom)
     for smallint in (False, True):
         A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
                                       "smallint" if smallint else "normal", config=9)
@@ -109,10 +109,10 @@ def test_every_tiled_tile(tm, tn, waves):
                         K, what=tile.name)
 
 
-@pytest.mark.parametrize("tm,tn,waves", dg.AB_LADDER)
-def test_every_ab_tile(tm, tn, waves):
+@pytest.mark.parametrize("tm,tn,waves,atom", dg.AB_LADDER)
+def test_every_ab_tile(tm, tn, waves, atom):
     M, N, K = EVERY_SHAPE
-    tile = dg.tiled_ab(tm, tn, waves)
+    tile = dg.tiled_ab(tm, tn, waves, atom)
     for smallint in (False, True):
         A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
                                       "smallint" if smallint else "normal", config=9)
@@ -139,10 +139,13 @@ def test_every_skinny_tile(tm, tn, M):
 
 
 @pytest.mark.parametrize("K", [16, 48, 80, 144, 64, 128])
-@pytest.mark.parametrize("tile", [None, dg.tiled(64, 64), dg.tiled(256, 128), dg.tiled(256, 256, 8),
-                                  dg.tiled_ab(256, 256, 8), dg.tiled_ab(128, 128, 4), dg.skinny(32, 16)],
-                         ids=["auto", "t64x64", "t256x128", "t256x256w8", "ab256x256w8", "ab128x128",
-                              "s32x16"])
+@pytest.mark.parametrize("tile", [None, dg.tiled(64, 64), dg.tiled(256, 128), dg.tiled(256, 128, 8),
+                                  dg.tiled_ab(256, 128, 4), dg.tiled_ab(128, 128, 4), dg.skinny(32, 16),
+                                  dg.tiled(128, 128, 4, 32), dg.tiled(256, 256, 8, 32),
+                                  dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 128, 4, 32)],
+                         ids=["auto", "t64x64", "t256x128", "t256x128w8", "ab256x128", "ab128x128",
+                              "s32x16", "t128x128a32", "t256x256w8a32", "ab256x256w8a32",
+                              "ab128x128a32"])
 def test_k_tails(K, tile):
     M, N = 30, 100
     A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=K)

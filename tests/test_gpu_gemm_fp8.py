@@ -56,22 +56,22 @@ def test_workload_shapes_sampled(name, smallint):
         check_close("fp8", got[None, :], vals[None, :], absv[None, :], K, scale=sa * sb, what=name)
 
 
-@pytest.mark.parametrize("tm,tn,waves", dg.TILED_LADDER)
-def test_every_tiled_tile(tm, tn, waves):
+@pytest.mark.parametrize("tm,tn,waves,atom", dg.TILED_LADDER)
+def test_every_tiled_tile(tm, tn, waves, atom):
     M, N, K = 263, 270, 192
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=19, smallint=True)
-    C, ok = run("fp8", A, B, tile=dg.tiled(tm, tn, waves), sa=0.5, sb=4.0)
+    C, ok = run("fp8", A, B, tile=dg.tiled(tm, tn, waves, atom), sa=0.5, sb=4.0)
     assert ok
-    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"tiled{tm}x{tn}w{waves}")
+    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"tiled{tm}x{tn}w{waves}a{atom}")
 
 
-@pytest.mark.parametrize("tm,tn,waves", dg.AB_LADDER)
-def test_every_ab_tile(tm, tn, waves):
+@pytest.mark.parametrize("tm,tn,waves,atom", dg.AB_LADDER)
+def test_every_ab_tile(tm, tn, waves, atom):
     M, N, K = 263, 270, 192
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=19, smallint=True)
-    C, ok = run("fp8", A, B, tile=dg.tiled_ab(tm, tn, waves), sa=0.5, sb=4.0)
+    C, ok = run("fp8", A, B, tile=dg.tiled_ab(tm, tn, waves, atom), sa=0.5, sb=4.0)
     assert ok
-    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"ab{tm}x{tn}w{waves}")
+    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"ab{tm}x{tn}w{waves}a{atom}")
 
 
 @pytest.mark.parametrize("tm,tn", dg.SKINNY_LADDER)
@@ -87,8 +87,9 @@ def test_every_skinny_tile(tm, tn):
 def test_k_tails(K):
     M, N = 40, 90
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=K, smallint=True)
-    for tile in (None, dg.tiled(64, 64), dg.tiled(128, 256), dg.tiled(256, 256, 8),
-                 dg.tiled_ab(256, 256, 8), dg.tiled_ab(256, 128, 4), dg.skinny(48, 32)):
+    for tile in (None, dg.tiled(64, 64), dg.tiled(128, 256), dg.tiled(256, 128, 8),
+                 dg.tiled_ab(256, 128, 4), dg.tiled_ab(256, 128, 4), dg.skinny(48, 32),
+                 dg.tiled(128, 128, 4, 32), dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 256, 4, 32)):
         C, ok = run("fp8", A, B, tile=tile)
         assert ok
         check_exact(C, oracle_full("fp8", A, B), f"K={K} {tile}")
