@@ -143,30 +143,36 @@ def gpu_setup(name: str, copies: int):
 
 
 def parse_tile(spec: str | None):
-    """'tiled:256x128', 'tiled:256x256w8', 'ab:256x256w8a32' or 'skinny:16x32' -> Tile
-    (an 'a32' suffix selects the 32 x 32 MFMA atom); None -> select_tile."""
+    """'tiled:256x128', 'tiled:256x256w8', 'ab:256x256w8a32s4k32' or 'skinny:16x32'
+    -> Tile (suffixes: aR = R x R MFMA atom, sN = N stages, kE = E K elements per
+    stage); None -> select_tile."""
     if spec is None:
         return None
+    import re
     import dense_gemm_linear_amd as dg
     kind, dims = spec.split(":")
-    atom = 16
-    if "a" in dims:
-        dims, a = dims.split("a")
-        atom = int(a)
+    atom, stages, tile_k = 16, 0, 0
+    m = re.fullmatch(r"(\d+x\d+(?:w\d+)?)(?:a(\d+))?(?:s(\d+))?(?:k(\d+))?", dims)
+    if not m:
+        raise ValueError(f"bad tile spec {spec!r}")
+    dims = m.group(1)
+    atom = int(m.group(2) or 16)
+    stages = int(m.group(3) or 0)
+    tile_k = int(m.group(4) or 0)
     waves = 4
     if "w" in dims:
         dims, w = dims.split("w")
         waves = int(w)
     tm, tn = (int(x) for x in dims.split("x"))
     if kind == "tiled":
-        return dg.tiled(tm, tn, waves, atom)
+        return dg.tiled(tm, tn, waves, atom, stages, tile_k)
     if kind == "ab":
-        return dg.tiled_ab(tm, tn, waves, atom)
+        return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k)
     return dg.skinny(tm, tn)
 
 
 def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True,
-              tile=None, setup=None):
+              tile=None, setup=None, soak: float = 0.0):
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
@@ -209,9 +215,10 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
     kern_us = [s.elapsed_time(e) * 1e3 for s, e in ev] if per_launch else []
+    clock = clock_under_load(call, soak) if soak > 0 else None
     return {
         "total_ms": total_ms, "wall_s": wall, "kernel_us": kern_us, "tile": tile,
-        "shuffle_us": shuffle_us, "copies": copies,
+        "shuffle_us": shuffle_us, "copies": copies, "clock": clock,
     }
 
 
@@ -252,6 +259,41 @@ def run_graph(name: str, reps: int, copies: int):
     return t0.elapsed_time(t1) * 1e3 / reps, shuffle_us
 
 
+def clock_under_load(call, seconds: float = 1.5):
+    """Shader clock and board power while `call` runs back to back for about
+    `seconds`, read in-process (torch.cuda.clock_rate / power_draw, which
+    query amdsmi) at 2/3 and at the end of the soak, while kernels are still
+    queued.  The timed steps are too short for the board to reach its
+    power-limited steady state, so this is reported beside them, not used in
+    `value`.  Returns None when the queries are unavailable."""
+    import torch
+    t0 = time.perf_counter()
+    marks = (t0 + seconds * 2 / 3, t0 + seconds)
+    samples = []
+    i = 0
+    while len(samples) < len(marks):
+        call(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+            call(i)          # keep the device busy while sampling
+            i += 1
+            if time.perf_counter() >= marks[len(samples)]:
+                try:
+                    samples.append((torch.cuda.clock_rate(), torch.cuda.power_draw()))
+                except Exception as e:  # noqa: BLE001 - any query failure means "unavailable"
+                    torch.cuda.synchronize()
+                    return {"error": f"{type(e).__name__}: {e}"}
+    torch.cuda.synchronize()
+    mhz = [c for c, _ in samples]
+    pw = [p for _, p in samples]
+    # power_draw reports milliwatts on some stacks and watts on others
+    watts = [p / 1000.0 if p > 20000 else float(p) for p in pw]
+    return {"gfx_mhz": mhz, "power_w": [round(w, 1) for w in watts], "calls": i,
+            "source": f"torch.cuda.clock_rate/power_draw at 2/3 and end of a {seconds:.1f} s "
+                      f"soak of the timed call"}
+
+
 # ------------------------------------------------------------ CPU oracle
 def cpu_baseline(name: str, budget_s: float = 20.0):
     """The oracle on whole rows of C of the same workload, scaled to TFLOP/s."""
@@ -285,6 +327,12 @@ def main(argv=None):
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="operand sets rotated through the timed calls (0 = enough to exceed twice "
+                         "the Infinity Cache, so operands come from HBM; 1 = hot cache)")
+    ap.add_argument("--soak", type=float, default=1.5,
+                    help="seconds of back-to-back calls after the timed steps, sampling the shader "
+                         "clock and board power (0 = skip)")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. tiled:256x256 or skinny:16x32")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
@@ -307,7 +355,8 @@ def main(argv=None):
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
         return sweep(name, args.steps, args.warmup)
-    r = run_timed(name, args.steps, args.warmup, tile=parse_tile(args.tile))
+    r = run_timed(name, args.steps, args.warmup, tile=parse_tile(args.tile), soak=args.soak,
+                  copies=args.copies or None)
     ms_per_step = r["total_ms"] / args.steps
     kern = sorted(r["kernel_us"])
     kern_avg = sum(kern) / len(kern)
@@ -343,6 +392,12 @@ def main(argv=None):
     }
     if bound == "mfma":
         out["config"]["pct_of_mfma_peak"] = round(100 * value / PEAK_TFLOPS[dt], 2)
+    clk = r["clock"]
+    out["clock_under_load"] = clk
+    if clk and clk.get("gfx_mhz") and bound == "mfma" and min(clk["gfx_mhz"]) > 0:
+        # the same kernel against the MFMA peak at the clock the chip sustains
+        mhz = sum(clk["gfx_mhz"]) / len(clk["gfx_mhz"])
+        out["roofline"]["frac_at_sustained_clock"] = round(achieved / (peak * mhz / 2400.0), 4)
     if not args.no_secondary and name != DECODE:
         dM, dN, dK, ddt = WORKLOADS[DECODE][:4]
         us_cold, _ = run_graph(DECODE, reps=60, copies=6)
@@ -371,7 +426,7 @@ def sweep(name: str, steps: int, warmup: int) -> int:
     per_set = alg_bytes(M, N, K, dt)
     copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
     setup = gpu_setup(name, copies)
-    tiles = dg.all_tiles(M)
+    tiles = dg.all_tiles(M, dt)
     res = {}
     for t in tiles:
         r = run_timed(name, steps, warmup, tile=t, setup=setup)

@@ -36,7 +36,7 @@ GEMM_KERNEL_SKINNY = 1
 GEMM_KERNEL_TILED_AB = 2
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
-           "gemm_status_string")
+           "gemm_tile_check", "gemm_status_string")
 
 
 class GemmTile(ctypes.Structure):
@@ -56,18 +56,22 @@ class Tile:
     atom: int = 16
     waves: int = 4
     k_split: int = 1
-    lds_stages: int = 2
+    lds_stages: int = 0
     tile_eff: float = 0.0
     wq_eff: float = 0.0
     predicted_us: float = 0.0
 
     @property
     def name(self) -> str:
+        """e.g. tiled128x128 (4 waves, 16x16 atom), ab256x256w8a32s4k32 (8 waves,
+        32x32 atom, 4 stages, 32-element k-tile); unset fields are omitted."""
         atom = "" if self.atom in (0, 16) else f"a{self.atom}"
+        pipe = (f"s{self.lds_stages}" if self.lds_stages else "") + (f"k{self.tile_k}" if self.tile_k else "")
         if self.kernel == GEMM_KERNEL_TILED:
-            return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}") + atom
+            return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}") + \
+                atom + pipe
         if self.kernel == GEMM_KERNEL_TILED_AB:
-            return f"ab{self.tile_m}x{self.tile_n}w{self.waves}" + atom
+            return f"ab{self.tile_m}x{self.tile_n}w{self.waves}" + atom + pipe
         return f"skinny{self.tile_m}x{self.tile_n}"
 
     def to_c(self) -> GemmTile:
@@ -80,34 +84,48 @@ class Tile:
                     t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
 
 
-def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16) -> Tile:
-    return Tile(GEMM_KERNEL_TILED, tm, tn, atom=atom, waves=waves)
+def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0) -> Tile:
+    """A rung of the tiled ladder; stages / tile_k (K elements per stage) 0 = any."""
+    return Tile(GEMM_KERNEL_TILED, tm, tn, tile_k=tile_k, atom=atom, waves=waves, lds_stages=stages)
 
 
-def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16) -> Tile:
-    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, atom=atom, waves=waves)
+def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0) -> Tile:
+    """A rung of the A+B-in-LDS ladder; stages / tile_k 0 = any."""
+    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, tile_k=tile_k, atom=atom, waves=waves,
+                lds_stages=stages)
 
 
 def skinny(tm: int, tn: int) -> Tile:
     return Tile(GEMM_KERNEL_SKINNY, tm, tn, k_split=4, lds_stages=0)
 
 
-# (tile_m, tile_n, waves, atom): 8-wave tiled rungs arrange the waves 2 (M) x 4 (N)
-TILED_LADDER = [(256, 128, 8, 16), (128, 256, 8, 16), (128, 128, 8, 16)] + \
-    [(m, n, 4, 16) for m in (256, 128, 64, 32) for n in (256, 128, 64) if (m, n) != (256, 256)] + \
-    [(256, 256, 8, 32), (256, 128, 8, 32), (128, 256, 8, 32), (128, 128, 8, 32),
-     (256, 128, 4, 32), (128, 256, 4, 32), (128, 128, 4, 32), (64, 256, 4, 32), (64, 128, 4, 32)]
-# (tile_m, tile_n, waves, atom): 8 waves form 2 x 4, 4 waves 2 x 2
-AB_LADDER = [(256, 128, 4, 16), (128, 256, 4, 16), (128, 128, 4, 16),
-             (256, 256, 8, 32), (256, 256, 4, 32), (256, 128, 8, 32), (256, 128, 4, 32),
-             (128, 256, 4, 32), (128, 128, 4, 32)]
+# The ladders of include/densegemm.h, as (tile_m, tile_n, waves, stages, atom,
+# k-tile bytes).  8-wave tiled rungs arrange the waves 2 (M) x 4 (N); A+B
+# rungs form 2 x (waves / 2).
+TILED_LADDER = [(256, 128, 8, 2, 16, 128), (128, 256, 8, 2, 16, 128), (128, 128, 8, 2, 16, 128)] + \
+    [(m, n, 4, 3, 16, 128) for m in (256, 128, 64, 32) for n in (256, 128, 64) if (m, n) != (256, 256)] + \
+    [(256, 256, 8, 2, 32, 128), (256, 128, 8, 2, 32, 128), (128, 256, 8, 2, 32, 128),
+     (128, 128, 8, 2, 32, 128), (256, 128, 4, 3, 32, 128), (128, 256, 4, 3, 32, 128),
+     (128, 128, 4, 3, 32, 128), (64, 256, 4, 3, 32, 128), (64, 128, 4, 3, 32, 128),
+     (128, 256, 4, 4, 32, 64), (128, 128, 4, 4, 32, 64), (256, 128, 4, 4, 32, 64)]
+AB_LADDER = [(256, 128, 4, 3, 16, 128), (128, 256, 4, 3, 16, 128), (128, 128, 4, 3, 16, 128),
+             (256, 256, 8, 2, 32, 128), (256, 256, 4, 2, 32, 128), (256, 128, 8, 3, 32, 128),
+             (256, 128, 4, 3, 32, 128), (128, 256, 4, 3, 32, 128), (128, 128, 4, 3, 32, 128),
+             (256, 256, 8, 4, 32, 64), (256, 256, 8, 5, 32, 64), (256, 256, 4, 4, 32, 64),
+             (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64)]
 SKINNY_LADDER = [(m, n) for m in (16, 32, 48, 64) for n in (16, 32, 64)]
 
 
-def all_tiles(M: int):
+def ladder_tiles(dtype="bf16"):
+    """Every tiled and A+B rung, fully specified for an element type."""
+    e = 2 if _dtype_code(dtype) == GEMM_BF16 else 1
+    return [tiled(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in TILED_LADDER] + \
+        [tiled_ab(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in AB_LADDER]
+
+
+def all_tiles(M: int, dtype="bf16"):
     """Every rung usable for a GEMM with M rows."""
-    t = [tiled(m, n, w, a) for m, n, w, a in TILED_LADDER] + \
-        [tiled_ab(m, n, w, a) for m, n, w, a in AB_LADDER]
+    t = ladder_tiles(dtype)
     if M <= 64:
         t += [skinny(m, n) for m, n in SKINNY_LADDER if M <= m < M + 16]
     return t
@@ -145,6 +163,8 @@ def _load_lib():
     lib.gemm_fp8_scaled.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
                                     ctypes.POINTER(GemmTile), P]
     lib.gemm_fp8_scaled.restype = ctypes.c_int
+    lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
+    lib.gemm_tile_check.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
     return lib
@@ -171,6 +191,11 @@ def select_tile(M: int, N: int, K: int, dtype="bf16", num_cus: int = 0) -> Tile:
     if st != GEMM_OK:
         raise GemmError("select_tile", st)
     return Tile.from_c(t)
+
+
+def tile_check(tile: Tile, M: int, dtype="bf16") -> int:
+    """Status of forcing `tile` on an M-row GEMM of this dtype (GEMM_OK if a rung)."""
+    return int(lib.gemm_tile_check(ctypes.byref(tile.to_c()), M, _dtype_code(dtype)))
 
 
 def shuffle_b_bytes(N: int, K: int, dtype="bf16") -> int:

@@ -9,16 +9,14 @@ namespace dg {
 
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out);
 
-hipError_t launch_ab(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s)
+hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
-    return dt == DT_BF16 ? launch_ab_bf16(tm, tn, waves, atom, a, s)
-                         : launch_ab_fp8(tm, tn, waves, atom, a, s);
+    return dt == DT_BF16 ? launch_ab_bf16(idx, a, s) : launch_ab_fp8(idx, a, s);
 }
 
-hipError_t launch_tiled(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s)
+hipError_t launch_tiled(int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
-    return dt == DT_BF16 ? launch_tiled_bf16(tm, tn, waves, atom, a, s)
-                         : launch_tiled_fp8(tm, tn, waves, atom, a, s);
+    return dt == DT_BF16 ? launch_tiled_bf16(idx, a, s) : launch_tiled_fp8(idx, a, s);
 }
 
 namespace {
@@ -58,18 +56,23 @@ gemm_status device_info(int* cus)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Is a forced tile usable for this shape?  (atom 0 means 16.)
-bool tile_feasible(gemm_tile& t, int64_t M)
+// The ladder rung a tile names, if it is usable for this shape: atom 0 means
+// 16; tile_k (elements) and lds_stages 0 mean the first rung that matches
+// the other fields.
+bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
 {
-    if (t.atom == 0)
-        t.atom = 16;
+    if (t.tile_k < 0 || t.tile_k > 4096 || t.lds_stages < 0)
+        return false;
+    const int atom = t.atom == 0 ? 16 : t.atom;
+    const int ktb = t.tile_k * e;
+    *idx = -1;
     if (t.kernel == GEMM_KERNEL_TILED)
-        return tiled_supported(t.tile_m, t.tile_n, t.waves, t.atom);
-    if (t.kernel == GEMM_KERNEL_SKINNY)
-        return skinny_supported(t.tile_m, t.tile_n) && M <= t.tile_m;
-    if (t.kernel == GEMM_KERNEL_TILED_AB)
-        return ab_supported(t.tile_m, t.tile_n, t.waves, t.atom);
-    return false;
+        *idx = tiled_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
+    else if (t.kernel == GEMM_KERNEL_TILED_AB)
+        *idx = ab_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
+    else if (t.kernel == GEMM_KERNEL_SKINNY)
+        *idx = skinny_supported(t.tile_m, t.tile_n) && M <= t.tile_m ? 0 : -1;
+    return *idx >= 0;
 }
 
 gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const float* sa,
@@ -98,9 +101,10 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         ldc * 2 > (INT64_C(1) << 22) || K * e > (INT64_C(1) << 20))
         return GEMM_ERR_UNSUPPORTED;
     gemm_tile t;
+    int idx = -1;
     if (tile) {
         t = *tile;
-        if (!tile_feasible(t, M))
+        if (!resolve_tile(t, M, e, &idx))
             return GEMM_ERR_UNSUPPORTED;
     }
     // ---- device
@@ -111,8 +115,11 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (K == 0)
         return launch_zero_c(C, ldc, M, N, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
-    if (!tile)
+    if (!tile) {
         choose_tile(M, N, K, dt, cus, &t);
+        if (!resolve_tile(t, M, e, &idx))
+            return GEMM_ERR_UNSUPPORTED;   // the selector names only rungs that exist
+    }
     GemmArgs a;
     memset(&a, 0, sizeof a);
     a.A = static_cast<const uint8_t*>(A);
@@ -136,9 +143,8 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     } else {
         a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
         a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
-        err = t.kernel == GEMM_KERNEL_TILED_AB
-                  ? launch_ab(dt, t.tile_m, t.tile_n, t.waves, t.atom, a, s)
-                  : launch_tiled(dt, t.tile_m, t.tile_n, t.waves, t.atom, a, s);
+        err = t.kernel == GEMM_KERNEL_TILED_AB ? launch_ab(dt, idx, a, s)
+                                               : launch_tiled(dt, idx, a, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -191,6 +197,15 @@ gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K
                                           static_cast<uint8_t*>(Bs), N, K * e, (K * e + 63) / 64,
                                           aligned, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status gemm_tile_check(const gemm_tile* tile, int64_t M, gemm_dtype dtype)
+{
+    if (!tile || M < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return GEMM_ERR_INVALID_VALUE;
+    int idx = -1;
+    return dg::resolve_tile(*tile, M, dtype == GEMM_BF16 ? 2 : 1, &idx) ? GEMM_OK
+                                                                        : GEMM_ERR_UNSUPPORTED;
 }
 
 const char* gemm_status_string(gemm_status status)

@@ -11,56 +11,69 @@
 
 namespace dg {
 
-// Tiled ladder: (tile_m, tile_n, waves, atom).  X(M, N, W, R) is applied to
-// every rung.  8-wave rungs arrange the waves 2 (M) x 4 (N).
-#define DG_TILED_LADDER(X)                                                              \
-    X(256, 128, 8, 16) X(128, 256, 8, 16) X(128, 128, 8, 16)                           \
-    X(256, 128, 4, 16) X(256, 64, 4, 16)                                               \
-    X(128, 256, 4, 16) X(128, 128, 4, 16) X(128, 64, 4, 16)                            \
-    X(64, 256, 4, 16) X(64, 128, 4, 16) X(64, 64, 4, 16)                               \
-    X(32, 256, 4, 16) X(32, 128, 4, 16) X(32, 64, 4, 16)                               \
-    X(256, 256, 8, 32) X(256, 128, 8, 32) X(128, 256, 8, 32) X(128, 128, 8, 32)        \
-    X(256, 128, 4, 32) X(128, 256, 4, 32) X(128, 128, 4, 32)                           \
-    X(64, 256, 4, 32) X(64, 128, 4, 32)
+// Tiled ladder: (tile_m, tile_n, waves, stages, atom, k-tile bytes).
+// X(M, N, W, ST, R, KTB) is applied to every rung.  8-wave rungs arrange the
+// waves 2 (M) x 4 (N).
+#define DG_TILED_LADDER(X)                                                                  \
+    X(256, 128, 8, 2, 16, 128) X(128, 256, 8, 2, 16, 128) X(128, 128, 8, 2, 16, 128)       \
+    X(256, 128, 4, 3, 16, 128) X(256, 64, 4, 3, 16, 128)                                   \
+    X(128, 256, 4, 3, 16, 128) X(128, 128, 4, 3, 16, 128) X(128, 64, 4, 3, 16, 128)        \
+    X(64, 256, 4, 3, 16, 128) X(64, 128, 4, 3, 16, 128) X(64, 64, 4, 3, 16, 128)           \
+    X(32, 256, 4, 3, 16, 128) X(32, 128, 4, 3, 16, 128) X(32, 64, 4, 3, 16, 128)           \
+    X(256, 256, 8, 2, 32, 128) X(256, 128, 8, 2, 32, 128) X(128, 256, 8, 2, 32, 128)       \
+    X(128, 128, 8, 2, 32, 128) X(256, 128, 4, 3, 32, 128) X(128, 256, 4, 3, 32, 128)       \
+    X(128, 128, 4, 3, 32, 128) X(64, 256, 4, 3, 32, 128) X(64, 128, 4, 3, 32, 128)         \
+    X(128, 256, 4, 4, 32, 64) X(128, 128, 4, 4, 32, 64) X(256, 128, 4, 4, 32, 64)
 
-// A+B-in-LDS ladder: (tile_m, tile_n, wave rows, wave columns, stages, atom).
-#define DG_AB_LADDER(X)                                                                 \
-    X(256, 128, 2, 2, 3, 16) X(128, 256, 2, 2, 3, 16) X(128, 128, 2, 2, 3, 16)          \
-    X(256, 256, 2, 4, 2, 32) X(256, 256, 2, 2, 2, 32) X(256, 128, 2, 4, 3, 32)          \
-    X(256, 128, 2, 2, 3, 32) X(128, 256, 2, 2, 3, 32) X(128, 128, 2, 2, 3, 32)
+// A+B-in-LDS ladder: (tile_m, tile_n, wave rows, wave columns, stages, atom,
+// k-tile bytes).
+#define DG_AB_LADDER(X)                                                                     \
+    X(256, 128, 2, 2, 3, 16, 128) X(128, 256, 2, 2, 3, 16, 128)                            \
+    X(128, 128, 2, 2, 3, 16, 128)                                                          \
+    X(256, 256, 2, 4, 2, 32, 128) X(256, 256, 2, 2, 2, 32, 128)                            \
+    X(256, 128, 2, 4, 3, 32, 128) X(256, 128, 2, 2, 3, 32, 128)                            \
+    X(128, 256, 2, 2, 3, 32, 128) X(128, 128, 2, 2, 3, 32, 128)                            \
+    X(256, 256, 2, 4, 4, 32, 64) X(256, 256, 2, 4, 5, 32, 64) X(256, 256, 2, 2, 4, 32, 64)  \
+    X(256, 128, 2, 4, 6, 32, 64) X(128, 256, 2, 2, 6, 32, 64)
 
 struct ABRung {
-    int tm, tn, wm, wn, st, atom;
+    int tm, tn, wm, wn, st, atom, ktb;
 };
 constexpr ABRung kABLadder[] = {
-#define DG_ABR(M_, N_, WM_, WN_, ST_, R_) {M_, N_, WM_, WN_, ST_, R_},
+#define DG_ABR(M_, N_, WM_, WN_, ST_, R_, KTB_) {M_, N_, WM_, WN_, ST_, R_, KTB_},
     DG_AB_LADDER(DG_ABR)
 #undef DG_ABR
 };
 
 struct TiledRung {
-    int tm, tn, waves, atom;
+    int tm, tn, waves, st, atom, ktb;
 };
 constexpr TiledRung kTiledLadder[] = {
-#define DG_RUNG(M_, N_, W_, R_) {M_, N_, W_, R_},
+#define DG_RUNG(M_, N_, W_, ST_, R_, KTB_) {M_, N_, W_, ST_, R_, KTB_},
     DG_TILED_LADDER(DG_RUNG)
 #undef DG_RUNG
 };
+
+// A rung matches a request when every field agrees; a requested stage count
+// or k-tile size of 0 matches any (the first such rung in ladder order).
+#define DG_MATCH(ST_, KTB_) ((st == 0 || st == (ST_)) && (ktb == 0 || ktb == (KTB_)))
 constexpr int kSkinnyTM[] = {16, 32, 48, 64};
 constexpr int kSkinnyTN[] = {16, 32, 64};
 
-bool tiled_supported(int tm, int tn, int waves, int atom);
-bool ab_supported(int tm, int tn, int waves, int atom);
+// Index of the ladder rung a request names, or -1 (st, ktb: 0 = any).
+int tiled_rung(int tm, int tn, int waves, int atom, int st, int ktb);
+int ab_rung(int tm, int tn, int waves, int atom, int st, int ktb);
 bool skinny_supported(int tm, int tn);
 
 // Launchers: return hipSuccess or the launch error.  Grids are computed from
 // the arguments; shapes are validated by the caller.
-hipError_t launch_tiled(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_bf16(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_fp8(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab(int dt, int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_bf16(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_fp8(int tm, int tn, int waves, int atom, const GemmArgs& a, hipStream_t s);
+// Launch rung `idx` of the tiled / AB ladder.
+hipError_t launch_tiled(int dt, int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled_bf16(int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled_fp8(int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab_bf16(int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_ab_fp8(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int dt, int tm, int tn, const GemmArgs& a, hipStream_t s);
 hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
@@ -77,8 +90,9 @@ inline hipError_t launch_args(F* kernel, dim3 grid, dim3 block, const GemmArgs& 
 }
 
 // Resource model of the tiled kernel (used by select_tile's feasibility check).
-int tiled_lds_bytes(int tm, int tn, int waves, int atom);
-int ab_lds_bytes(int tm, int tn, int waves, int atom);
-int tiled_vgpr_estimate(int tm, int tn, int waves, int atom);
+// Resource model of rung `idx` (used by select_tile's feasibility check).
+int tiled_lds_bytes(int idx);
+int ab_lds_bytes(int idx);
+int tiled_vgpr_estimate(const TiledRung& r);
 
 }  // namespace dg

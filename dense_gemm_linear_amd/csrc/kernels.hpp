@@ -35,15 +35,6 @@ namespace dg {
 
 enum { DT_BF16 = 0, DT_FP8 = 1 };
 
-// Depth of the tiled kernel's load pipeline (k-tiles in LDS / registers):
-// 3 for 4-wave tiles (one wave per SIMD hides its own latency), 2 for 8-wave
-// tiles (two waves per SIMD share 512 registers and hide each other's).
-#ifndef DG_STAGES_4WAVE
-#define DG_STAGES_4WAVE 3
-#endif
-#ifndef DG_STAGES_8WAVE
-#define DG_STAGES_8WAVE 2
-#endif
 // Tile rows per raster group, and whether workgroups are renumbered per XCD.
 #ifndef DG_GROUP_M
 #define DG_GROUP_M 4
@@ -55,7 +46,6 @@ enum { DT_BF16 = 0, DT_FP8 = 1 };
 #ifndef DG_XCD_REMAP
 #define DG_XCD_REMAP 1
 #endif
-constexpr int tiled_stages(int waves) { return waves == 8 ? DG_STAGES_8WAVE : DG_STAGES_4WAVE; }
 
 struct GemmArgs {
     const uint8_t* A;     // [M, lda] elements, row-major
@@ -99,9 +89,6 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
     tn = in / gm;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // ---------------------------------------------------------------------------
 // MFMA atoms.  An atom is one R x R block of C computed by one MFMA per K
@@ -190,22 +177,41 @@ __device__ __forceinline__ typename AT::acc_t zero_acc()
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The A tile of one k-tile in LDS: TM rows of 128 bytes, the 16-byte chunk c
-// of row r stored at slot c ^ ((r >> 1) & 7) ("GEMM Optimization Guide"
-// page, section 3: an XOR swizzle at 16-byte granularity, applied on both
-// the write and the read side).  The global -> LDS copy is a 16-byte LDS DMA
-// per lane (page section 11: 16 bytes per op on gfx950): one wave load fills
-// one 1 KiB chunk = 8 rows, lane l landing at row l / 8, slot l % 8, so the
-// swizzle is applied to the global address instead.
+// ---------------------------------------------------------------------------
+// The k-tile: KTB bytes of K (64 or 128) per pipeline stage.  A stage of the
+// A tile holds TM rows of KTB bytes; 16-byte chunk c of row r is stored at
+// slot c ^ key(r), key(r) = (r / (256 / KTB)) % (KTB / 16): an XOR swizzle at
+// 16-byte granularity ("GEMM Optimization Guide" page, section 3) chosen so
+// that 16 lanes reading the same chunk of 16 consecutive rows touch all 64
+// LDS banks once.  The global -> LDS copy is a 16-byte LDS DMA per lane (page
+// section 11: 16 bytes per op on gfx950): one wave load fills 1 KiB = 1024 /
+// KTB rows, lane l landing in row l / (KTB / 16), slot l % (KTB / 16), so the
+// swizzle is applied to the global address.  B arrives as whole 1 KiB blocks
+// of the preshuffled layout (16 columns x 64 K bytes), KTB / 64 per 16-column
+// block per k-tile.
+template <int KTB>
+struct KTile {
+    static_assert(KTB == 64 || KTB == 128, "k-tile of 64 or 128 bytes");
+    static constexpr int CHUNKS = KTB / 16;        // 16-byte chunks per A row
+    static constexpr int ROWS_PER_LOAD = 1024 / KTB;
+    static constexpr int KPK = KTB / 64;           // Bs blocks per 16 columns per k-tile
+    static __host__ __device__ constexpr uint32_t key(uint32_t row)
+    {
+        return (row / (256 / KTB)) % CHUNKS;
+    }
+};
+
 struct ADma {
     uint32_t goff;   // byte offset of this lane's 16 bytes in the A slab (k-tile 0)
     uint32_t col;    // its K byte within the k-tile (for the K-tail mask)
 };
 
+template <int KTB>
 __device__ __forceinline__ ADma a_dma_lane(int chunk, int lane, int64_t lda_b)
 {
-    const uint32_t row = 8 * (uint32_t)chunk + (uint32_t)(lane >> 3);
-    const uint32_t col = (uint32_t)(lane & 7) ^ ((row >> 1) & 7);
+    using KT = KTile<KTB>;
+    const uint32_t row = KT::ROWS_PER_LOAD * (uint32_t)chunk + (uint32_t)(lane / KT::CHUNKS);
+    const uint32_t col = (uint32_t)(lane % KT::CHUNKS) ^ KT::key(row);
     return {row * (uint32_t)lda_b + col * 16, col * 16};
 }
 
@@ -213,8 +219,13 @@ __device__ __forceinline__ ADma a_dma_lane(int chunk, int lane, int64_t lda_b)
 // wave's (MR*R) x (NR*R) accumulator block through its private LDS region
 // CH atom rows at a time, and store 16-byte row pieces ("GEMM Optimization
 // Guide" page, section 7.2).  Rows past M fall outside the C descriptor; the
-// column predicate keeps a row's padding and the next row intact, and odd
-// leading dimensions or an unaligned C take 2-byte stores.
+// column predicate keeps a row's padding and the next row intact.
+//
+// C rows need not start on a 16-byte boundary (odd ldc, or an unaligned C):
+// each staged row segment is cut at the 16-byte boundaries of its absolute
+// address, so that all but one of its 16-byte pieces are aligned stores; the
+// one piece that straddles the segment ends (sh elements at the head, 8 - sh
+// at the tail) is written element by element.
 template <int DT, class AT, int MR, int NR, int CH, int SROW, int WCOLS>
 __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                                              const typename AT::acc_t (&acc)[MR][NR],
@@ -227,6 +238,10 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
     constexpr int PPR = WCOLS / 8;                 // 16-byte pieces per staged row
     constexpr int PIECES = CH * R * PPR;
     const int lc = lane % R;
+    // element phase (mod 8) of this tile's C base
+    const uint32_t base_ph =
+        (uint32_t)((((uintptr_t)p.C) >> 1) + (uint64_t)m0 * (uint64_t)p.ldc + (uint32_t)col_w) & 7u;
+    const uint32_t ldc_ph = (uint32_t)p.ldc & 7u;
 #pragma unroll
     for (int cc = 0; cc < MR / CH; ++cc) {
 #pragma unroll
@@ -248,18 +263,54 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
             const int q = q0 + lane;
             if (PIECES % 64 == 0 || q < PIECES) {
                 const int prow = q / PPR, pc = q % PPR;
-                const i32x4 v = *reinterpret_cast<const i32x4*>(stage + prow * SROW + pc * 16);
                 const int trow = row0 + cc * CH * R + prow;   // row within the tile
-                const int gcol = col_w + pc * 8;
-                const uint32_t off = (uint32_t)(((int64_t)trow * p.ldc + gcol) * 2);
-                if (p.c_vec && gcol + 8 <= p.N) {
-                    store16(rc, off, v);
-                } else {
+                const uint32_t row_off = (uint32_t)((int64_t)trow * p.ldc + col_w);  // elements
+                const uint8_t* srow = stage + prow * SROW;
+                // elements before the row segment's first 16-byte boundary
+                const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
+                if (p.c_vec || sh == 0 || pc < PPR - 1) {
+                    const int o = (p.c_vec ? 0 : sh) + 8 * pc;     // staged column of the piece
+                    i32x4 v;
+                    if (p.c_vec || sh == 0) {
+                        v = *reinterpret_cast<const i32x4*>(srow + o * 2);
+                    } else {
+                        // 8 bf16 from a 2-byte aligned LDS offset: 5 dwords, funnel-shifted
+                        const uint32_t* d = reinterpret_cast<const uint32_t*>(srow + (o & ~1) * 2);
+                        const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
+                        const int odd = o & 1;
+                        v[0] = (int)(odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0);
+                        v[1] = (int)(odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1);
+                        v[2] = (int)(odd ? __builtin_amdgcn_alignbit(w3, w2, 16) : w2);
+                        v[3] = (int)(odd ? __builtin_amdgcn_alignbit(w4, w3, 16) : w3);
+                    }
+                    const int gcol = col_w + o;
+                    const uint32_t off = (row_off + (uint32_t)o) * 2u;
+                    if (gcol + 8 <= p.N) {
+                        store16(rc, off, v);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gcol + e < p.N)
-                            store2(rc, off + 2 * e, (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1))));
+                        for (int e = 0; e < 8; ++e)
+                            if (gcol + e < p.N)
+                                store2(rc, off + 2 * e,
+                                       (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1))));
+                    }
                 }
+            }
+        }
+        if (!p.c_vec) {
+            // The straddling piece of every row: head [0, sh) and tail
+            // [sh + 8 (PPR-1), WCOLS), one element per lane per store.
+            constexpr int ELEMS = CH * R * 8;
+#pragma unroll
+            for (int u0 = 0; u0 < ELEMS; u0 += 64) {
+                const int u = u0 + lane;
+                const int prow = u >> 3, e = u & 7;
+                const int trow = row0 + cc * CH * R + prow;
+                const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
+                const int col = e < sh ? e : sh + 8 * (PPR - 1) + (e - sh);
+                if (sh != 0 && col_w + col < p.N)
+                    store2(rc, ((uint32_t)((int64_t)trow * p.ldc + col_w) + (uint32_t)col) * 2u,
+                           *reinterpret_cast<const uint16_t*>(stage + prow * SROW + col * 2));
             }
         }
         __syncthreads();
@@ -276,40 +327,140 @@ constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
     return ch;
 }
 
-// Barrier without the workgroup memory fence of __syncthreads (which would
-// drain every outstanding load, prefetches included); an explicit vmcnt wait
-// before it is what makes the next stage visible.
-__device__ __forceinline__ void stage_barrier()
+// s_waitcnt (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vector-memory counter at most n, every LDS access of this
+// wave complete (lgkmcnt 0; expcnt left at its maximum).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// End of a k-tile: this wave's LDS reads of the stage are done and its share
+// of the next k-tile has landed (at most `vm` newer loads in flight); the
+// barrier then makes both true for the whole workgroup.  No workgroup memory
+// fence (__syncthreads would drain every outstanding load, prefetches
+// included).
+#define DG_STAGE_BARRIER(VM)                                     \
+    do {                                                         \
+        __builtin_amdgcn_sched_barrier(0);                       \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));        \
+        asm volatile("" ::: "memory");                           \
+        __builtin_amdgcn_s_barrier();                            \
+        asm volatile("" ::: "memory");                           \
+        __builtin_amdgcn_sched_barrier(0);                       \
+    } while (0)
+
+// Issue order inside one K step: its MFMAs with the LDS reads of the next
+// step (or of the next k-tile's first step) and this step's share of the
+// global loads spread between them, so that neither the LDS pipe nor the
+// texture-address FIFO sees all of a k-tile's requests in one burst ("GEMM
+// Optimization Guide" page, section 5: one VMEM per scheduler iteration, LDS
+// reads between MFMA groups).
+template <int MF, int RD, int VM>
+__device__ __forceinline__ void schedule_step()
 {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < RD)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < VM)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    if (RD > MF)
+        __builtin_amdgcn_sched_group_barrier(0x100, RD > MF ? RD - MF : 1, 0);
+    if (VM > MF)
+        __builtin_amdgcn_sched_group_barrier(0x020, VM > MF ? VM - MF : 1, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issue order of one k-tile's LDS reads and MFMAs: the reads of step 0, then
-// the MFMAs of each step with the next step's reads spread between them, so
-// that reads are in flight while MFMAs issue.
-template <int STEPS, int MF, int RD>
-__device__ __forceinline__ void schedule_ktile()
+// Fragment register sets: consecutive K steps alternate between sets, and a
+// trip of ST phases of STEPS steps must return to set 0, so the count
+// divides ST * STEPS: 2 when that is even, else its smallest odd divisor.
+constexpr int frag_sets(int st, int steps)
 {
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    const int n = st * steps;
+    if (n % 2 == 0)
+        return 2;
+    for (int d = 3; d < n; d += 2)
+        if (n % d == 0)
+            return d;
+    return n;
+}
+
+// Runs f(kt + i, integral_constant<i>) for i in I... (one trip of the
+// steady-state loop: ST phases with compile-time stage indices), and the
+// tail variant only while kt + i < nkt.
+template <class F, int... I>
+__device__ __forceinline__ void run_phases(F& f, int kt, std::integer_sequence<int, I...>)
+{
+    (f(kt + I, std::integral_constant<int, I>{}), ...);
+}
+template <class F, int... I>
+__device__ __forceinline__ void run_tail(F& f, int kt, int nkt, std::integer_sequence<int, I...>)
+{
+    ((kt + I < nkt ? f(kt + I, std::integral_constant<int, I>{}) : void()), ...);
+}
+
+// The K loop shared by both tiled kernels.  Phase t multiplies k-tile t out
+// of stage t % ST while k-tile t + ST - 1 streams into the stage that phase
+// t - 1 finished with; its loads are issued in STEPS parts, one at the start
+// of each K step.  The workgroup barrier of phase t sits before the
+// MFMAs of its last K step: after it, the first fragments of k-tile t + 1 are
+// read from LDS while those MFMAs run, so no LDS latency is exposed at the
+// k-tile boundary.  Fragment registers alternate between two sets along the
+// global sequence of K steps, NS = frag_sets(ST, STEPS) of them.
+//   load(kt, stage, part)      issue part `part` (of STEPS) of the loads of
+//                              k-tile kt (zeros past K)
+//   read(stage, step, set)     LDS -> fragment registers
+//   mma(stage, step, set)      the MFMAs of one K step
+template <int ST, int STEPS, int LOADS, int MF, int RD, class Load, class Read, class Mma>
+__device__ __forceinline__ void k_loop(int nkt, Load& load, Read& read, Mma& mma)
+{
+    constexpr int NS = frag_sets(ST, STEPS);
+    static_assert(ST >= 2 && (ST - 2) * LOADS <= 63, "pipeline depth vs vmcnt");
+    // Spreading the loads over the K steps keeps the texture-address FIFO from
+    // filling in a burst (measured: +10% on the register-B kernel); with a
+    // 2-stage ring the next k-tile's loads are needed one phase later, so
+    // they all go out at the start of the phase instead.
+    constexpr bool SPREAD = ST >= 3;
+    constexpr int VM = SPREAD ? (LOADS + STEPS - 1) / STEPS : 0;   // loads per K step
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        if (s + 1 < STEPS) {
+    for (int t = 0; t < ST - 1; ++t)
 #pragma unroll
-            for (int i = 0; i < MF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i < RD)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int part = 0; part < STEPS; ++part)
+            load(t, t, part);
+    DG_STAGE_BARRIER((ST - 2) * LOADS);
+    read(0, 0, 0);
+    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int si = decltype(sc)::value;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int cur = (si * STEPS + st) % NS;
+            const int nxt = (si * STEPS + st + 1) % NS;
+            if (SPREAD) {
+                load(t + ST - 1, (si + ST - 1) % ST, st);
+            } else if (st == 0) {
+#pragma unroll
+                for (int part = 0; part < STEPS; ++part)
+                    load(t + ST - 1, (si + ST - 1) % ST, part);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (RD > MF)
-                __builtin_amdgcn_sched_group_barrier(0x100, RD > MF ? RD - MF : 1, 0);
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+            if (st + 1 < STEPS) {
+                read(si, st + 1, nxt);
+            } else {
+                DG_STAGE_BARRIER((ST - 2) * LOADS);
+                read((si + 1) % ST, 0, nxt);
+            }
+            mma(si, st, cur);
+            schedule_step<MF, RD, VM>();
         }
-    }
+    };
+    int kt = 0;
+    for (; kt + ST <= nkt; kt += ST)
+        run_phases(phase, kt, std::make_integer_sequence<int, ST>{});
+    run_tail(phase, kt, nkt, std::make_integer_sequence<int, ST - 1>{});
+    // Loads past nkt (zeros) still target LDS: drain them everywhere before
+    // the epilogue reuses it.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -317,35 +468,38 @@ __device__ __forceinline__ void schedule_ktile()
 // WM x 4 waves, the 4 wave columns splitting tile_n (section 1.1); A through
 // LDS (ST-stage ring fed by LDS DMA), B straight from the preshuffled layout
 // into VGPRs (section 4.2), ST - 1 k-tiles ahead.
-template <int TM, int TN, int WM, int ST, int R>
+template <int TM, int TN, int WM, int ST, int R, int KTB>
 struct TiledShape {
+    using KT = KTile<KTB>;
     static constexpr int WAVES = 4 * WM;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int MR = TM / WM / R;        // atoms per wave along M
-    static constexpr int NR = TN / 4 / R;         // atoms per wave along N
-    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
-    static constexpr int A_BUF = TM * 128;        // bytes of one A stage
-    static constexpr int B_LOADS = TN / 32;       // 16-byte B loads per lane per k-tile
-    static constexpr int LOADS = A_DMA + B_LOADS; // vector-memory ops per wave per k-tile
-    static constexpr int WCOLS = TN / 4;          // C columns per wave
-    static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
+    static constexpr int MR = TM / WM / R;          // atoms per wave along M
+    static constexpr int NR = TN / 4 / R;           // atoms per wave along N
+    static constexpr int A_BUF = TM * KTB;          // bytes of one A stage
+    static constexpr int A_DMA = A_BUF / 1024 / WAVES;
+    static constexpr int B_LOADS = TN * KTB / 4096;  // 16-byte B loads per lane per k-tile
+    static constexpr int LOADS = A_DMA + B_LOADS;   // vector-memory ops per wave per k-tile
+    static constexpr int WCOLS = TN / 4;            // C columns per wave
+    static constexpr int SROW = WCOLS * 2 + 16;     // staging row pitch (padded)
     static constexpr int CH = fit_stage_rows(MR, WAVES, R, SROW, ST * A_BUF);
     static constexpr int LDS = (ST * A_BUF > WAVES * CH * R * SROW) ? ST * A_BUF
                                                                     : WAVES * CH * R * SROW;
     static_assert(MR >= 1 && NR >= 1 && MR * WM * R == TM && NR * 4 * R == TN, "tile shape");
-    static_assert(A_DMA >= 1 && A_DMA * 8 * WAVES == TM, "A DMA split");
-    static_assert(ST >= 2 && ST <= 4 && (ST - 2) * LOADS <= 63, "pipeline depth");
+    static_assert(A_DMA >= 1 && A_DMA * 1024 * WAVES == A_BUF, "A DMA split");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int ST, int R>
+template <int DT, int TM, int TN, int WM, int ST, int R, int KTB>
 __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 {
-    using S = TiledShape<TM, TN, WM, ST, R>;
+    using S = TiledShape<TM, TN, WM, ST, R, KTB>;
+    using KT = KTile<KTB>;
     using AT = Atom<DT, R>;
     using acc_t = typename AT::acc_t;
     constexpr int MR = S::MR, NR = S::NR, A_DMA = S::A_DMA, A_BUF = S::A_BUF;
-    constexpr int WAVES = S::WAVES, STEPS = AT::STEPS, P = AT::P;
+    constexpr int WAVES = S::WAVES, P = AT::P, KPK = KT::KPK;
+    constexpr int STEPS = AT::STEPS * KTB / 128;    // K steps per k-tile
+    static_assert(STEPS >= 1 && AT::STEPS * KTB % 128 == 0, "atom does not fit the k-tile");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
 
     const int tid = threadIdx.x;
@@ -357,6 +511,8 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
+    const int nkt = (p.KB + KPK - 1) / KPK;
+    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;   // first k-tile that needs masking
 
     // Descriptors rebased at this tile: rows past M and 16-column blocks past
     // ceil(N/16) fall outside and read as zero.
@@ -370,15 +526,16 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     ADma ad[A_DMA];
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
-        ad[i] = a_dma_lane(wave + WAVES * i, lane, p.lda_b);
+        ad[i] = a_dma_lane<KTB>(wave + WAVES * i, lane, p.lda_b);
     const int lr = lane % R;                       // row / column of this lane in an atom
-    const uint32_t swz = (uint32_t)((lane & 15) >> 1) & 7;
+    const uint32_t swz = KT::key((uint32_t)(lane & 15));
     const uint32_t row0 = (uint32_t)(wm * (TM / WM));   // first A row of this wave
     // 16-column block of this lane's column in atom 0 of this wave
     const uint32_t bblk = (uint32_t)(wn * NR * (R / 16) + (lr >> 4));
     const uint32_t b_lane = bblk * (uint32_t)p.KB * 1024u + (uint32_t)(lane & 15) * 16;
 
     i32x4 breg[ST][NR][STEPS][P];
+    i32x4 af[frag_sets(ST, STEPS)][MR][P];
     acc_t acc[MR][NR];
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
@@ -388,110 +545,54 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 
     // A k-tile past the real K (kt >= nkt, or the K tail of the last one)
     // loads through out-of-range offsets: zeros, and no memory traffic.
-    const int last_full = p.tail ? p.nkt - 1 : p.nkt;   // first k-tile that needs masking
-    auto load_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    // Load op n (A DMAs first, then B fragments) belongs to part n % STEPS.
+    auto load = [&](int kt, int stage, int part) __attribute__((always_inline)) {
         const bool mask = kt >= last_full;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            uint32_t off = ad[i].goff + (uint32_t)kt * 128;
-            if (mask && (int)((uint32_t)kt * 128 + ad[i].col) >= p.KA_b)
+            if (i % STEPS != part)
+                continue;
+            uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(lds + stage * A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
         }
-    };
-    auto load_b = [&](i32x4 (&dst)[NR][STEPS][P], int kt) __attribute__((always_inline)) {
-        const bool mask = kt >= last_full;
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
             for (int s = 0; s < STEPS; ++s)
 #pragma unroll
                 for (int q = 0; q < P; ++q) {
-                    const int kb = kt * 2 + AT::b_half(s, q);
+                    if ((A_DMA + (j * STEPS + s) * P + q) % STEPS != part)
+                        continue;
+                    const int kb = kt * KPK + AT::b_half(s, q);
                     uint32_t off = b_lane + (uint32_t)(j * (R / 16) * p.KB + kb) * 1024u +
                                    ((uint32_t)AT::b_group(s, lane, q) << 8);
                     if (mask && kb >= p.KB)
                         off = kOOB;
-                    dst[j][s][q] = load16(rb, off);
+                    breg[stage][j][s][q] = load16(rb, off);
                 }
     };
-    auto read_a = [&](int stage, int s, i32x4 (&dst)[MR][P]) __attribute__((always_inline)) {
+    auto read = [&](int stage, int s, int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
             for (int q = 0; q < P; ++q) {
                 const uint32_t row = row0 + (uint32_t)(mi * R + lr);
-                const uint32_t off = (uint32_t)(stage * A_BUF) + row * 128 +
+                const uint32_t off = (uint32_t)(stage * A_BUF) + row * KTB +
                                      (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
-                dst[mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
+                af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
     };
-    auto compute = [&](int stage, const i32x4 (&b)[NR][STEPS][P]) __attribute__((always_inline)) {
-        i32x4 af[2][MR][P];
-        read_a(stage, 0, af[0]);
+    auto mma = [&](int stage, int s, int set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            if (s + 1 < STEPS)
-                read_a(stage, s + 1, af[(s + 1) & 1]);
+        for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
-            for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-                for (int j = 0; j < NR; ++j)
-                    acc[mi][j] = AT::mma(af[s & 1][mi], b[j][s], acc[mi][j]);
-        }
-        schedule_ktile<STEPS, MR * NR, MR * P>();
+            for (int j = 0; j < NR; ++j)
+                acc[mi][j] = AT::mma(af[set][mi], breg[stage][j][s], acc[mi][j]);
     };
-
-    // Prologue: k-tiles 0 .. ST-2 in flight, wait for k-tile 0.
-#pragma unroll
-    for (int t = 0; t < ST - 1; ++t) {
-        load_a(t, t);
-        load_b(breg[t], t);
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-    stage_barrier();
-
-    // Phase t multiplies k-tile t out of stage t % ST while k-tile t + ST - 1
-    // streams into the stage that phase t - 1 just finished with.  At the end
-    // of the phase, k-tile t + 1 must have landed: at most the ST - 2 newer
-    // k-tiles' loads may still be in flight.  Loads past nkt read zeros.
-    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        constexpr int pre = (s + ST - 1) % ST;
-        load_a(t + ST - 1, pre);
-        load_b(breg[pre], t + ST - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(s, breg[s]);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-        stage_barrier();
-    };
-    // Steady state: ST unconditional phases per trip (no control-flow merges
-    // inside the loop, so the accumulators keep their registers); the last
-    // nkt % ST k-tiles run after it.
-    int kt = 0;
-    for (; kt + ST <= p.nkt; kt += ST) {
-        phase(kt, std::integral_constant<int, 0>{});
-        phase(kt + 1, std::integral_constant<int, 1>{});
-        if constexpr (ST > 2)
-            phase(kt + 2, std::integral_constant<int, 2>{});
-        if constexpr (ST > 3)
-            phase(kt + 3, std::integral_constant<int, 3>{});
-    }
-    if (kt < p.nkt)
-        phase(kt, std::integral_constant<int, 0>{});
-    if constexpr (ST > 2) {
-        if (kt + 1 < p.nkt)
-            phase(kt + 1, std::integral_constant<int, 1>{});
-    }
-    if constexpr (ST > 3) {
-        if (kt + 2 < p.nkt)
-            phase(kt + 2, std::integral_constant<int, 2>{});
-    }
-    // The zero prefetches past nkt still target LDS: drain them everywhere
-    // before the epilogue reuses it.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
+    k_loop<ST, STEPS, S::LOADS, MR * NR, MR * P>(nkt, load, read, mma);
 
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
@@ -511,43 +612,46 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 // MI355X, the L2 -> CU path, not the MFMA, bounds that kernel once the tile
 // is large.  Here each k-tile of A *and* B enters the workgroup once, by
 // 16-byte LDS DMA, and the WM x WN waves read their fragments from LDS.  The
-// preshuffled B blocks (1 KiB = 16 columns x 64 K bytes) land in LDS
-// unchanged, so a B fragment read is a run of 256 contiguous bytes per 16
-// lanes.  Per stage: [A: TM rows x 128 B, XOR-swizzled][B: TN/16 blocks x 2
-// halves x 1 KiB].
-template <int TM, int TN, int WM, int WN, int ST, int R>
+// preshuffled B blocks land in LDS unchanged, so a B fragment read is a run
+// of 256 contiguous bytes per 16 lanes.  Per stage: [A: TM rows x KTB bytes,
+// swizzled][B: TN/16 blocks x KTB/64 x 1 KiB].
+template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
 struct ABShape {
+    using KT = KTile<KTB>;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int MR = TM / WM / R;        // atoms per wave along M
-    static constexpr int NR = TN / WN / R;        // atoms per wave along N
-    static constexpr int A_BUF = TM * 128;
-    static constexpr int B_BUF = TN * 128;
+    static constexpr int MR = TM / WM / R;          // atoms per wave along M
+    static constexpr int NR = TN / WN / R;          // atoms per wave along N
+    static constexpr int A_BUF = TM * KTB;
+    static constexpr int B_BUF = TN * KTB;
     static constexpr int STAGE = A_BUF + B_BUF;
-    static constexpr int A_DMA = TM / 8 / WAVES;  // 1 KiB A loads per wave per k-tile
-    static constexpr int B_DMA = TN / 8 / WAVES;  // 1 KiB B loads per wave per k-tile
+    static constexpr int A_DMA = A_BUF / 1024 / WAVES;  // 1 KiB A loads per wave per k-tile
+    static constexpr int B_DMA = B_BUF / 1024 / WAVES;  // 1 KiB B loads per wave per k-tile
     static constexpr int LOADS = A_DMA + B_DMA;
-    static constexpr int WCOLS = TN / WN;         // C columns per wave
-    static constexpr int SROW = WCOLS * 2 + 16;   // staging row pitch (padded)
+    static constexpr int WCOLS = TN / WN;           // C columns per wave
+    static constexpr int SROW = WCOLS * 2 + 16;     // staging row pitch (padded)
     static constexpr int CH = fit_stage_rows(MR, WAVES, R, SROW, ST * STAGE);
     static constexpr int LDS = (ST * STAGE > WAVES * CH * R * SROW) ? ST * STAGE
                                                                     : WAVES * CH * R * SROW;
     static_assert(MR >= 1 && NR >= 1 && MR * WM * R == TM && NR * WN * R == TN, "tile shape");
-    static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * 8 * WAVES == TM && B_DMA * 8 * WAVES == TN,
+    static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * 1024 * WAVES == A_BUF &&
+                      B_DMA * 1024 * WAVES == B_BUF,
                   "DMA split");
-    static_assert(ST >= 2 && ST <= 4 && (ST - 2) * LOADS <= 63, "pipeline depth");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int WN, int ST, int R>
+template <int DT, int TM, int TN, int WM, int WN, int ST, int R, int KTB>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 {
-    using S = ABShape<TM, TN, WM, WN, ST, R>;
+    using S = ABShape<TM, TN, WM, WN, ST, R, KTB>;
+    using KT = KTile<KTB>;
     using AT = Atom<DT, R>;
     using acc_t = typename AT::acc_t;
     constexpr int MR = S::MR, NR = S::NR, A_BUF = S::A_BUF, STAGE = S::STAGE;
     constexpr int WAVES = S::WAVES, A_DMA = S::A_DMA, B_DMA = S::B_DMA;
-    constexpr int STEPS = AT::STEPS, P = AT::P;
+    constexpr int P = AT::P, KPK = KT::KPK;
+    constexpr int STEPS = AT::STEPS * KTB / 128;
+    static_assert(STEPS >= 1 && AT::STEPS * KTB % 128 == 0, "atom does not fit the k-tile");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
 
     const int tid = threadIdx.x;
@@ -559,6 +663,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
+    const int nkt = (p.KB + KPK - 1) / KPK;
+    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;
     const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
                                 (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
     const int nb0 = n0 >> 4;
@@ -566,26 +672,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
                                 (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 
-    // A chunk w + WAVES*i: rows 8c .. 8c+7.  B chunk w + WAVES*i: 16-column
-    // block b / 2, 64-byte half b % 2 of the k-tile.
+    // A chunk w + WAVES*i: rows (1024/KTB) c ...  B chunk b = w + WAVES*i:
+    // 16-column block b / KPK, 64-byte block b % KPK of the k-tile.
     ADma ad[A_DMA];
     uint32_t b_goff[B_DMA], b_half[B_DMA];
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
-        ad[i] = a_dma_lane(wave + WAVES * i, lane, p.lda_b);
+        ad[i] = a_dma_lane<KTB>(wave + WAVES * i, lane, p.lda_b);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
         const uint32_t b = wave + WAVES * i;
-        b_goff[i] = ((b >> 1) * (uint32_t)p.KB + (b & 1)) * 1024u + lane * 16;
-        b_half[i] = b & 1;
+        b_goff[i] = ((b / KPK) * (uint32_t)p.KB + (b % KPK)) * 1024u + lane * 16;
+        b_half[i] = b % KPK;
     }
     const int lr = lane % R;
-    const uint32_t swz = (uint32_t)((lane & 15) >> 1) & 7;
+    const uint32_t swz = KT::key((uint32_t)(lane & 15));
     const uint32_t row0 = (uint32_t)(wm * (TM / WM));
     // LDS byte offset (within a stage's B region) of this lane's column in
-    // atom 0 of this wave, group 0, half 0.
-    const uint32_t b_lds = (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * 2048 + (lane & 15) * 16);
+    // atom 0 of this wave, group 0, 64-byte block 0.
+    const uint32_t b_lds =
+        (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * KPK * 1024 + (lane & 15) * 16);
 
+    i32x4 af[frag_sets(ST, STEPS)][MR][P], bf[frag_sets(ST, STEPS)][NR][P];
     acc_t acc[MR][NR];
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
@@ -593,101 +701,60 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         for (int j = 0; j < NR; ++j)
             acc[mi][j] = zero_acc<AT>();
 
-    const int last_full = p.tail ? p.nkt - 1 : p.nkt;
-    auto load = [&](int kt, int stage) __attribute__((always_inline)) {
+    // Load op n (A DMAs first, then B DMAs) belongs to part n % STEPS.
+    auto load = [&](int kt, int stage, int part) __attribute__((always_inline)) {
         const bool mask = kt >= last_full;
         uint8_t* base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            uint32_t off = ad[i].goff + (uint32_t)kt * 128;
-            if (mask && (int)((uint32_t)kt * 128 + ad[i].col) >= p.KA_b)
+            if (i % STEPS != part)
+                continue;
+            uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) {
-            uint32_t off = b_goff[i] + (uint32_t)kt * 2048u;
-            if (mask && kt * 2 + (int)b_half[i] >= p.KB)
+            if ((A_DMA + i) % STEPS != part)
+                continue;
+            uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
+            if (mask && kt * KPK + (int)b_half[i] >= p.KB)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
         }
     };
-    auto read_frags = [&](int stage, int s, i32x4 (&af)[MR][P], i32x4 (&bf)[NR][P])
-                          __attribute__((always_inline)) {
+    auto read = [&](int stage, int s, int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
             for (int q = 0; q < P; ++q) {
                 const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) + b_lds +
-                                     (uint32_t)(j * (R / 16) * 2048) +
+                                     (uint32_t)(j * (R / 16) * KPK * 1024) +
                                      ((uint32_t)AT::b_half(s, q) << 10) +
                                      ((uint32_t)AT::b_group(s, lane, q) << 8);
-                bf[j][q] = *reinterpret_cast<const i32x4*>(lds + off);
+                bf[set][j][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
             for (int q = 0; q < P; ++q) {
                 const uint32_t row = row0 + (uint32_t)(mi * R + lr);
-                const uint32_t off = (uint32_t)(stage * STAGE) + row * 128 +
+                const uint32_t off = (uint32_t)(stage * STAGE) + row * KTB +
                                      (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
-                af[mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
+                af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
     };
-    auto compute = [&](int stage) __attribute__((always_inline)) {
-        i32x4 af[2][MR][P], bf[2][NR][P];
-        read_frags(stage, 0, af[0], bf[0]);
+    auto mma = [&](int, int, int set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            if (s + 1 < STEPS)
-                read_frags(stage, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+        for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
-            for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-                for (int j = 0; j < NR; ++j)
-                    acc[mi][j] = AT::mma(af[s & 1][mi], bf[s & 1][j], acc[mi][j]);
-        }
-        schedule_ktile<STEPS, MR * NR, (MR + NR) * P>();
+            for (int j = 0; j < NR; ++j)
+                acc[mi][j] = AT::mma(af[set][mi], bf[set][j], acc[mi][j]);
     };
-    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        constexpr int pre = (s + ST - 1) % ST;
-        load(t + ST - 1, pre);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(s);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-        stage_barrier();
-    };
-
-#pragma unroll
-    for (int t = 0; t < ST - 1; ++t)
-        load(t, t);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((ST - 2) * S::LOADS));
-    stage_barrier();
-
-    int kt = 0;
-    for (; kt + ST <= p.nkt; kt += ST) {
-        phase(kt, std::integral_constant<int, 0>{});
-        phase(kt + 1, std::integral_constant<int, 1>{});
-        if constexpr (ST > 2)
-            phase(kt + 2, std::integral_constant<int, 2>{});
-        if constexpr (ST > 3)
-            phase(kt + 3, std::integral_constant<int, 3>{});
-    }
-    if (kt < p.nkt)
-        phase(kt, std::integral_constant<int, 0>{});
-    if constexpr (ST > 2) {
-        if (kt + 1 < p.nkt)
-            phase(kt + 1, std::integral_constant<int, 1>{});
-    }
-    if constexpr (ST > 3) {
-        if (kt + 2 < p.nkt)
-            phase(kt + 2, std::integral_constant<int, 2>{});
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
+    k_loop<ST, STEPS, S::LOADS, MR * NR, (MR + NR) * P>(nkt, load, read, mma);
 
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {

@@ -65,21 +65,21 @@ hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStre
                            dim3(256), args, 0, s);
 }
 
-int ab_lds_bytes(int tm, int tn, int waves, int atom)
+int ab_lds_bytes(int idx)
 {
-#define DG_CASE(M_, N_, WM_, WN_, ST_, R_)                            \
-    if (tm == M_ && tn == N_ && waves == WM_ * WN_ && atom == R_)     \
-        return ABShape<M_, N_, WM_, WN_, ST_, R_>::LDS;
+    int i = 0;
+#define DG_CASE(M_, N_, WM_, WN_, ST_, R_, KTB_) \
+    if (idx == i++) return ABShape<M_, N_, WM_, WN_, ST_, R_, KTB_>::LDS;
     DG_AB_LADDER(DG_CASE)
 #undef DG_CASE
     return -1;
 }
 
-int tiled_lds_bytes(int tm, int tn, int waves, int atom)
+int tiled_lds_bytes(int idx)
 {
-#define DG_CASE(M_, N_, W_, R_)                                  \
-    if (tm == M_ && tn == N_ && waves == W_ && atom == R_)       \
-        return TiledShape<M_, N_, W_ / 4, tiled_stages(W_), R_>::LDS;
+    int i = 0;
+#define DG_CASE(M_, N_, W_, ST_, R_, KTB_) \
+    if (idx == i++) return TiledShape<M_, N_, W_ / 4, ST_, R_, KTB_>::LDS;
     DG_TILED_LADDER(DG_CASE)
 #undef DG_CASE
     return -1;

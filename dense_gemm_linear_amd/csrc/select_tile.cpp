@@ -54,25 +54,28 @@ double atom_rate(int dt, int atom)
     return 0.98;
 }
 
-void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4, int atom = 16)
+void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4, int atom = 16,
+                 int stages = 0, int ktb = 128)
 {
     memset(&t, 0, sizeof t);
     t.kernel = kernel;
     t.tile_m = tm;
     t.tile_n = tn;
-    t.tile_k = dt == GEMM_BF16 ? 64 : 128;
+    t.tile_k = kernel == GEMM_KERNEL_SKINNY ? 0 : ktb / (dt == GEMM_BF16 ? 2 : 1);
     t.atom = atom;
     t.waves = waves;
     t.k_split = kernel == GEMM_KERNEL_SKINNY ? 4 : 1;
-    t.lds_stages = kernel == GEMM_KERNEL_TILED ? 2 : 0;
+    t.lds_stages = stages;
 }
 
-bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, const TiledRung& r,
+bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const TiledRung& r,
                  const Chip& c, Cand& out)
 {
     const int tm = r.tm, tn = r.tn, waves = r.waves;
-    const int lds = tiled_lds_bytes(tm, tn, waves, r.atom);
-    const int vgpr = tiled_vgpr_estimate(tm, tn, waves, r.atom);
+    if (dt == GEMM_FP8_E4M3 && r.atom == 16 && r.ktb != 128)
+        return false;
+    const int lds = tiled_lds_bytes(idx);
+    const int vgpr = tiled_vgpr_estimate(r);
     if (lds < 0 || lds > c.lds_per_cu || vgpr > 512)
         return false;
     const int waves_per_simd = std::min(8, 512 / align8(vgpr));
@@ -95,7 +98,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, const TiledRu
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves, r.atom);
+    fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
     const int64_t rounds = cdiv(tiles, cus);
     out.t.tile_eff = (float)te;
@@ -108,11 +111,11 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, const TiledRu
 
 // A and B staged in LDS: each k-tile enters the workgroup once; waves read
 // their A and B fragments from LDS.
-bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r, const Chip& c,
-              Cand& out)
+bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const ABRung& r,
+              const Chip& c, Cand& out)
 {
     const int waves = r.wm * r.wn;
-    const int lds = ab_lds_bytes(r.tm, r.tn, waves, r.atom);
+    const int lds = ab_lds_bytes(idx);
     if (lds < 0 || lds > c.lds_per_cu)
         return false;
     // accumulators + two sets of fragments + addresses
@@ -136,12 +139,11 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, const ABRung& r,
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves, r.atom);
+    fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
     const int64_t rounds = cdiv(tiles, cus);
     out.t.tile_eff = (float)te;
     out.t.wq_eff = (float)((double)tiles / ((double)rounds * cus));
-    out.t.lds_stages = r.st;
     out.t.predicted_us = (float)us;
     out.us = us;
     out.screened = 1.0 / te > 1.25;
@@ -177,30 +179,36 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int 
 
 }  // namespace
 
-int tiled_vgpr_estimate(int tm, int tn, int waves, int atom)
+int tiled_vgpr_estimate(const TiledRung& r)
 {
-    (void)atom;
-    const int acc = tm * tn / (waves * 64);          // fp32 accumulators per lane
-    const int b = tn / 32 * 4 * tiled_stages(waves);  // B k-tiles in flight
+    const int acc = r.tm * r.tn / (r.waves * 64);         // fp32 accumulators per lane
+    const int b = r.tn * r.ktb / 4096 * 4 * r.st;          // B k-tiles in flight
     const int a_frag = 8;
     const int misc = 40;                      // addresses, offsets, loop state
     return acc + b + a_frag + misc;
 }
 
-bool tiled_supported(int tm, int tn, int waves, int atom)
+int tiled_rung(int tm, int tn, int waves, int atom, int st, int ktb)
 {
-    for (const TiledRung& r : kTiledLadder)
-        if (r.tm == tm && r.tn == tn && r.waves == waves && r.atom == atom)
-            return true;
-    return false;
+    int i = 0;
+    for (const TiledRung& r : kTiledLadder) {
+        if (r.tm == tm && r.tn == tn && r.waves == waves && r.atom == atom && DG_MATCH(r.st, r.ktb))
+            return i;
+        ++i;
+    }
+    return -1;
 }
 
-bool ab_supported(int tm, int tn, int waves, int atom)
+int ab_rung(int tm, int tn, int waves, int atom, int st, int ktb)
 {
-    for (const ABRung& r : kABLadder)
-        if (r.tm == tm && r.tn == tn && r.wm * r.wn == waves && r.atom == atom)
-            return true;
-    return false;
+    int i = 0;
+    for (const ABRung& r : kABLadder) {
+        if (r.tm == tm && r.tn == tn && r.wm * r.wn == waves && r.atom == atom &&
+            DG_MATCH(r.st, r.ktb))
+            return i;
+        ++i;
+    }
+    return -1;
 }
 
 bool skinny_supported(int tm, int tn)
@@ -234,14 +242,16 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
                     consider(cd);
             }
     }
+    int idx = 0;
     for (const TiledRung& r : kTiledLadder) {
         Cand cd;
-        if (price_tiled(M, N, K, dt, cus, r, chip, cd))
+        if (price_tiled(M, N, K, dt, cus, idx++, r, chip, cd))
             consider(cd);
     }
+    idx = 0;
     for (const ABRung& r : kABLadder) {
         Cand cd;
-        if (price_ab(M, N, K, dt, cus, r, chip, cd))
+        if (price_ab(M, N, K, dt, cus, idx++, r, chip, cd))
             consider(cd);
     }
     *out = have ? best.t : best_screened.t;

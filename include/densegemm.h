@@ -55,32 +55,47 @@ typedef enum {
 } gemm_kernel;
 
 /*
- * One launch configuration.  Inputs to the kernels: kernel, tile_m, tile_n
- * (and for the skinny kernel k_split).  The remaining fields are reported by
+ * One launch configuration.  Inputs to the kernels: kernel, tile_m, tile_n,
+ * waves, atom, tile_k and lds_stages (and for the skinny kernel the rows and
+ * columns only).  tile_eff, wq_eff and predicted_us are reported by
  * select_tile for information and ignored when a tile is forced.
  *
- *   tiled:  (tile_m, tile_n, waves) in {256x128, 256x64, 128x256, 128x128,
- *           128x64, 64x256, 64x128, 64x64, 32x256, 32x128, 32x64} with 4 waves
- *           of 64 lanes splitting tile_n ("GEMM Optimization Guide" page,
- *           sections 1.1 and 1.4), or {256x256, 256x128, 128x256, 128x128}
- *           with 8 waves (2 rows x 4 columns); tile_k is 128 bytes of K (64
- *           bf16 or 128 e4m3).
- *   tiled_ab: (tile_m, tile_n, waves) in {256x256 x 8, 256x256 x 4,
- *           256x128 x 4, 128x256 x 4, 128x128 x 4}; the waves form a 2 x
- *           (waves/2) grid and A and B are both staged in LDS.
+ * A forced tiled or A+B tile names one rung of a ladder by its fields; atom 0
+ * means 16, and tile_k 0 or lds_stages 0 match the first rung that agrees
+ * on the other fields.
+ *
+ *   tiled (A through LDS, B from the preshuffled layout straight into
+ *   registers; waves 4 split tile_n, waves 8 form 2 x 4):
+ *     16 x 16 atoms, 128-byte k-tiles: 256x128, 128x256, 128x128 with 8 waves
+ *       and 2 stages; 256x128, 256x64, 128x256, 128x128, 128x64, 64x256,
+ *       64x128, 64x64, 32x256, 32x128, 32x64 with 4 waves and 3 stages
+ *       ("GEMM Optimization Guide" page, sections 1.1 and 1.4);
+ *     32 x 32 atoms, 128-byte k-tiles: 256x256, 256x128, 128x256, 128x128
+ *       with 8 waves and 2 stages; 256x128, 128x256, 128x128, 64x256, 64x128
+ *       with 4 waves and 3 stages;
+ *     32 x 32 atoms, 64-byte k-tiles, 4 waves, 4 stages: 128x256, 128x128,
+ *       256x128.
+ *   tiled_ab (A and B both through LDS; waves form 2 x waves/2):
+ *     16 x 16, 128-byte k-tiles, 4 waves, 3 stages: 256x128, 128x256, 128x128;
+ *     32 x 32, 128-byte k-tiles: 256x256 (8 or 4 waves, 2 stages), 256x128
+ *       (8 or 4 waves, 3 stages), 128x256 and 128x128 (4 waves, 3 stages);
+ *     32 x 32, 64-byte k-tiles: 256x256 with 8 waves and 4 or 5 stages or 4
+ *       waves and 4 stages, 256x128 with 8 waves and 6 stages, 128x256 with
+ *       4 waves and 6 stages.
+ *   16 x 16 e4m3 atoms need 128-byte k-tiles.
  *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering
- *           M), tile_n in {16, 32, 64} (16-column blocks per workgroup),
- *           k_split = waves that split K in one workgroup (4).
+ *     M), tile_n in {16, 32, 64} (16-column blocks per workgroup), k_split
+ *     = waves that split K in one workgroup (4).
  */
 typedef struct {
     int32_t kernel;      /* gemm_kernel */
     int32_t tile_m;
     int32_t tile_n;
-    int32_t tile_k;      /* elements of K per pipeline stage (informational) */
-    int32_t atom;        /* MFMA block edge: 16 (informational) */
-    int32_t waves;       /* waves per workgroup (selects the rung of a ladder) */
-    int32_t k_split;     /* skinny: waves splitting K */
-    int32_t lds_stages;  /* 2 = ping-pong A buffers (informational) */
+    int32_t tile_k;      /* elements of K per pipeline stage (k-tile); 0 = any */
+    int32_t atom;        /* MFMA block edge: 16 or 32 (0 = 16) */
+    int32_t waves;       /* waves per workgroup */
+    int32_t k_split;     /* skinny: waves splitting K (informational) */
+    int32_t lds_stages;  /* k-tiles in the LDS ring (2 = ping-pong); 0 = any */
     float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */
     float wq_eff;        /* tiles / (ceil(tiles / CUs) * CUs) */
     float predicted_us;  /* cost model estimate (informational) */
@@ -180,6 +195,14 @@ gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* 
 gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
                             const float* scale_b, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
                             int64_t K, const gemm_tile* tile, void* stream);
+
+/*
+ * gemm_tile_check -- would `tile`, forced on gemm_bf16 (dtype GEMM_BF16) or
+ * gemm_fp8_scaled (GEMM_FP8_E4M3) with M rows, name a rung the library has?
+ * Pure host function, no device access.  GEMM_OK if so, GEMM_ERR_UNSUPPORTED
+ * if not, GEMM_ERR_INVALID_VALUE for tile == NULL, M < 0 or an unknown dtype.
+ */
+gemm_status gemm_tile_check(const gemm_tile* tile, int64_t M, gemm_dtype dtype);
 
 /* Static, human-readable name of a status code ("GEMM_OK", ...). */
 const char* gemm_status_string(gemm_status status);

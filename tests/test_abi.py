@@ -61,8 +61,11 @@ def test_select_tile_metrics_match_oracle(M, N, K, dt):
     t = dg.select_tile(M, N, K, dt, num_cus=256)
     assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY, dg.GEMM_KERNEL_TILED_AB)
     if t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB):
-        ladder = dg.TILED_LADDER if t.kernel == dg.GEMM_KERNEL_TILED else dg.AB_LADDER
-        assert (t.tile_m, t.tile_n, t.waves, t.atom) in ladder
+        assert t in dg.ladder_tiles(dt) or any(
+            (t.kernel, t.tile_m, t.tile_n, t.waves, t.atom, t.lds_stages, t.tile_k) ==
+            (r.kernel, r.tile_m, r.tile_n, r.waves, r.atom, r.lds_stages, r.tile_k)
+            for r in dg.ladder_tiles(dt))
+        assert dg.tile_check(t, M, dt) == dg.GEMM_OK
         tiles, te, we, de = oracle.dim_eff(M, N, t.tile_m, t.tile_n, 256)
         assert abs(t.tile_eff - te) < 1e-6 and abs(t.wq_eff - we) < 1e-6
         # padding screen: padded output at most 1.25x the real one when any tile passes
@@ -72,6 +75,28 @@ def test_select_tile_metrics_match_oracle(M, N, K, dt):
         assert M <= t.tile_m < M + 16
     assert t.predicted_us > 0
     assert dg.select_tile(M, N, K, dt, num_cus=256) == t       # deterministic
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_every_python_rung_is_a_library_rung(dt):
+    tiles = dg.ladder_tiles(dt)
+    assert len({t.name for t in tiles}) == len(tiles)            # no duplicates
+    for t in tiles:
+        assert dg.tile_check(t, 1000, dt) == dg.GEMM_OK, t.name
+    for tm, tn in dg.SKINNY_LADDER:
+        assert dg.tile_check(dg.skinny(tm, tn), tm, dt) == dg.GEMM_OK
+        assert dg.tile_check(dg.skinny(tm, tn), tm + 1, dt) == dg.GEMM_ERR_UNSUPPORTED
+    # wildcards: stages / tile_k 0 pick the first matching rung
+    assert dg.tile_check(dg.tiled(128, 128), 100, dt) == dg.GEMM_OK
+    assert dg.tile_check(dg.tiled_ab(256, 256, 8, 32), 100, dt) == dg.GEMM_OK
+    # not rungs
+    U = dg.GEMM_ERR_UNSUPPORTED
+    assert dg.tile_check(dg.tiled(96, 128), 100, dt) == U
+    assert dg.tile_check(dg.tiled(128, 128, 4, 32, stages=7), 100, dt) == U
+    assert dg.tile_check(dg.tiled(128, 128, 4, 32, tile_k=48), 100, dt) == U
+    assert dg.tile_check(dg.tiled_ab(256, 256, 8, 16), 100, dt) == U
+    assert dg.tile_check(dg.Tile(7, 128, 128), 100, dt) == U
+    assert dg.lib.gemm_tile_check(None, 1, 0) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def test_select_tile_routes_small_m_to_skinny():

@@ -92,27 +92,9 @@ def test_workload_shapes_sampled(name, smallint):
 EVERY_SHAPE = (263, 270, 176)   # divides no tile in M, N or the 64-element k-tile
 
 
-@pytest.mark.parametrize("tm,tn,waves,atom", dg.TILED_LADDER)
-def test_every_tiled_tile(tm, tn, waves, atom):
+@pytest.mark.parametrize("tile", dg.ladder_tiles("bf16"), ids=lambda t: t.name)
+def test_every_ladder_tile(tile):
     M, N, K = EVERY_SHAPE
-    tile = dg.tiled(tm, tn, waves, atom)
-    for smallint in (False, True):
-        A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
-                                      "smallint" if smallint else "normal", config=9)
-        C, ok = run("bf16", A, B, tile=tile)
-        assert ok, "guard band written"
-        Cref = oracle_full("bf16", A, B)
-        if smallint:
-            check_exact(C, Cref, tile.name)
-        else:
-            check_close("bf16", C, Cref, oracle_full("bf16", abs_bits("bf16", A), abs_bits("bf16", B)),
-                        K, what=tile.name)
-
-
-@pytest.mark.parametrize("tm,tn,waves,atom", dg.AB_LADDER)
-def test_every_ab_tile(tm, tn, waves, atom):
-    M, N, K = EVERY_SHAPE
-    tile = dg.tiled_ab(tm, tn, waves, atom)
     for smallint in (False, True):
         A, B = datagen.make_bf16_pair(M, N, K, "smallint" if smallint else "normal",
                                       "smallint" if smallint else "normal", config=9)

@@ -56,22 +56,13 @@ def test_workload_shapes_sampled(name, smallint):
         check_close("fp8", got[None, :], vals[None, :], absv[None, :], K, scale=sa * sb, what=name)
 
 
-@pytest.mark.parametrize("tm,tn,waves,atom", dg.TILED_LADDER)
-def test_every_tiled_tile(tm, tn, waves, atom):
+@pytest.mark.parametrize("tile", dg.ladder_tiles("fp8"), ids=lambda t: t.name)
+def test_every_ladder_tile(tile):
     M, N, K = 263, 270, 192
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=19, smallint=True)
-    C, ok = run("fp8", A, B, tile=dg.tiled(tm, tn, waves, atom), sa=0.5, sb=4.0)
+    C, ok = run("fp8", A, B, tile=tile, sa=0.5, sb=4.0)
     assert ok
-    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"tiled{tm}x{tn}w{waves}a{atom}")
-
-
-@pytest.mark.parametrize("tm,tn,waves,atom", dg.AB_LADDER)
-def test_every_ab_tile(tm, tn, waves, atom):
-    M, N, K = 263, 270, 192
-    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=19, smallint=True)
-    C, ok = run("fp8", A, B, tile=dg.tiled_ab(tm, tn, waves, atom), sa=0.5, sb=4.0)
-    assert ok
-    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), f"ab{tm}x{tn}w{waves}a{atom}")
+    check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), tile.name)
 
 
 @pytest.mark.parametrize("tm,tn", dg.SKINNY_LADDER)
