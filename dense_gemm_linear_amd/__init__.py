@@ -72,7 +72,7 @@ class Tile:
                 atom + pipe
         if self.kernel == GEMM_KERNEL_TILED_AB:
             return f"ab{self.tile_m}x{self.tile_n}w{self.waves}" + atom + pipe
-        return f"skinny{self.tile_m}x{self.tile_n}"
+        return f"skinny{self.tile_m}x{self.tile_n}" + ("" if self.k_split in (0, 4) else f"w{self.k_split}")
 
     def to_c(self) -> GemmTile:
         return GemmTile(self.kernel, self.tile_m, self.tile_n, self.tile_k, self.atom, self.waves,
@@ -95,8 +95,9 @@ def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, 
                 lds_stages=stages)
 
 
-def skinny(tm: int, tn: int) -> Tile:
-    return Tile(GEMM_KERNEL_SKINNY, tm, tn, k_split=4, lds_stages=0)
+def skinny(tm: int, tn: int, waves: int = 4) -> Tile:
+    """A rung of the skinny ladder; `waves` split K inside one workgroup."""
+    return Tile(GEMM_KERNEL_SKINNY, tm, tn, waves=waves, k_split=waves, lds_stages=0)
 
 
 # The ladders of include/densegemm.h, as (tile_m, tile_n, waves, stages, atom,
@@ -113,7 +114,9 @@ AB_LADDER = [(256, 128, 4, 3, 16, 128), (128, 256, 4, 3, 16, 128), (128, 128, 4,
              (256, 128, 4, 3, 32, 128), (128, 256, 4, 3, 32, 128), (128, 128, 4, 3, 32, 128),
              (256, 256, 8, 4, 32, 64), (256, 256, 8, 5, 32, 64), (256, 256, 4, 4, 32, 64),
              (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64)]
-SKINNY_LADDER = [(m, n) for m in (16, 32, 48, 64) for n in (16, 32, 64)]
+# (tile_m, tile_n, waves splitting K)
+SKINNY_LADDER = [(m, n, 4) for m in (16, 32, 48, 64) for n in (16, 32, 64)] + \
+    [(16, 16, 8), (16, 32, 8), (32, 16, 8), (32, 32, 8), (16, 16, 16), (32, 16, 16)]
 
 
 def ladder_tiles(dtype="bf16"):
@@ -127,7 +130,7 @@ def all_tiles(M: int, dtype="bf16"):
     """Every rung usable for a GEMM with M rows."""
     t = ladder_tiles(dtype)
     if M <= 64:
-        t += [skinny(m, n) for m, n in SKINNY_LADDER if M <= m < M + 16]
+        t += [skinny(m, n, w) for m, n, w in SKINNY_LADDER if M <= m < M + 16]
     return t
 
 

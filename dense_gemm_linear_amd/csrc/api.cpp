@@ -71,7 +71,9 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
     else if (t.kernel == GEMM_KERNEL_TILED_AB)
         *idx = ab_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
     else if (t.kernel == GEMM_KERNEL_SKINNY)
-        *idx = skinny_supported(t.tile_m, t.tile_n) && M <= t.tile_m ? 0 : -1;
+        *idx = skinny_supported(t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split) && M <= t.tile_m
+                   ? 0
+                   : -1;
     return *idx >= 0;
 }
 
@@ -139,7 +141,7 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     a.c_vec = (((uintptr_t)C & 15u) == 0) && (ldc % 8 == 0);
     hipError_t err;
     if (t.kernel == GEMM_KERNEL_SKINNY) {
-        err = launch_skinny(dt, t.tile_m, t.tile_n, a, s);
+        err = launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
     } else {
         a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
         a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);

@@ -57,13 +57,25 @@ constexpr TiledRung kTiledLadder[] = {
 // A rung matches a request when every field agrees; a requested stage count
 // or k-tile size of 0 matches any (the first such rung in ladder order).
 #define DG_MATCH(ST_, KTB_) ((st == 0 || st == (ST_)) && (ktb == 0 || ktb == (KTB_)))
-constexpr int kSkinnyTM[] = {16, 32, 48, 64};
-constexpr int kSkinnyTN[] = {16, 32, 64};
+// Skinny ladder: (tile_m, tile_n, waves splitting K).
+#define DG_SKINNY_LADDER(X)                                                   \
+    X(16, 16, 4) X(16, 32, 4) X(16, 64, 4) X(32, 16, 4) X(32, 32, 4) X(32, 64, 4) \
+    X(48, 16, 4) X(48, 32, 4) X(48, 64, 4) X(64, 16, 4) X(64, 32, 4) X(64, 64, 4) \
+    X(16, 16, 8) X(16, 32, 8) X(32, 16, 8) X(32, 32, 8) X(16, 16, 16) X(32, 16, 16)
+
+struct SkinnyRung {
+    int tm, tn, waves;
+};
+constexpr SkinnyRung kSkinnyLadder[] = {
+#define DG_SR(M_, N_, W_) {M_, N_, W_},
+    DG_SKINNY_LADDER(DG_SR)
+#undef DG_SR
+};
 
 // Index of the ladder rung a request names, or -1 (st, ktb: 0 = any).
 int tiled_rung(int tm, int tn, int waves, int atom, int st, int ktb);
 int ab_rung(int tm, int tn, int waves, int atom, int st, int ktb);
-bool skinny_supported(int tm, int tn);
+bool skinny_supported(int tm, int tn, int waves);
 
 // Launchers: return hipSuccess or the launch error.  Grids are computed from
 // the arguments; shapes are validated by the caller.
@@ -74,7 +86,7 @@ hipError_t launch_tiled_fp8(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab_bf16(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab_fp8(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_skinny(int dt, int tm, int tn, const GemmArgs& a, hipStream_t s);
+hipError_t launch_skinny(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
 hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
                             int64_t KB, int aligned, hipStream_t s);

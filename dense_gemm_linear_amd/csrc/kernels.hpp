@@ -766,12 +766,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         scale_a, scale_b);
 }
 
-// Skinny kernel: NB 16-column blocks per workgroup, MR 16-row blocks cover M.
-template <int DT, int MR, int NB>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
+// Skinny kernel (small M: decode and short prefill): one workgroup per NB
+// 16-column blocks of B covering all M rows (MR 16-row MFMA blocks).  Its W
+// waves split K; each streams its K range of the preshuffled B once, with two
+// batches of U k-tiles of loads in flight (the next batch is issued before
+// the current one is consumed, so the HBM latency is paid once per wave, not
+// once per batch), and reads A straight from global (small; it stays in L2).
+// Partial sums are reduced in LDS in a fixed order: deterministic, no
+// workspace.
+template <int DT, int MR, int NB, int W>
+__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs p)
 {
-    constexpr int U = 4;   // k-tiles in flight per wave
-    __shared__ f32x4 red[4][MR * NB][64];
+    constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);   // k-tiles per batch
+    __shared__ f32x4 red[W][MR * NB][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -783,7 +790,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
                                 (uint32_t)nbv * (uint32_t)p.KB * 1024u);
     const rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)(p.M - 1) * p.lda_b + p.KA_b));
 
-    const int per = (p.nkt + 3) >> 2;
+    const int per = (p.nkt + W - 1) / W;
     const int kt0 = wave * per;
     const int kt1 = min(p.nkt, kt0 + per);
 
@@ -794,8 +801,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
         for (int j = 0; j < NB; ++j)
             acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kt = kt0; kt < kt1; kt += U) {
-        i32x4 bv[U][NB][2], av[U][MR][2];
+    i32x4 bv[2][U][NB][2], av[2][U][MR][2];
+    // k-tiles at or past kt1 (and the K tail) load through out-of-range
+    // offsets: zeros, no memory traffic.
+    auto load = [&](int set, int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = kt + u;
@@ -808,7 +817,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
                     uint32_t off = (uint32_t)(j * p.KB + kb) * 1024u + lane * 16;
                     if (!kv || kb >= p.KB)
                         off = kOOB;
-                    bv[u][j][c] = load16(rb, off);
+                    bv[set][u][j][c] = load16(rb, off);
                 }
 #pragma unroll
             for (int mi = 0; mi < MR; ++mi)
@@ -818,9 +827,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
                     uint32_t off = (uint32_t)(mi * 16 + r16) * (uint32_t)p.lda_b + (uint32_t)byte;
                     if (!kv || byte >= p.KA_b)
                         off = kOOB;
-                    av[u][mi][h] = load16(ra, off);
+                    av[set][u][mi][h] = load16(ra, off);
                 }
         }
+    };
+    auto comp = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (DT == DT_BF16) {
@@ -830,15 +841,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
                     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
                         for (int j = 0; j < NB; ++j)
-                            acc[mi][j] = mfma_bf16(av[u][mi][s], bv[u][j][s], acc[mi][j]);
+                            acc[mi][j] = mfma_bf16(av[set][u][mi][s], bv[set][u][j][s], acc[mi][j]);
             } else {
 #pragma unroll
                 for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
-                        acc[mi][j] = mfma_fp8(cat(av[u][mi][0], av[u][mi][1]),
-                                              cat(bv[u][j][0], bv[u][j][1]), acc[mi][j]);
+                        acc[mi][j] = mfma_fp8(cat(av[set][u][mi][0], av[set][u][mi][1]),
+                                              cat(bv[set][u][j][0], bv[set][u][j][1]), acc[mi][j]);
             }
+        }
+    };
+    if (kt0 < kt1) {
+        load(0, kt0);
+        for (int kt = kt0; kt < kt1; kt += 2 * U) {
+            load(1, kt + U);
+            comp(0);
+            if (kt + 2 * U < kt1)
+                load(0, kt + 2 * U);
+            comp(1);
         }
     }
 
@@ -854,11 +875,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    for (int a = wave; a < MR * NB; a += 4) {
+    for (int a = wave; a < MR * NB; a += W) {
         f32x4 s = red[0][a][lane];
-        s = s + red[1][a][lane];
-        s = s + red[2][a][lane];
-        s = s + red[3][a][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            s = s + red[w][a][lane];
         const int mi = a / NB, j = a % NB;
         const int col = (nb0 + j) * 16 + r16;
         if (col < p.N) {

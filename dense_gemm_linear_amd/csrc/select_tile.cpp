@@ -150,9 +150,10 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
     return true;
 }
 
-bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int tn, const Chip& c,
-                  Cand& out)
+bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, const SkinnyRung& r,
+                  const Chip& c, Cand& out)
 {
+    const int tm = r.tm, tn = r.tn;
     if (M > tm || tm - M >= 16)
         return false;  // the smallest 16-row multiple that covers M
     const int e = dt == GEMM_BF16 ? 2 : 1;
@@ -166,7 +167,8 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, int tm, int 
     const int64_t per_cu = cdiv(nwg, cus);
     const double cu_bytes = per_cu * ((double)nb * 16 * K * e + (double)tm * K * e);
     us = std::max(us, cu_bytes / (c.cu_stream_bytes_per_clk * c.clock_hz) * 1e6) + 3.0;
-    fill_common(out.t, GEMM_KERNEL_SKINNY, tm, tn, dt);
+    fill_common(out.t, GEMM_KERNEL_SKINNY, tm, tn, dt, r.waves);
+    out.t.k_split = r.waves;
     const double te = (double)M * N / ((double)tm * (double)nwg * tn);
     out.t.tile_eff = (float)te;
     const int64_t rounds = cdiv(nwg, cus);
@@ -211,12 +213,11 @@ int ab_rung(int tm, int tn, int waves, int atom, int st, int ktb)
     return -1;
 }
 
-bool skinny_supported(int tm, int tn)
+bool skinny_supported(int tm, int tn, int waves)
 {
-    for (int m : kSkinnyTM)
-        for (int n : kSkinnyTN)
-            if (m == tm && n == tn)
-                return true;
+    for (const SkinnyRung& r : kSkinnyLadder)
+        if (r.tm == tm && r.tn == tn && r.waves == waves)
+            return true;
     return false;
 }
 
@@ -235,12 +236,11 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
         }
     };
     if (M <= 64) {
-        for (int tm : kSkinnyTM)
-            for (int tn : kSkinnyTN) {
-                Cand cd;
-                if (price_skinny(M, N, K, dt, cus, tm, tn, chip, cd))
-                    consider(cd);
-            }
+        for (const SkinnyRung& r : kSkinnyLadder) {
+            Cand cd;
+            if (price_skinny(M, N, K, dt, cus, r, chip, cd))
+                consider(cd);
+        }
     }
     int idx = 0;
     for (const TiledRung& r : kTiledLadder) {

@@ -85,7 +85,9 @@ typedef enum {
  *   16 x 16 e4m3 atoms need 128-byte k-tiles.
  *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering
  *     M), tile_n in {16, 32, 64} (16-column blocks per workgroup), k_split
- *     = waves that split K in one workgroup (4).
+ *     = waves that split K in one workgroup: 4 for every (tile_m, tile_n),
+ *     8 for tile_m, tile_n in {16, 32}, 16 for tile_m in {16, 32} with
+ *     tile_n 16; k_split 0 means 4.
  */
 typedef struct {
     int32_t kernel;      /* gemm_kernel */
@@ -94,7 +96,7 @@ typedef struct {
     int32_t tile_k;      /* elements of K per pipeline stage (k-tile); 0 = any */
     int32_t atom;        /* MFMA block edge: 16 or 32 (0 = 16) */
     int32_t waves;       /* waves per workgroup */
-    int32_t k_split;     /* skinny: waves splitting K (informational) */
+    int32_t k_split;     /* skinny: waves splitting K (0 = 4) */
     int32_t lds_stages;  /* k-tiles in the LDS ring (2 = ping-pong); 0 = any */
     float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */
     float wq_eff;        /* tiles / (ceil(tiles / CUs) * CUs) */

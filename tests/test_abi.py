@@ -71,7 +71,7 @@ def test_select_tile_metrics_match_oracle(M, N, K, dt):
         # padding screen: padded output at most 1.25x the real one when any tile passes
         assert 1.0 / t.tile_eff <= 1.25 + 1e-6
     else:
-        assert (t.tile_m, t.tile_n) in dg.SKINNY_LADDER
+        assert (t.tile_m, t.tile_n, t.k_split) in dg.SKINNY_LADDER
         assert M <= t.tile_m < M + 16
     assert t.predicted_us > 0
     assert dg.select_tile(M, N, K, dt, num_cus=256) == t       # deterministic
@@ -83,9 +83,10 @@ def test_every_python_rung_is_a_library_rung(dt):
     assert len({t.name for t in tiles}) == len(tiles)            # no duplicates
     for t in tiles:
         assert dg.tile_check(t, 1000, dt) == dg.GEMM_OK, t.name
-    for tm, tn in dg.SKINNY_LADDER:
-        assert dg.tile_check(dg.skinny(tm, tn), tm, dt) == dg.GEMM_OK
-        assert dg.tile_check(dg.skinny(tm, tn), tm + 1, dt) == dg.GEMM_ERR_UNSUPPORTED
+    for tm, tn, w in dg.SKINNY_LADDER:
+        assert dg.tile_check(dg.skinny(tm, tn, w), tm, dt) == dg.GEMM_OK
+        assert dg.tile_check(dg.skinny(tm, tn, w), tm + 1, dt) == dg.GEMM_ERR_UNSUPPORTED
+    assert dg.tile_check(dg.skinny(64, 64, 8), 64, dt) == dg.GEMM_ERR_UNSUPPORTED
     # wildcards: stages / tile_k 0 pick the first matching rung
     assert dg.tile_check(dg.tiled(128, 128), 100, dt) == dg.GEMM_OK
     assert dg.tile_check(dg.tiled_ab(256, 256, 8, 32), 100, dt) == dg.GEMM_OK

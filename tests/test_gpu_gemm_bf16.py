@@ -108,16 +108,16 @@ def test_every_ladder_tile(tile):
                         K, what=tile.name)
 
 
-@pytest.mark.parametrize("tm,tn", dg.SKINNY_LADDER)
+@pytest.mark.parametrize("tm,tn,w", dg.SKINNY_LADDER)
 @pytest.mark.parametrize("M", [1, 13, 16, 17, 31, 47, 48, 64])
-def test_every_skinny_tile(tm, tn, M):
+def test_every_skinny_tile(tm, tn, w, M):
     if M > tm:
         pytest.skip("tile rows do not cover M")
     N, K = 270, 176
     A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=10 + M)
-    C, ok = run("bf16", A, B, tile=dg.skinny(tm, tn))
+    C, ok = run("bf16", A, B, tile=dg.skinny(tm, tn, w))
     assert ok
-    check_exact(C, oracle_full("bf16", A, B), f"skinny{tm}x{tn} M={M}")
+    check_exact(C, oracle_full("bf16", A, B), f"skinny{tm}x{tn}w{w} M={M}")
 
 
 @pytest.mark.parametrize("K", [16, 48, 80, 144, 64, 128])

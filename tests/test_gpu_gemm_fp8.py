@@ -65,13 +65,13 @@ def test_every_ladder_tile(tile):
     check_exact(C, oracle_full("fp8", A, B, 0.5, 4.0), tile.name)
 
 
-@pytest.mark.parametrize("tm,tn", dg.SKINNY_LADDER)
-def test_every_skinny_tile(tm, tn):
+@pytest.mark.parametrize("tm,tn,w", dg.SKINNY_LADDER)
+def test_every_skinny_tile(tm, tn, w):
     M, N, K = tm - 3, 270, 320
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=20 + tm, smallint=True)
-    C, ok = run("fp8", A, B, tile=dg.skinny(tm, tn))
+    C, ok = run("fp8", A, B, tile=dg.skinny(tm, tn, w))
     assert ok
-    check_exact(C, oracle_full("fp8", A, B), f"skinny{tm}x{tn}")
+    check_exact(C, oracle_full("fp8", A, B), f"skinny{tm}x{tn}w{w}")
 
 
 @pytest.mark.parametrize("K", [64, 192, 320])
