@@ -35,6 +35,35 @@ import time
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+# The device code whose hash identifies "the kernel" a traffic measurement
+# belongs to: a measurement taken on other sources is not reported.
+KERNEL_SOURCES = ["device.hpp", "kernels.hpp", "tiled.inc", "tiled_bf16.hip", "tiled_fp8.hip",
+                  "skinny.hip"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_gemm_linear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, tile_name: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this workload
+    (profiles/traffic_<workload>.json, written by --traffic-summary), or None
+    if absent or taken on another rung or other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("tile") != tile_name or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
 
 
 def flops(M: int, N: int, K: int) -> float:
@@ -337,6 +366,11 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                           "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of the "
+                         "workload's GEMM, then of --copy-calibration 256) into "
+                         "profiles/traffic_<workload>.json for --workload/--tile, and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
@@ -351,6 +385,8 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.traffic_summary:
+        return traffic_summary(args.workload, args.tile, *args.traffic_summary)
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
@@ -387,11 +423,18 @@ def main(argv=None):
                    "operand_copies_rotated": r["copies"], "pct_of_mfma_peak": None},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_r,
                      "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes": alg_bytes(M, N, K, dt),
                      "kernel_us_avg": round(kern_avg, 3), "kernel_us_median": round(kern[len(kern) // 2], 3)},
         "shuffle_b_us": round(r["shuffle_us"], 2),
     }
     if bound == "mfma":
         out["config"]["pct_of_mfma_peak"] = round(100 * value / PEAK_TFLOPS[dt], 2)
+    tr = load_traffic(name, tile.name)
+    if tr:
+        out["roofline"]["traffic"] = tr["hbm_bytes_per_launch"]
+        out["roofline"]["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes",
+                                                                 "fetch_factor", "write_factor",
+                                                                 "source")}
     clk = r["clock"]
     out["clock_under_load"] = clk
     if clk and clk.get("gfx_mhz") and bound == "mfma" and min(clk["gfx_mhz"]) > 0:
@@ -456,6 +499,50 @@ def copy_calibration(mib: int) -> int:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+    return 0
+
+
+def _pmc_mean(folder: str, counter: str, kernel_substr: str) -> float:
+    """Mean per-dispatch value (KiB for FETCH_SIZE / WRITE_SIZE) of `counter`
+    over the dispatches of kernels whose name contains `kernel_substr`."""
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{kernel_substr}' under {folder}")
+    return sum(vals) / len(vals)
+
+
+def traffic_summary(name: str, tile_spec, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> int:
+    """HBM traffic of the GEMM kernel per launch: its FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by bytes / counter of a plain device copy
+    of 256 MiB measured the same way."""
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    tile = parse_tile(tile_spec) if tile_spec else dg.select_tile(M, N, K, dt, num_cus=256)
+    copy_bytes = 256 * 2 ** 20
+    cf = _pmc_mean(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw = _pmc_mean(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    kern = "gemm_"
+    gf = _pmc_mean(fetch_dir, "FETCH_SIZE", kern)
+    gw = _pmc_mean(write_dir, "WRITE_SIZE", kern)
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    t = {"workload": name, "tile": tile.name, "kernel_source_hash": kernel_source_hash(),
+         "fetch_bytes": round(gf * 1024 * ff), "write_bytes": round(gw * 1024 * wf),
+         "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+         "algorithmic_bytes": alg_bytes(M, N, K, dt),
+         "source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM kernel, "
+                   "scaled by a 256 MiB device copy's bytes / counter"}
+    t["hbm_bytes_per_launch"] = t["fetch_bytes"] + t["write_bytes"]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"traffic_{name}.json"), "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t), flush=True)
     return 0
 
 

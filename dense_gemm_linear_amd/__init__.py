@@ -112,7 +112,7 @@ TILED_LADDER = [(256, 128, 8, 2, 16, 128), (128, 256, 8, 2, 16, 128), (128, 128,
 AB_LADDER = [(256, 128, 4, 3, 16, 128), (128, 256, 4, 3, 16, 128), (128, 128, 4, 3, 16, 128),
              (256, 256, 8, 2, 32, 128), (256, 256, 4, 2, 32, 128), (256, 128, 8, 3, 32, 128),
              (256, 128, 4, 3, 32, 128), (128, 256, 4, 3, 32, 128), (128, 128, 4, 3, 32, 128),
-             (256, 256, 8, 4, 32, 64), (256, 256, 8, 5, 32, 64), (256, 256, 4, 4, 32, 64),
+             (256, 256, 8, 4, 32, 64), (256, 256, 4, 4, 32, 64),
              (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64)]
 # (tile_m, tile_n, waves splitting K)
 SKINNY_LADDER = [(m, n, 4) for m in (16, 32, 48, 64) for n in (16, 32, 64)] + \

@@ -33,7 +33,7 @@ namespace dg {
     X(256, 256, 2, 4, 2, 32, 128) X(256, 256, 2, 2, 2, 32, 128)                            \
     X(256, 128, 2, 4, 3, 32, 128) X(256, 128, 2, 2, 3, 32, 128)                            \
     X(128, 256, 2, 2, 3, 32, 128) X(128, 128, 2, 2, 3, 32, 128)                            \
-    X(256, 256, 2, 4, 4, 32, 64) X(256, 256, 2, 4, 5, 32, 64) X(256, 256, 2, 2, 4, 32, 64)  \
+    X(256, 256, 2, 4, 4, 32, 64) X(256, 256, 2, 2, 4, 32, 64)                            \
     X(256, 128, 2, 4, 6, 32, 64) X(128, 256, 2, 2, 6, 32, 64)
 
 struct ABRung {

@@ -385,18 +385,18 @@ constexpr int frag_sets(int st, int steps)
     return n;
 }
 
-// Runs f(kt + i, integral_constant<i>) for i in I... (one trip of the
-// steady-state loop: ST phases with compile-time stage indices), and the
+// Runs f(kt + i, integral_constant<i>, tail) for i in I...: one trip of the
+// steady-state loop (ST phases with compile-time stage indices), and the
 // tail variant only while kt + i < nkt.
 template <class F, int... I>
 __device__ __forceinline__ void run_phases(F& f, int kt, std::integer_sequence<int, I...>)
 {
-    (f(kt + I, std::integral_constant<int, I>{}), ...);
+    (f(kt + I, std::integral_constant<int, I>{}, std::false_type{}), ...);
 }
 template <class F, int... I>
 __device__ __forceinline__ void run_tail(F& f, int kt, int nkt, std::integer_sequence<int, I...>)
 {
-    ((kt + I < nkt ? f(kt + I, std::integral_constant<int, I>{}) : void()), ...);
+    ((kt + I < nkt ? f(kt + I, std::integral_constant<int, I>{}, std::true_type{}) : void()), ...);
 }
 
 // The K loop shared by both tiled kernels.  Phase t multiplies k-tile t out
@@ -407,6 +407,12 @@ __device__ __forceinline__ void run_tail(F& f, int kt, int nkt, std::integer_seq
 // read from LDS while those MFMAs run, so no LDS latency is exposed at the
 // k-tile boundary.  Fragment registers alternate between two sets along the
 // global sequence of K steps, NS = frag_sets(ST, STEPS) of them.
+//
+// The last nkt % ST phases (the tail) would only load k-tiles past K: they
+// issue no loads and wait for every load in flight.  (Their register loads
+// would be dead code the compiler removes, and the steady-state wait counts
+// assume every phase issues exactly LOADS loads: with loads removed, a count
+// of in-flight loads no longer proves the next k-tile has landed.)
 //   load(kt, stage, part)      issue part `part` (of STEPS) of the loads of
 //                              k-tile kt (zeros past K)
 //   read(stage, step, set)     LDS -> fragment registers
@@ -429,24 +435,30 @@ __device__ __forceinline__ void k_loop(int nkt, Load& load, Read& read, Mma& mma
             load(t, t, part);
     DG_STAGE_BARRIER((ST - 2) * LOADS);
     read(0, 0, 0);
-    auto phase = [&](int t, auto sc) __attribute__((always_inline)) {
+    auto phase = [&](int t, auto sc, auto tail) __attribute__((always_inline)) {
         constexpr int si = decltype(sc)::value;
+        constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const int cur = (si * STEPS + st) % NS;
             const int nxt = (si * STEPS + st + 1) % NS;
-            if (SPREAD) {
-                load(t + ST - 1, (si + ST - 1) % ST, st);
-            } else if (st == 0) {
+            if constexpr (!TAIL) {
+                if (SPREAD) {
+                    load(t + ST - 1, (si + ST - 1) % ST, st);
+                } else if (st == 0) {
 #pragma unroll
-                for (int part = 0; part < STEPS; ++part)
-                    load(t + ST - 1, (si + ST - 1) % ST, part);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int part = 0; part < STEPS; ++part)
+                        load(t + ST - 1, (si + ST - 1) % ST, part);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             if (st + 1 < STEPS) {
                 read(si, st + 1, nxt);
             } else {
-                DG_STAGE_BARRIER((ST - 2) * LOADS);
+                if constexpr (TAIL)
+                    DG_STAGE_BARRIER(0);
+                else
+                    DG_STAGE_BARRIER((ST - 2) * LOADS);
                 read((si + 1) % ST, 0, nxt);
             }
             mma(si, st, cur);

@@ -1,6 +1,8 @@
 // select_tile: analytic choice of kernel and tile for an M x N x K GEMM.
 //
-// The model (pure host, deterministic):
+// The model (pure host, deterministic).  Rungs measured on MI355X are priced
+// by their calibrated cost (calibration.inc, fitted by calibrate.py from tile
+// sweeps); the analytic model below prices the rest:
 //   - tile quantization tile_eff = M*N / (M_pad*N_pad) and wave quantization
 //     wq_eff = tiles / (rounds * slots) as the TraceLens GEMM analysis page
 //     defines them ("Tile quantization efficiency", "Wave quantization
@@ -23,6 +25,38 @@
 namespace dg {
 
 namespace {
+
+// Measured per-rung cost constants (calibrate.py): t_us = a * n_cu * K_bytes
+// / 1000 + b * n_cu + c, n_cu = ceil(tiles / CUs).
+struct RungCalib {
+    int dt, kernel, tm, tn, waves, atom, st, ktb;
+    float a, b, c;
+    int points;
+};
+#include "calibration.inc"
+
+const RungCalib* find_calib(int dt, int kernel, int tm, int tn, int waves, int atom, int st,
+                            int ktb)
+{
+    for (const RungCalib& r : kRungCalib)
+        if (r.dt == dt && r.kernel == kernel && r.tm == tm && r.tn == tn && r.waves == waves &&
+            r.atom == atom && r.st == st && r.ktb == ktb)
+            return &r;
+    return nullptr;
+}
+
+// Calibrated time of a tiled / A+B rung, or `fallback` if it was never measured.
+double calibrated_us(int dt, int kernel, int tm, int tn, int waves, int atom, int st, int ktb,
+                     int64_t M, int64_t N, int64_t K, int cus, double fallback)
+{
+    const RungCalib* r = find_calib(dt, kernel, tm, tn, waves, atom, st, ktb);
+    if (!r)
+        return fallback;
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+    const double ncu = (double)((tiles + cus - 1) / cus);
+    return r->a * ncu * (double)K * e / 1000.0 + r->b * ncu + r->c;
+}
 
 struct Chip {
     double clock_hz = 2.4e9;
@@ -98,6 +132,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, cons
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
+    us = calibrated_us(dt, GEMM_KERNEL_TILED, tm, tn, waves, r.atom, r.st, r.ktb, M, N, K, cus, us);
     fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
     const int64_t rounds = cdiv(tiles, cus);
@@ -139,6 +174,8 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
+    us = calibrated_us(dt, GEMM_KERNEL_TILED_AB, r.tm, r.tn, waves, r.atom, r.st, r.ktb, M, N, K,
+                       cus, us);
     fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
     const int64_t rounds = cdiv(tiles, cus);

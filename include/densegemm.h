@@ -79,8 +79,7 @@ typedef enum {
  *     16 x 16, 128-byte k-tiles, 4 waves, 3 stages: 256x128, 128x256, 128x128;
  *     32 x 32, 128-byte k-tiles: 256x256 (8 or 4 waves, 2 stages), 256x128
  *       (8 or 4 waves, 3 stages), 128x256 and 128x128 (4 waves, 3 stages);
- *     32 x 32, 64-byte k-tiles: 256x256 with 8 waves and 4 or 5 stages or 4
- *       waves and 4 stages, 256x128 with 8 waves and 6 stages, 128x256 with
+ *     32 x 32, 64-byte k-tiles: 256x256 with 8 or 4 waves and 4 stages, 256x128 with 8 waves and 6 stages, 128x256 with
  *       4 waves and 6 stages.
  *   16 x 16 e4m3 atoms need 128-byte k-tiles.
  *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering

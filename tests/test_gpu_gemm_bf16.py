@@ -108,6 +108,21 @@ def test_every_ladder_tile(tile):
                         K, what=tile.name)
 
 
+@pytest.mark.parametrize("tile", dg.ladder_tiles("bf16"), ids=lambda t: t.name)
+def test_every_ladder_tile_short_k(tile):
+    """1 to 5 k-tiles: K loops that end inside the prologue or run only the
+    tail phases (fewer k-tiles than pipeline stages).  Each case runs three
+    times: a missing wait shows up as stale LDS data in some runs only."""
+    M, N = 128, 256
+    for K in (64, 128, 192, 256, 320):
+        A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=K + 3)
+        ref = oracle_full("bf16", A, B)
+        for rep in range(3):
+            C, ok = run("bf16", A, B, tile=tile)
+            assert ok, "guard band written"
+            check_exact(C, ref, f"{tile.name} K={K} run {rep}")
+
+
 @pytest.mark.parametrize("tm,tn,w", dg.SKINNY_LADDER)
 @pytest.mark.parametrize("M", [1, 13, 16, 17, 31, 47, 48, 64])
 def test_every_skinny_tile(tm, tn, w, M):
