@@ -197,6 +197,8 @@ def parse_tile(spec: str | None):
         return dg.tiled(tm, tn, waves, atom, stages, tile_k)
     if kind == "ab":
         return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k)
+    if kind == "pp":
+        return dg.tiled_pp(tm, tn, atom, stages, tile_k)
     return dg.skinny(tm, tn)
 
 

@@ -34,6 +34,7 @@ GEMM_FP8_E4M3 = 1
 GEMM_KERNEL_TILED = 0
 GEMM_KERNEL_SKINNY = 1
 GEMM_KERNEL_TILED_AB = 2
+GEMM_KERNEL_TILED_PP = 3
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string")
@@ -72,6 +73,8 @@ class Tile:
                 atom + pipe
         if self.kernel == GEMM_KERNEL_TILED_AB:
             return f"ab{self.tile_m}x{self.tile_n}w{self.waves}" + atom + pipe
+        if self.kernel == GEMM_KERNEL_TILED_PP:
+            return f"pp{self.tile_m}x{self.tile_n}" + atom + pipe
         return f"skinny{self.tile_m}x{self.tile_n}" + ("" if self.k_split in (0, 4) else f"w{self.k_split}")
 
     def to_c(self) -> GemmTile:
@@ -95,6 +98,11 @@ def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, 
                 lds_stages=stages)
 
 
+def tiled_pp(tm: int, tn: int, atom: int = 32, stages: int = 0, tile_k: int = 0) -> Tile:
+    """A rung of the ping-pong A+B ladder (8 waves); stages / tile_k 0 = any."""
+    return Tile(GEMM_KERNEL_TILED_PP, tm, tn, tile_k=tile_k, atom=atom, waves=8, lds_stages=stages)
+
+
 def skinny(tm: int, tn: int, waves: int = 4) -> Tile:
     """A rung of the skinny ladder; `waves` split K inside one workgroup."""
     return Tile(GEMM_KERNEL_SKINNY, tm, tn, waves=waves, k_split=waves, lds_stages=0)
@@ -115,6 +123,8 @@ AB_LADDER = [(256, 128, 4, 3, 16, 128), (128, 256, 4, 3, 16, 128), (128, 128, 4,
              (256, 256, 8, 4, 32, 64), (256, 256, 4, 4, 32, 64),
              (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64)]
 # (tile_m, tile_n, waves splitting K)
+# (tile_m, tile_n, stages, atom, k-tile bytes)
+PP_LADDER = [(256, 256, 4, 32, 64)]
 SKINNY_LADDER = [(m, n, 4) for m in (16, 32, 48, 64) for n in (16, 32, 64)] + \
     [(16, 16, 8), (16, 32, 8), (32, 16, 8), (32, 32, 8), (16, 16, 16), (32, 16, 16)]
 
@@ -123,7 +133,8 @@ def ladder_tiles(dtype="bf16"):
     """Every tiled and A+B rung, fully specified for an element type."""
     e = 2 if _dtype_code(dtype) == GEMM_BF16 else 1
     return [tiled(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in TILED_LADDER] + \
-        [tiled_ab(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in AB_LADDER]
+        [tiled_ab(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in AB_LADDER] + \
+        [tiled_pp(m, n, a, st, kb // e) for m, n, st, a, kb in PP_LADDER]
 
 
 def all_tiles(M: int, dtype="bf16"):

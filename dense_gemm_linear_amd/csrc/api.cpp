@@ -14,6 +14,11 @@ hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s)
     return dt == DT_BF16 ? launch_ab_bf16(idx, a, s) : launch_ab_fp8(idx, a, s);
 }
 
+hipError_t launch_pp(int dt, int idx, const GemmArgs& a, hipStream_t s)
+{
+    return dt == DT_BF16 ? launch_pp_bf16(idx, a, s) : launch_pp_fp8(idx, a, s);
+}
+
 hipError_t launch_tiled(int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
     return dt == DT_BF16 ? launch_tiled_bf16(idx, a, s) : launch_tiled_fp8(idx, a, s);
@@ -70,6 +75,8 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
         *idx = tiled_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
     else if (t.kernel == GEMM_KERNEL_TILED_AB)
         *idx = ab_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
+    else if (t.kernel == GEMM_KERNEL_TILED_PP)
+        *idx = pp_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
     else if (t.kernel == GEMM_KERNEL_SKINNY)
         *idx = skinny_supported(t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split) && M <= t.tile_m
                    ? 0
@@ -145,8 +152,9 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     } else {
         a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
         a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
-        err = t.kernel == GEMM_KERNEL_TILED_AB ? launch_ab(dt, idx, a, s)
-                                               : launch_tiled(dt, idx, a, s);
+        err = t.kernel == GEMM_KERNEL_TILED_AB   ? launch_ab(dt, idx, a, s)
+              : t.kernel == GEMM_KERNEL_TILED_PP ? launch_pp(dt, idx, a, s)
+                                                 : launch_tiled(dt, idx, a, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

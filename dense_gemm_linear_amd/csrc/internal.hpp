@@ -36,6 +36,20 @@ namespace dg {
     X(256, 256, 2, 4, 4, 32, 64) X(256, 256, 2, 2, 4, 32, 64)                            \
     X(256, 128, 2, 4, 6, 32, 64) X(128, 256, 2, 2, 6, 32, 64)
 
+// Ping-pong A+B ladder (8 waves, 2 groups x 4): (tile_m, tile_n, stages, atom,
+// k-tile bytes).  Narrower tiles halve each wave's MFMAs per k-tile while its
+// loads stay the same, and 128-byte k-tiles exceed 256 VGPRs.
+#define DG_PP_LADDER(X) X(256, 256, 4, 32, 64)
+
+struct PPRung {
+    int tm, tn, st, atom, ktb;
+};
+constexpr PPRung kPPLadder[] = {
+#define DG_PPR(M_, N_, ST_, R_, KTB_) {M_, N_, ST_, R_, KTB_},
+    DG_PP_LADDER(DG_PPR)
+#undef DG_PPR
+};
+
 struct ABRung {
     int tm, tn, wm, wn, st, atom, ktb;
 };
@@ -75,6 +89,7 @@ constexpr SkinnyRung kSkinnyLadder[] = {
 // Index of the ladder rung a request names, or -1 (st, ktb: 0 = any).
 int tiled_rung(int tm, int tn, int waves, int atom, int st, int ktb);
 int ab_rung(int tm, int tn, int waves, int atom, int st, int ktb);
+int pp_rung(int tm, int tn, int waves, int atom, int st, int ktb);
 bool skinny_supported(int tm, int tn, int waves);
 
 // Launchers: return hipSuccess or the launch error.  Grids are computed from
@@ -86,6 +101,9 @@ hipError_t launch_tiled_fp8(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab_bf16(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_ab_fp8(int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_pp(int dt, int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_pp_bf16(int idx, const GemmArgs& a, hipStream_t s);
+hipError_t launch_pp_fp8(int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
 hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
@@ -105,6 +123,7 @@ inline hipError_t launch_args(F* kernel, dim3 grid, dim3 block, const GemmArgs& 
 // Resource model of rung `idx` (used by select_tile's feasibility check).
 int tiled_lds_bytes(int idx);
 int ab_lds_bytes(int idx);
+int pp_lds_bytes(int idx);
 int tiled_vgpr_estimate(const TiledRung& r);
 
 }  // namespace dg

@@ -778,6 +778,186 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         scale_a, scale_b);
 }
 
+// ---------------------------------------------------------------------------
+// A+B kernel with ping-pong wave groups ("PP" kernel).
+//
+// 8 waves in two groups of four; a workgroup's waves are spread round robin
+// over the 4 SIMDs, so SIMD i runs wave i of group 0 and wave i of group 1.
+// Group g owns rows [g TM/2, (g+1) TM/2) of the tile; within a group the 4
+// waves split tile_n.  The K loop runs in half-periods separated by
+// workgroup barriers.  In every half one group issues all MFMAs of a k-tile
+// from fragments already in its registers while the other group issues its
+// share of the LDS DMA and reads the fragments of its next k-tile from LDS,
+// so each SIMD's MFMA pipe is fed by one wave while its other wave moves
+// data:
+//   half 2t:     group 0 loads k-tile t, group 1 multiplies k-tile t - 1
+//   half 2t + 1: group 1 loads k-tile t, group 0 multiplies k-tile t
+// Stage t % ST is read in halves 2t and 2t + 1 and refilled, with k-tile
+// t + ST, in half 2t + 2 (group 0's share) and 2t + 3 (group 1's share).
+// Waits at the end of each half: before half 2t both groups' shares of
+// k-tile t must have landed (each wave: at most (ST-2) x LOADS of its loads
+// still in flight); at the end of half 2t only group 1 needs that much (its
+// next read is k-tile t, already complete), group 0 none.
+template <int DT, int TM, int TN, int ST, int R, int KTB>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
+{
+    using S = ABShape<TM, TN, 2, 4, ST, R, KTB>;
+    using KT = KTile<KTB>;
+    using AT = Atom<DT, R>;
+    using acc_t = typename AT::acc_t;
+    constexpr int MR = S::MR, NR = S::NR, A_BUF = S::A_BUF, STAGE = S::STAGE;
+    constexpr int WAVES = 8, A_DMA = S::A_DMA, B_DMA = S::B_DMA, LOADS = S::LOADS;
+    constexpr int P = AT::P, KPK = KT::KPK;
+    constexpr int STEPS = AT::STEPS * KTB / 128;
+    static_assert(STEPS >= 1 && AT::STEPS * KTB % 128 == 0, "atom does not fit the k-tile");
+    static_assert(ST >= 2 && (ST - 1) * LOADS <= 63, "pipeline depth vs vmcnt");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;     // wm = the group
+    const bool g0 = wm == 0;
+    int tm, tn;
+    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+    const int nkt = (p.KB + KPK - 1) / KPK;
+    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
+
+    ADma ad[A_DMA];
+    uint32_t b_goff[B_DMA], b_half[B_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+        ad[i] = a_dma_lane<KTB>(wave + WAVES * i, lane, p.lda_b);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const uint32_t b = wave + WAVES * i;
+        b_goff[i] = ((b / KPK) * (uint32_t)p.KB + (b % KPK)) * 1024u + lane * 16;
+        b_half[i] = b % KPK;
+    }
+    const int lr = lane % R;
+    const uint32_t swz = KT::key((uint32_t)(lane & 15));
+    const uint32_t row0 = (uint32_t)(wm * (TM / 2));
+    const uint32_t b_lds =
+        (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * KPK * 1024 + (lane & 15) * 16);
+
+    i32x4 af[STEPS][MR][P], bf[STEPS][NR][P];
+    acc_t acc[MR][NR];
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[mi][j] = zero_acc<AT>();
+
+    // A k-tile past K loads through out-of-range offsets: zeros, no traffic.
+    auto load = [&](int kt, int stage) __attribute__((always_inline)) {
+        const bool mask = kt >= last_full;
+        uint8_t* base = lds + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
+                off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i) {
+            uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
+            if (mask && kt * KPK + (int)b_half[i] >= p.KB)
+                off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    // all fragments of one k-tile
+    auto read = [&](int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int q = 0; q < P; ++q) {
+                    const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) + b_lds +
+                                         (uint32_t)(j * (R / 16) * KPK * 1024) +
+                                         ((uint32_t)AT::b_half(s, q) << 10) +
+                                         ((uint32_t)AT::b_group(s, lane, q) << 8);
+                    bf[s][j][q] = *reinterpret_cast<const i32x4*>(lds + off);
+                }
+#pragma unroll
+            for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+                for (int q = 0; q < P; ++q) {
+                    const uint32_t row = row0 + (uint32_t)(mi * R + lr);
+                    const uint32_t off = (uint32_t)(stage * STAGE) + row * KTB +
+                                         (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+                    af[s][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
+                }
+        }
+    };
+    auto mma = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+            for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    acc[mi][j] = AT::mma(af[s][mi], bf[s][j], acc[mi][j]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+#pragma unroll
+    for (int t = 0; t < ST - 1; ++t)
+        load(t, t);
+    DG_STAGE_BARRIER((ST - 2) * LOADS);
+    int stage = 0;           // = t % ST
+    int pre = ST - 1;        // = (t + ST - 1) % ST
+    for (int t = 0; t < nkt; ++t) {
+        // half 2t
+        if (g0) {
+            load(t + ST - 1, pre);
+            read(stage);
+            DG_STAGE_BARRIER((ST - 1) * LOADS);
+        } else {
+            if (t > 0)
+                mma();
+            DG_STAGE_BARRIER((ST - 2) * LOADS);
+        }
+        // half 2t + 1
+        if (!g0) {
+            load(t + ST - 1, pre);
+            read(stage);
+        } else {
+            mma();
+        }
+        DG_STAGE_BARRIER((ST - 2) * LOADS);
+        stage = stage + 1 == ST ? 0 : stage + 1;
+        pre = pre + 1 == ST ? 0 : pre + 1;
+    }
+    if (!g0)
+        mma();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+
+    float scale_a = 1.f, scale_b = 1.f;
+    if constexpr (DT == DT_FP8) {
+        scale_a = *p.sa;
+        scale_b = *p.sb;
+    }
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+        p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
+        scale_a, scale_b);
+}
+
 // Skinny kernel (small M: decode and short prefill): one workgroup per NB
 // 16-column blocks of B covering all M rows (MR 16-row MFMA blocks).  Its W
 // waves split K; each streams its K range of the preshuffled B once, with two

@@ -75,6 +75,16 @@ int ab_lds_bytes(int idx)
     return -1;
 }
 
+int pp_lds_bytes(int idx)
+{
+    int i = 0;
+#define DG_CASE(M_, N_, ST_, R_, KTB_) \
+    if (idx == i++) return ABShape<M_, N_, 2, 4, ST_, R_, KTB_>::LDS;
+    DG_PP_LADDER(DG_CASE)
+#undef DG_CASE
+    return -1;
+}
+
 int tiled_lds_bytes(int idx)
 {
     int i = 0;

@@ -187,6 +187,41 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
     return true;
 }
 
+// Ping-pong rungs: the A+B model with the 2 x 4 wave grid, unless calibrated.
+bool price_pp(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const PPRung& r,
+              const Chip& c, Cand& out)
+{
+    const int lds = pp_lds_bytes(idx);
+    if (lds < 0 || lds > c.lds_per_cu)
+        return false;
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    const int64_t nkt = cdiv(K * e, r.ktb);
+    const int64_t tiles_m = cdiv(M, r.tm), tiles_n = cdiv(N, r.tn);
+    const int64_t tiles = tiles_m * tiles_n;
+    const double mfma = 2.0 * r.tm * r.tn * ((double)r.ktb / e) / (c.mfma_flop_per_clk_cu[dt] * 0.98);
+    const double vmem = (double)(r.tm + r.tn) * r.ktb / c.vmem_bytes_per_clk;
+    const double per_kt = std::max(mfma, vmem) * 1.25;
+    const double tile_cyc = nkt * per_kt + (double)r.tm * r.tn * 2 / c.vmem_bytes_per_clk + 1400.0;
+    const int64_t per_cu = cdiv(tiles, cus);
+    double us = per_cu * tile_cyc / c.clock_hz * 1e6;
+    const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
+    us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
+    // An uncalibrated ping-pong rung is only ever run when forced.
+    if (!find_calib(dt, GEMM_KERNEL_TILED_PP, r.tm, r.tn, 8, r.atom, r.st, r.ktb))
+        return false;
+    us = calibrated_us(dt, GEMM_KERNEL_TILED_PP, r.tm, r.tn, 8, r.atom, r.st, r.ktb, M, N, K, cus,
+                       us);
+    fill_common(out.t, GEMM_KERNEL_TILED_PP, r.tm, r.tn, dt, 8, r.atom, r.st, r.ktb);
+    const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
+    const int64_t rounds = cdiv(tiles, cus);
+    out.t.tile_eff = (float)te;
+    out.t.wq_eff = (float)((double)tiles / ((double)rounds * cus));
+    out.t.predicted_us = (float)us;
+    out.us = us;
+    out.screened = 1.0 / te > 1.25;
+    return true;
+}
+
 bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, const SkinnyRung& r,
                   const Chip& c, Cand& out)
 {
@@ -232,6 +267,19 @@ int tiled_rung(int tm, int tn, int waves, int atom, int st, int ktb)
     int i = 0;
     for (const TiledRung& r : kTiledLadder) {
         if (r.tm == tm && r.tn == tn && r.waves == waves && r.atom == atom && DG_MATCH(r.st, r.ktb))
+            return i;
+        ++i;
+    }
+    return -1;
+}
+
+int pp_rung(int tm, int tn, int waves, int atom, int st, int ktb)
+{
+    if (waves != 0 && waves != 8)
+        return -1;
+    int i = 0;
+    for (const PPRung& r : kPPLadder) {
+        if (r.tm == tm && r.tn == tn && r.atom == atom && DG_MATCH(r.st, r.ktb))
             return i;
         ++i;
     }
@@ -289,6 +337,12 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
     for (const ABRung& r : kABLadder) {
         Cand cd;
         if (price_ab(M, N, K, dt, cus, idx++, r, chip, cd))
+            consider(cd);
+    }
+    idx = 0;
+    for (const PPRung& r : kPPLadder) {
+        Cand cd;
+        if (price_pp(M, N, K, dt, cus, idx++, r, chip, cd))
             consider(cd);
     }
     *out = have ? best.t : best_screened.t;

@@ -51,7 +51,9 @@ typedef enum {
 typedef enum {
     GEMM_KERNEL_TILED = 0,    /* block tiles, A pipelined through LDS, B straight to VGPRs */
     GEMM_KERNEL_SKINNY = 1,   /* M <= 64: B streamed once, waves split K, LDS reduction    */
-    GEMM_KERNEL_TILED_AB = 2  /* block tiles, A and B both pipelined through LDS           */
+    GEMM_KERNEL_TILED_AB = 2, /* block tiles, A and B both pipelined through LDS           */
+    GEMM_KERNEL_TILED_PP = 3  /* A+B in LDS, 8 waves in two groups taking turns: one group  */
+                              /* multiplies while the other moves the next k-tile           */
 } gemm_kernel;
 
 /*
@@ -81,6 +83,8 @@ typedef enum {
  *       (8 or 4 waves, 3 stages), 128x256 and 128x128 (4 waves, 3 stages);
  *     32 x 32, 64-byte k-tiles: 256x256 with 8 or 4 waves and 4 stages, 256x128 with 8 waves and 6 stages, 128x256 with
  *       4 waves and 6 stages.
+ *   tiled_pp (8 waves; group g owns tile rows [g tile_m/2, (g+1) tile_m/2)):
+ *     32 x 32: 256x256 with 4 stages of 64-byte k-tiles.
  *   16 x 16 e4m3 atoms need 128-byte k-tiles.
  *   skinny: tile_m in {16, 32, 48, 64} (rows of 16-row MFMA blocks covering
  *     M), tile_n in {16, 32, 64} (16-column blocks per workgroup), k_split

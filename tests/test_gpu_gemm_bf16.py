@@ -139,10 +139,11 @@ def test_every_skinny_tile(tm, tn, w, M):
 @pytest.mark.parametrize("tile", [None, dg.tiled(64, 64), dg.tiled(256, 128), dg.tiled(256, 128, 8),
                                   dg.tiled_ab(256, 128, 4), dg.tiled_ab(128, 128, 4), dg.skinny(32, 16),
                                   dg.tiled(128, 128, 4, 32), dg.tiled(256, 256, 8, 32),
-                                  dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 128, 4, 32)],
+                                  dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 128, 4, 32),
+                                  dg.tiled_pp(256, 256)],
                          ids=["auto", "t64x64", "t256x128", "t256x128w8", "ab256x128", "ab128x128",
                               "s32x16", "t128x128a32", "t256x256w8a32", "ab256x256w8a32",
-                              "ab128x128a32"])
+                              "ab128x128a32", "pp256x256"])
 def test_k_tails(K, tile):
     M, N = 30, 100
     A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=K)

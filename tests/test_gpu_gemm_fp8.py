@@ -93,8 +93,8 @@ def test_k_tails(K):
     M, N = 40, 90
     A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=K, smallint=True)
     for tile in (None, dg.tiled(64, 64), dg.tiled(128, 256), dg.tiled(256, 128, 8),
-                 dg.tiled_ab(256, 128, 4), dg.tiled_ab(256, 128, 4), dg.skinny(48, 32),
-                 dg.tiled(128, 128, 4, 32), dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 256, 4, 32)):
+                 dg.tiled_ab(256, 128, 4), dg.skinny(48, 32), dg.tiled(128, 128, 4, 32),
+                 dg.tiled_ab(256, 256, 8, 32), dg.tiled_ab(128, 256, 4, 32), dg.tiled_pp(256, 256)):
         C, ok = run("fp8", A, B, tile=tile)
         assert ok
         check_exact(C, oracle_full("fp8", A, B), f"K={K} {tile}")
