@@ -35,6 +35,11 @@ import time
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
+CUS = 256
+# split-K: the workspace the bench hands the library (the selector weighs
+# split-K tiles whose fp32 partials fit), and the slice counts a sweep tries
+WORKSPACE_MIB = 64
+SPLITS = (2, 3, 4, 6, 8, 12, 16)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 # The device code whose hash identifies "the kernel" a traffic measurement
@@ -111,7 +116,14 @@ WORKLOADS = {
     "bf16_2048x11007x1024": (2048, 11007, 1024, "bf16", "normal", 1.0, "normal", 1.0, 46),
     "bf16_4095x4095x1024": (4095, 4095, 1024, "bf16", "normal", 1.0, "normal", 1.0, 47),
     "bf16_528x528x1024": (528, 528, 1024, "bf16", "normal", 1.0, "normal", 1.0, 48),
+    # one GPU's share of the LLaMA-2-7B MLP under 8-way tensor parallelism:
+    # column-parallel up/gate (N = 11008 / 8) at prefill and decode, and the
+    # row-parallel down projection (K = 11008 / 8)
+    "bf16_tp8_up_597x1376x4096": (597, 1376, 4096, "bf16", "normal", 1.0, "normal", 0.02, 61),
+    "bf16_tp8_decode_1x1376x4096": (1, 1376, 4096, "bf16", "normal", 1.0, "normal", 0.02, 62),
+    "bf16_tp8_down_597x4096x1376": (597, 4096, 1376, "bf16", "normal", 1.0, "normal", 0.02, 63),
     "fp8_4096cube": (4096, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 5),
+    "fp8_tp8_up_597x1376x4096": (597, 1376, 4096, "fp8", "normal", 1.0, "normal", 1.0, 64),
     "fp8_32x4096": (32, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 51),
 }
 HEADLINE = "bf16_4096cube"
@@ -181,29 +193,30 @@ def parse_tile(spec: str | None):
     import dense_gemm_linear_amd as dg
     kind, dims = spec.split(":")
     atom, stages, tile_k = 16, 0, 0
-    m = re.fullmatch(r"(\d+x\d+(?:w\d+)?)(?:a(\d+))?(?:s(\d+))?(?:k(\d+))?", dims)
+    m = re.fullmatch(r"(\d+x\d+(?:w\d+)?)(?:a(\d+))?(?:s(\d+))?(?:k(\d+))?(?:sk(\d+))?", dims)
     if not m:
         raise ValueError(f"bad tile spec {spec!r}")
     dims = m.group(1)
     atom = int(m.group(2) or 16)
     stages = int(m.group(3) or 0)
     tile_k = int(m.group(4) or 0)
+    k_split = int(m.group(5) or 1)
     waves = 4
     if "w" in dims:
         dims, w = dims.split("w")
         waves = int(w)
     tm, tn = (int(x) for x in dims.split("x"))
     if kind == "tiled":
-        return dg.tiled(tm, tn, waves, atom, stages, tile_k)
+        return dg.tiled(tm, tn, waves, atom, stages, tile_k, k_split)
     if kind == "ab":
-        return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k)
+        return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k, k_split)
     if kind == "pp":
-        return dg.tiled_pp(tm, tn, atom, stages, tile_k)
+        return dg.tiled_pp(tm, tn, atom, stages, tile_k, k_split)
     return dg.skinny(tm, tn)
 
 
 def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True,
-              tile=None, setup=None, soak: float = 0.0):
+              tile=None, setup=None, soak: float = 0.0, workspace=None):
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
@@ -215,15 +228,16 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     sets, (s_a, s_b), shuffle_us = setup
     copies = len(sets)
     forced = tile
+    ws_bytes = 0 if workspace is None else workspace.numel()
     if tile is None:
-        tile = dg.select_tile(M, N, K, dt)
+        tile = dg.select_tile(M, N, K, dt, workspace_bytes=ws_bytes)
 
     def call(i):
         a, bs, c = sets[i % copies]
         if dt == "bf16":
-            dg.gemm_bf16(a, bs, N, out=c, tile=forced)
+            dg.gemm_bf16(a, bs, N, out=c, tile=forced, workspace=workspace)
         else:
-            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, tile=forced)
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, tile=forced, workspace=workspace)
 
     for i in range(warmup):
         call(i)
@@ -253,22 +267,13 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     }
 
 
-def run_graph(name: str, reps: int, copies: int):
-    """Decode-size kernels are shorter than a Python launch: time R launches
-    captured in one HIP graph (no memset nodes: the kernels write every output
-    element themselves)."""
+def time_graph(call, reps: int, trials: int = 1) -> float:
+    """Per-launch time of `call` (launches only: no allocation, no memset,
+    the kernels write every output element themselves) from R calls captured
+    in one HIP graph: the median over `trials` replays of replay time / R.
+    Kernels shorter than a Python launch are timed without the host's
+    submission gaps this way."""
     import torch
-    import dense_gemm_linear_amd as dg
-    M, N, K, dt = WORKLOADS[name][:4]
-    sets, (s_a, s_b), shuffle_us = gpu_setup(name, copies)
-
-    def call(i):
-        a, bs, c = sets[i % copies]
-        if dt == "bf16":
-            dg.gemm_bf16(a, bs, N, out=c)
-        else:
-            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c)
-
     for i in range(3):
         call(i)
     torch.cuda.synchronize()
@@ -282,12 +287,38 @@ def run_graph(name: str, reps: int, copies: int):
     torch.cuda.current_stream().wait_stream(s)
     g.replay()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / reps, shuffle_us
+    per = []
+    for _ in range(trials):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) * 1e3 / reps)
+    del g
+    return sorted(per)[len(per) // 2]
+
+
+def gemm_call(name: str, sets, scales, tile=None, workspace=None):
+    """call(i): one GEMM of the workload on operand set i mod len(sets)."""
+    import dense_gemm_linear_amd as dg
+    N, dt = WORKLOADS[name][1], WORKLOADS[name][3]
+    s_a, s_b = scales
+
+    def call(i):
+        a, bs, c = sets[i % len(sets)]
+        if dt == "bf16":
+            dg.gemm_bf16(a, bs, N, out=c, tile=tile, workspace=workspace)
+        else:
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, tile=tile, workspace=workspace)
+    return call
+
+
+def run_graph(name: str, reps: int, copies: int):
+    """Decode-size kernels are shorter than a Python launch: time R launches
+    captured in one HIP graph."""
+    sets, scales, shuffle_us = gpu_setup(name, copies)
+    return time_graph(gemm_call(name, sets, scales), reps), shuffle_us
 
 
 def clock_under_load(call, seconds: float = 1.5):
@@ -373,6 +404,8 @@ def main(argv=None):
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of the "
                          "workload's GEMM, then of --copy-calibration 256) into "
                          "profiles/traffic_<workload>.json for --workload/--tile, and exit")
+    ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
+                    help="split-K workspace handed to the library (0: no split-K)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
@@ -392,11 +425,14 @@ def main(argv=None):
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
-        return sweep(name, args.steps, args.warmup)
+        return sweep(name, args.steps, args.warmup, args.workspace_mib)
+    workspace = (torch.empty(args.workspace_mib << 20, dtype=torch.uint8, device="cuda")
+                 if args.workspace_mib > 0 else None)
     # No events between launches: the K calls run back to back, and the event
-    # pair around them gives the average launch duration.
+    # pair around them gives the average launch duration (with split-K: of
+    # the GEMM and its reduction).
     r = run_timed(name, args.steps, args.warmup, tile=parse_tile(args.tile), soak=args.soak,
-                  copies=args.copies or None, per_launch=False)
+                  copies=args.copies or None, per_launch=False, workspace=workspace)
     ms_per_step = r["total_ms"] / args.steps
     kern_avg = r["total_ms"] * 1e3 / args.steps
     bound = bound_of(M, N, K, dt)
@@ -423,7 +459,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "tile": tile.name,
                    "tile_eff": round(tile.tile_eff, 4), "wq_eff": round(tile.wq_eff, 4),
-                   "operand_copies_rotated": r["copies"], "pct_of_mfma_peak": None},
+                   "operand_copies_rotated": r["copies"], "pct_of_mfma_peak": None,
+                   "workspace_mib": args.workspace_mib},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_r,
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "algorithmic_bytes": alg_bytes(M, N, K, dt),
@@ -464,9 +501,10 @@ def main(argv=None):
     return 0
 
 
-def sweep(name: str, steps: int, warmup: int) -> int:
-    """Every feasible tile on one workload; prints a line per tile and a summary
-    with the selector's regret (its pick's time over the best time)."""
+def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> int:
+    """Every feasible tile on one workload, graph-timed (`steps` launches per
+    graph, median of 3 replays); prints a line per tile and a summary with
+    the selector's regret (its pick's time over the best time)."""
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
@@ -474,15 +512,29 @@ def sweep(name: str, steps: int, warmup: int) -> int:
     copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
     setup = gpu_setup(name, copies)
     tiles = dg.all_tiles(M, dt)
+    # split-K variants of the rungs that leave CUs idle, one per distinct
+    # slice count after the library lowers it
+    ws_bytes = ws_mib << 20
+    for t in list(tiles):
+        if t.kernel == dg.GEMM_KERNEL_SKINNY or -(-M // t.tile_m) * -(-N // t.tile_n) >= CUS:
+            continue
+        seen = set()
+        for S in SPLITS:
+            ts = dg.with_split(t, S)
+            need = dg.workspace_bytes(M, N, K, dt, ts)
+            if 0 < need <= ws_bytes and need not in seen:
+                seen.add(need)
+                tiles.append(ts)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    sets, scales, _ = setup
     res = {}
     for t in tiles:
-        r = run_timed(name, steps, warmup, tile=t, setup=setup)
-        us = sorted(r["kernel_us"])[len(r["kernel_us"]) // 2]
+        us = time_graph(gemm_call(name, sets, scales, t, workspace), reps=steps, trials=3)
         res[t.name] = us
         print(json.dumps({"sweep": name, "tile": t.name, "kernel_us_median": round(us, 3),
                           "tflops": round(flops(M, N, K) / (us * 1e-6) / 1e12, 1),
                           "gbps": round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)}), flush=True)
-    pick = dg.select_tile(M, N, K, dt)
+    pick = dg.select_tile(M, N, K, dt, workspace_bytes=ws_bytes)
     best = min(res, key=res.get)
     print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
                       "best": best, "best_us": round(res[best], 3),

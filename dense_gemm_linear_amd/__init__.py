@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdensegemm.so")
@@ -37,7 +37,8 @@ GEMM_KERNEL_TILED_AB = 2
 GEMM_KERNEL_TILED_PP = 3
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
-           "gemm_tile_check", "gemm_status_string")
+           "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
+           "gemm_bf16_ws", "gemm_fp8_scaled_ws")
 
 
 class GemmTile(ctypes.Structure):
@@ -65,9 +66,12 @@ class Tile:
     @property
     def name(self) -> str:
         """e.g. tiled128x128 (4 waves, 16x16 atom), ab256x256w8a32s4k32 (8 waves,
-        32x32 atom, 4 stages, 32-element k-tile); unset fields are omitted."""
+        32x32 atom, 4 stages, 32-element k-tile), tiled128x128a32s3k64sk4 (split
+        over 4 K slices); unset fields are omitted."""
         atom = "" if self.atom in (0, 16) else f"a{self.atom}"
         pipe = (f"s{self.lds_stages}" if self.lds_stages else "") + (f"k{self.tile_k}" if self.tile_k else "")
+        if self.kernel != GEMM_KERNEL_SKINNY and self.k_split > 1:
+            pipe += f"sk{self.k_split}"
         if self.kernel == GEMM_KERNEL_TILED:
             return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}") + \
                 atom + pipe
@@ -87,20 +91,33 @@ class Tile:
                     t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
 
 
-def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0) -> Tile:
-    """A rung of the tiled ladder; stages / tile_k (K elements per stage) 0 = any."""
-    return Tile(GEMM_KERNEL_TILED, tm, tn, tile_k=tile_k, atom=atom, waves=waves, lds_stages=stages)
-
-
-def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0) -> Tile:
-    """A rung of the A+B-in-LDS ladder; stages / tile_k 0 = any."""
-    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, tile_k=tile_k, atom=atom, waves=waves,
+def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0,
+          k_split: int = 1) -> Tile:
+    """A rung of the tiled ladder; stages / tile_k (K elements per stage) 0 = any;
+    k_split > 1 splits K over that many workgroups (needs a workspace)."""
+    return Tile(GEMM_KERNEL_TILED, tm, tn, tile_k=tile_k, atom=atom, waves=waves, k_split=k_split,
                 lds_stages=stages)
 
 
-def tiled_pp(tm: int, tn: int, atom: int = 32, stages: int = 0, tile_k: int = 0) -> Tile:
+def tiled_ab(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0,
+             k_split: int = 1) -> Tile:
+    """A rung of the A+B-in-LDS ladder; stages / tile_k 0 = any."""
+    return Tile(GEMM_KERNEL_TILED_AB, tm, tn, tile_k=tile_k, atom=atom, waves=waves,
+                k_split=k_split, lds_stages=stages)
+
+
+def tiled_pp(tm: int, tn: int, atom: int = 32, stages: int = 0, tile_k: int = 0,
+             k_split: int = 1) -> Tile:
     """A rung of the ping-pong A+B ladder (8 waves); stages / tile_k 0 = any."""
-    return Tile(GEMM_KERNEL_TILED_PP, tm, tn, tile_k=tile_k, atom=atom, waves=8, lds_stages=stages)
+    return Tile(GEMM_KERNEL_TILED_PP, tm, tn, tile_k=tile_k, atom=atom, waves=8, k_split=k_split,
+                lds_stages=stages)
+
+
+def with_split(tile: Tile, k_split: int) -> Tile:
+    """The same tiled rung split over k_split K slices."""
+    if tile.kernel == GEMM_KERNEL_SKINNY:
+        raise ValueError("the skinny kernel splits K inside one workgroup")
+    return replace(tile, k_split=k_split)
 
 
 def skinny(tm: int, tn: int, waves: int = 4) -> Tile:
@@ -177,6 +194,17 @@ def _load_lib():
     lib.gemm_fp8_scaled.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
                                     ctypes.POINTER(GemmTile), P]
     lib.gemm_fp8_scaled.restype = ctypes.c_int
+    lib.select_tile_ws.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int32, ctypes.c_size_t,
+                                   ctypes.POINTER(GemmTile)]
+    lib.select_tile_ws.restype = ctypes.c_int
+    lib.gemm_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(GemmTile)]
+    lib.gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.gemm_bf16_ws.argtypes = [P, I64, P, P, I64, I64, I64, I64, ctypes.POINTER(GemmTile), P,
+                                 ctypes.c_size_t, P]
+    lib.gemm_bf16_ws.restype = ctypes.c_int
+    lib.gemm_fp8_scaled_ws.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
+                                       ctypes.POINTER(GemmTile), P, ctypes.c_size_t, P]
+    lib.gemm_fp8_scaled_ws.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
@@ -199,12 +227,23 @@ def _dtype_code(dtype) -> int:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def select_tile(M: int, N: int, K: int, dtype="bf16", num_cus: int = 0) -> Tile:
+def select_tile(M: int, N: int, K: int, dtype="bf16", num_cus: int = 0,
+                workspace_bytes: int = 0) -> Tile:
+    """The library's choice; with workspace_bytes > 0, split-K tiles whose
+    partials fit are candidates too (select_tile_ws)."""
     t = GemmTile()
-    st = lib.select_tile(M, N, K, _dtype_code(dtype), num_cus, ctypes.byref(t))
+    if workspace_bytes:
+        st = lib.select_tile_ws(M, N, K, _dtype_code(dtype), num_cus, workspace_bytes, ctypes.byref(t))
+    else:
+        st = lib.select_tile(M, N, K, _dtype_code(dtype), num_cus, ctypes.byref(t))
     if st != GEMM_OK:
         raise GemmError("select_tile", st)
     return Tile.from_c(t)
+
+
+def workspace_bytes(M: int, N: int, K: int, dtype, tile: Tile) -> int:
+    """Device workspace `tile` needs on M x N x K (0 unless it splits K)."""
+    return int(lib.gemm_workspace_bytes(M, N, K, _dtype_code(dtype), ctypes.byref(tile.to_c())))
 
 
 def tile_check(tile: Tile, M: int, dtype="bf16") -> int:
@@ -278,27 +317,60 @@ def _tile_ptr(tile):
     return ctypes.byref(tile.to_c())
 
 
-def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None):
-    """C[M, N] = A[M, K] * B[N, K]^T with Bs = shuffle_b(B); returns C (bf16)."""
+def _workspace(A, N: int, K: int, code: int, tile, workspace):
+    """(pointer, bytes) of the split-K workspace: the caller's uint8 device
+    tensor, or a new one when a forced split-K tile needs it, else none."""
+    if workspace is not None:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if tile is None or tile.kernel == GEMM_KERNEL_SKINNY or tile.k_split <= 1:
+        return None, 0
+    nbytes = workspace_bytes(A.shape[0], N, K, code, tile)
+    if nbytes == 0:
+        return None, 0
+    # torch's caching allocator hands this block out again only to work
+    # ordered after ours on the same (current) stream, so it may be freed on
+    # return
+    ws = _torch().empty(nbytes, dtype=_torch().uint8, device=A.device)
+    return ws.data_ptr(), nbytes
+
+
+def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None, workspace=None):
+    """C[M, N] = A[M, K] * B[N, K]^T with Bs = shuffle_b(B); returns C (bf16).
+    workspace: a uint8 device tensor for split-K (then tile None lets the
+    library weigh split-K tiles that fit in it)."""
     _check_rows("A", A)
     C = _out(A, N, out)
     M, K = A.shape
-    st = lib.gemm_bf16(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0), M, N,
-                       K, _tile_ptr(tile), _stream_ptr(A))
+    ws, nbytes = _workspace(A, N, K, GEMM_BF16, tile, workspace)
+    if ws is None:
+        st = lib.gemm_bf16(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0), M,
+                           N, K, _tile_ptr(tile), _stream_ptr(A))
+    else:
+        st = lib.gemm_bf16_ws(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0),
+                              M, N, K, _tile_ptr(tile), ws, nbytes, _stream_ptr(A))
     if st != GEMM_OK:
         raise GemmError("gemm_bf16", st)
     return C
 
 
-def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None = None):
+def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None = None,
+                    workspace=None):
     """C = (A * B^T) * scale_a * scale_b for e4m3 A [M, K] and Bs = shuffle_b(B);
     scale_a / scale_b are one-element float32 device tensors."""
     _check_rows("A", A)
     C = _out(A, N, out)
     M, K = A.shape
-    st = lib.gemm_fp8_scaled(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
-                             scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
-                             _tile_ptr(tile), _stream_ptr(A))
+    ws, nbytes = _workspace(A, N, K, GEMM_FP8_E4M3, tile, workspace)
+    if ws is None:
+        st = lib.gemm_fp8_scaled(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
+                                 scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
+                                 _tile_ptr(tile), _stream_ptr(A))
+    else:
+        st = lib.gemm_fp8_scaled_ws(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
+                                    scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
+                                    _tile_ptr(tile), ws, nbytes, _stream_ptr(A))
     if st != GEMM_OK:
         raise GemmError("gemm_fp8_scaled", st)
     return C

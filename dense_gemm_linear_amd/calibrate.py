@@ -38,7 +38,8 @@ def workloads():
     return bench.WORKLOADS
 
 
-NAME = re.compile(r"(tiled|ab|pp)(\d+)x(\d+)(?:w(\d+))?(?:a(\d+))?s(\d+)k(\d+)$")
+SKINNY = re.compile(r"skinny(\d+)x(\d+)(?:w(\d+))?$")
+NAME = re.compile(r"(tiled|ab|pp)(\d+)x(\d+)(?:w(\d+))?(?:a(\d+))?s(\d+)k(\d+)(?:sk(\d+))?$")
 
 
 def parse(name: str):
@@ -46,44 +47,117 @@ def parse(name: str):
     m = NAME.match(name)
     if not m:
         return None
-    kind, tm, tn, w, a, st, tk = m.groups()
+    kind, tm, tn, w, a, st, tk, sk = m.groups()
     return {"kernel": {"tiled": 0, "ab": 2, "pp": 3}[kind], "tm": int(tm), "tn": int(tn),
-            "waves": int(w or (8 if kind == "pp" else 4)), "atom": int(a or 16), "stages": int(st), "tile_k": int(tk)}
+            "waves": int(w or (8 if kind == "pp" else 4)), "atom": int(a or 16), "stages": int(st),
+            "tile_k": int(tk), "k_split": int(sk or 1)}
 
 
-def fit(paths):
+def split_plan(M, N, K, e, ktb, k_split):
+    """(slices, k-tiles per slice, ldw) as the library lowers k_split."""
+    nkt = math.ceil(K * e / ktb)
+    want = max(1, min(k_split, nkt))
+    per = math.ceil(nkt / want)
+    return math.ceil(nkt / per), per, math.ceil(N / 4) * 4
+
+
+def load_points(paths):
+    """(rung key, features, split features, t) per tiled sweep line and
+    (skinny key, features, t) per skinny line."""
     wl = workloads()
-    rows = {}
+    pts, sk = [], []
     for p in paths:
         for line in open(p):
             d = json.loads(line)
+            M, N, K, dt = wl[d["sweep"]][:4]
+            e = 2 if dt == "bf16" else 1
+            t = d["kernel_us_median"]
+            m = SKINNY.match(d["tile"])
+            if m:
+                tm, tn, w = int(m.group(1)), int(m.group(2)), int(m.group(3) or 4)
+                nwg = math.ceil(math.ceil(N / 16) / (tn // 16))
+                per_cu = math.ceil(nwg / CUS)
+                wg_mb = (tn * K * e + tm * K * e) / 1e6
+                total_mb = (math.ceil(N / 16) * 16 * K * e + M * K * e + 2 * M * N) / 1e6
+                sk.append(((dt, tm, tn, w), [per_cu * wg_mb, total_mb, 1.0], t))
+                continue
             r = parse(d["tile"])
             if r is None:
                 continue
-            M, N, K, dt = wl[d["sweep"]][:4]
-            e = 2 if dt == "bf16" else 1
-            ncu = math.ceil(math.ceil(M / r["tm"]) * math.ceil(N / r["tn"]) / CUS)
-            key = (dt, r["kernel"], r["tm"], r["tn"], r["waves"], r["atom"], r["stages"],
-                   r["tile_k"] * e)
-            rows.setdefault(key, []).append((ncu * K * e / 1000.0, ncu, d["kernel_us_median"]))
-    out = []
-    for key, pts in sorted(rows.items()):
-        X = np.array([[x, n, 1.0] for x, n, _ in pts])
-        y = np.array([t for _, _, t in pts])
-        coef, _ = nnls(X, y)
-        out.append((key, coef, len(pts)))
-    return out
+            ktb = r["tile_k"] * e
+            key = (dt, r["kernel"], r["tm"], r["tn"], r["waves"], r["atom"], r["stages"], ktb)
+            tiles = math.ceil(M / r["tm"]) * math.ceil(N / r["tn"])
+            S, per, ldw = split_plan(M, N, K, e, ktb, r["k_split"])
+            kbytes = K * e if S == 1 else per * ktb
+            ncu = math.ceil(tiles * S / CUS)
+            extra = [0.0, 0.0, 0.0] if S == 1 else \
+                [ncu * r["tm"] * r["tn"] * 4 / 1e6, (S * M * ldw * 4 + 2 * M * N) / 1e6, 1.0]
+            total_mb = (M * K * e + N * K * e + 2 * M * N) / 1e6
+            pts.append((key, [ncu * kbytes / 1000.0, ncu, total_mb, 1.0], extra, t))
+    return pts, sk
+
+
+def fit(paths):
+    """Three fits, all non-negative least squares:
+    - per rung a, b, g, c of t = a * n_cu * K_bytes / 1000 + b * n_cu
+      + g * MB + c (MB: A, B and C bytes / 1e6) from its one-pass points (the
+      model one-pass candidates are priced with);
+    - a second set per rung fitted jointly over one-pass and split points,
+      with three split-K costs shared by all rungs that only split runs pay:
+          d * n_cu * tile_m * tile_n * 4 / 1e6    (fp32 partial stores per CU)
+        + r1 * (S * M * ldw * 4 + 2 * M * N) / 1e6  (the reduction's traffic)
+        + r0                                      (its launch),
+      weighted by 1 / t (relative error ranks candidates); split candidates
+      are priced with it, since it is pinned at the short K of one slice;
+    - per skinny rung t = a * per_cu * MB_per_workgroup + b * MB_total + c."""
+    pts, sk = load_points(paths)
+    keys = sorted({k for k, _, x, _ in pts if x[2] == 0.0})
+    plain = {}
+    for k in keys:
+        f = [(ff, t) for kk, ff, x, t in pts if kk == k and x[2] == 0.0]
+        plain[k] = (nnls(np.array([a for a, _ in f]), np.array([t for _, t in f]))[0], len(f))
+    F = 4
+    col = {k: F * i for i, k in enumerate(keys)}
+    rows = [(k, f, x, t) for k, f, x, t in pts if k in col]
+    X = np.zeros((len(rows), F * len(keys) + 3))
+    y = np.zeros(len(rows))
+    for i, (k, f, x, t) in enumerate(rows):
+        X[i, col[k]:col[k] + F] = f
+        X[i, -3:] = x
+        y[i] = t
+    w = 1.0 / np.maximum(y, 1.0)
+    coef, _ = nnls(X * w[:, None], y * w)
+    rungs = [(k, plain[k][0], coef[col[k]:col[k] + F], plain[k][1]) for k in keys]
+    n_split = sum(1 for r in rows if r[2][2] == 1.0)
+    skinny = []
+    for k in sorted({k for k, _, _ in sk}):
+        f = [(ff, t) for kk, ff, t in sk if kk == k]
+        skinny.append((k, nnls(np.array([a for a, _ in f]), np.array([t for _, t in f]))[0], len(f)))
+    return rungs, (coef[-3:], n_split), skinny
 
 
 def emit(fits, path):
+    rungs, ((d_st, r1, r0), n_split), skinny = fits
     lines = ["// Generated by calibrate.py from measured MI355X tile sweeps; do not edit.",
-             "// {dtype, kernel, tile_m, tile_n, waves, atom, stages, k-tile bytes, a, b, c, points}:",
-             "// t_us = a * n_cu * K_bytes / 1000 + b * n_cu + c",
+             "// {dtype, kernel, tile_m, tile_n, waves, atom, stages, k-tile bytes, a, b, g, c,",
+             "//  a, b, g, c of the split-K set, one-pass points}:",
+             "// t_us = a * n_cu * K_bytes / 1000 + b * n_cu + g * (A + B + C bytes) / 1e6 + c",
              "static const RungCalib kRungCalib[] = {"]
-    for (dt, kern, tm, tn, w, atom, st, ktb), (a, b, c), n in fits:
+    for (dt, kern, tm, tn, w, atom, st, ktb), (a, b, g, c), (a2, b2, g2, c2), n in rungs:
         d = 0 if dt == "bf16" else 1
         lines.append(f"    {{{d}, {kern}, {tm}, {tn}, {w}, {atom}, {st}, {ktb}, "
-                     f"{a:.5f}f, {b:.5f}f, {c:.5f}f, {n}}},")
+                     f"{a:.5f}f, {b:.5f}f, {g:.5f}f, {c:.5f}f, "
+                     f"{a2:.5f}f, {b2:.5f}f, {g2:.5f}f, {c2:.5f}f, {n}}},")
+    lines.append("};")
+    lines += ["// split-K beyond the rung's own model: d * n_cu * partial-tile MB + r1 * reduce MB + r0",
+              "// {d, r1, r0, points}",
+              f"static const SplitCalib kSplitCalib = {{{d_st:.5f}f, {r1:.5f}f, {r0:.5f}f, {n_split}}};",
+              "// skinny rungs {dtype, tile_m, tile_n, waves, a, b, c, points}:",
+              "// t_us = a * per_cu * MB_per_workgroup + b * MB_total + c",
+              "static const SkinnyCalib kSkinnyCalib[] = {"]
+    for (dt, tm, tn, w), (a, b, c), n in skinny:
+        d = 0 if dt == "bf16" else 1
+        lines.append(f"    {{{d}, {tm}, {tn}, {w}, {a:.5f}f, {b:.5f}f, {c:.5f}f, {n}}},")
     lines.append("};")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -93,4 +167,6 @@ if __name__ == "__main__":
     paths = sys.argv[1:] or [os.path.join(HERE, "calibration", "mi355x_sweep.jsonl")]
     fits = fit(paths)
     emit(fits, os.path.join(HERE, "csrc", "calibration.inc"))
-    print(f"{len(fits)} rungs calibrated")
+    (d_st, r1, r0), n = fits[1]
+    print(f"{len(fits[0])} rungs, {len(fits[2])} skinny rungs calibrated; split-K from {n} points: "
+          f"{d_st:.3f} us per MB of partials per CU, {r1:.3f} us per MB reduced, {r0:.2f} us launch")

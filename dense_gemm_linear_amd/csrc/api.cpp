@@ -7,8 +7,6 @@
 
 namespace dg {
 
-void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out);
-
 hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
     return dt == DT_BF16 ? launch_ab_bf16(idx, a, s) : launch_ab_fp8(idx, a, s);
@@ -61,12 +59,23 @@ gemm_status device_info(int* cus)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int kMaxKSplit = 64;
+
+// Split-K plan of a resolved tile (S == 1: none).
+SplitPlan tile_split(const gemm_tile& t, int idx, int64_t M, int64_t N, int64_t K, int e)
+{
+    if (t.kernel == GEMM_KERNEL_SKINNY || t.k_split <= 1 || K == 0)
+        return SplitPlan{1, 0, 0, 0};
+    return split_plan(M, N, K, e, rung_ktb(t.kernel, idx), t.k_split);
+}
+
 // The ladder rung a tile names, if it is usable for this shape: atom 0 means
 // 16; tile_k (elements) and lds_stages 0 mean the first rung that matches
 // the other fields.
 bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
 {
-    if (t.tile_k < 0 || t.tile_k > 4096 || t.lds_stages < 0)
+    if (t.tile_k < 0 || t.tile_k > 4096 || t.lds_stages < 0 || t.k_split < 0 ||
+        (t.kernel != GEMM_KERNEL_SKINNY && t.k_split > kMaxKSplit))
         return false;
     const int atom = t.atom == 0 ? 16 : t.atom;
     const int ktb = t.tile_k * e;
@@ -86,7 +95,7 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
 
 gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const float* sa,
                      const float* sb, uint16_t* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                     const gemm_tile* tile, void* stream)
+                     const gemm_tile* tile, void* ws, size_t ws_bytes, void* stream)
 {
     const int e = dt == DT_BF16 ? 2 : 1;
     // ---- argument checks (no HIP call before this block ends)
@@ -102,6 +111,8 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     if ((K > 0 && (!aligned16(A) || !aligned16(Bs) || (lda * e) % 16 != 0)) ||
         ((uintptr_t)C & 1u) != 0)
         return GEMM_ERR_INVALID_VALUE;
+    if (ws_bytes > 0 && (!ws || !aligned16(ws)))
+        return GEMM_ERR_INVALID_VALUE;
     if (K % (dt == DT_BF16 ? 16 : 64) != 0)
         return GEMM_ERR_UNSUPPORTED;
     // 32-bit buffer offsets: a tile of up to 256 rows of A or C, and one
@@ -111,10 +122,16 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         return GEMM_ERR_UNSUPPORTED;
     gemm_tile t;
     int idx = -1;
+    SplitPlan pl{1, 0, 0, 0};
     if (tile) {
         t = *tile;
         if (!resolve_tile(t, M, e, &idx))
             return GEMM_ERR_UNSUPPORTED;
+        pl = tile_split(t, idx, M, N, K, e);
+        if (pl.S > 1 && !partial_plane_fits(M, pl.ldw))
+            return GEMM_ERR_UNSUPPORTED;
+        if (pl.ws_bytes > (int64_t)ws_bytes)
+            return ws_bytes == 0 ? GEMM_ERR_UNSUPPORTED : GEMM_ERR_INVALID_VALUE;
     }
     // ---- device
     int cus = 0;
@@ -125,9 +142,12 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     if (K == 0)
         return launch_zero_c(C, ldc, M, N, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     if (!tile) {
-        choose_tile(M, N, K, dt, cus, &t);
+        choose_tile(M, N, K, dt, cus, ws_bytes, &t);
         if (!resolve_tile(t, M, e, &idx))
             return GEMM_ERR_UNSUPPORTED;   // the selector names only rungs that exist
+        pl = tile_split(t, idx, M, N, K, e);
+        if (pl.ws_bytes > (int64_t)ws_bytes)
+            return GEMM_ERR_UNSUPPORTED;   // the selector keeps within the workspace
     }
     GemmArgs a;
     memset(&a, 0, sizeof a);
@@ -146,6 +166,10 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     a.tail = (a.KA_b % 128) != 0;
     a.nblk = (int)((N + 15) / 16);
     a.c_vec = (((uintptr_t)C & 15u) == 0) && (ldc % 8 == 0);
+    a.splits = pl.S;
+    a.kt_per = pl.kt_per;
+    a.ldw = pl.ldw;
+    a.ws = pl.S > 1 ? static_cast<float*>(ws) : nullptr;
     hipError_t err;
     if (t.kernel == GEMM_KERNEL_SKINNY) {
         err = launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
@@ -155,6 +179,8 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         err = t.kernel == GEMM_KERNEL_TILED_AB   ? launch_ab(dt, idx, a, s)
               : t.kernel == GEMM_KERNEL_TILED_PP ? launch_pp(dt, idx, a, s)
                                                  : launch_tiled(dt, idx, a, s);
+        if (err == hipSuccess && pl.S > 1)
+            err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -167,14 +193,46 @@ extern "C" {
 gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
                       int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* stream)
 {
-    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, stream);
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, nullptr,
+                        0, stream);
 }
 
 gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
                             const float* scale_b, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
                             int64_t K, const gemm_tile* tile, void* stream)
 {
-    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, stream);
+    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, nullptr,
+                        0, stream);
+}
+
+gemm_status gemm_bf16_ws(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile,
+                        workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_fp8_scaled_ws(const uint8_t* A, int64_t lda, const void* Bs,
+                               const float* scale_a, const float* scale_b, uint16_t* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               const gemm_tile* tile, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile,
+                        workspace, workspace_bytes, stream);
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                            const gemm_tile* tile)
+{
+    if (!tile || M <= 0 || N <= 0 || K <= 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return 0;
+    const int e = dtype == GEMM_BF16 ? 2 : 1;
+    int idx = -1;
+    if (!dg::resolve_tile(*tile, M, e, &idx))
+        return 0;
+    return (size_t)dg::tile_split(*tile, idx, M, N, K, e).ws_bytes;
 }
 
 size_t shuffle_b_bytes(int64_t N, int64_t K, gemm_dtype dtype)

@@ -126,4 +126,28 @@ int ab_lds_bytes(int idx);
 int pp_lds_bytes(int idx);
 int tiled_vgpr_estimate(const TiledRung& r);
 
+// Split-K plan of a tiled rung with k-tiles of ktb bytes asked for k_split
+// slices: S slices of kt_per k-tiles each (S <= k_split; no slice is empty),
+// and the fp32 partial workspace S * M * ldw * 4 bytes, ldw = N rounded up
+// to 4.  S == 1 needs no workspace.
+struct SplitPlan {
+    int S, kt_per, ldw;
+    int64_t ws_bytes;
+};
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int e, int ktb, int k_split);
+// k-tile bytes of a resolved tiled / A+B / ping-pong rung
+int rung_ktb(int kernel, int idx);
+void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                 gemm_tile* out);
+hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,
+                                int64_t ldc, const float* sa, const float* sb, hipStream_t s);
+// Split-K addresses a partial plane with 32-bit byte offsets, also for the
+// up to 256 rows a tile reaches past M (their stores are dropped by the
+// buffer bound): (M + 256) * ldw * 4 must stay within 2 GiB.
+constexpr int64_t kMaxPartialPlaneBytes = INT64_C(1) << 31;
+inline bool partial_plane_fits(int64_t M, int64_t ldw)
+{
+    return (M + 256) * ldw * 4 <= kMaxPartialPlaneBytes;
+}
+
 }  // namespace dg

@@ -63,7 +63,61 @@ struct GemmArgs {
     int tiles_m, tiles_n; // tiled kernel grid
     int nblk;             // ceil(N / 16)
     int c_vec;            // C base 16-byte aligned and ldc % 8 == 0
+    // Split-K (tiled kernels): the grid is tiles x splits workgroups; slice s
+    // multiplies k-tiles [s kt_per, (s+1) kt_per) and writes its fp32 partial
+    // tile to plane s of ws ([splits][M][ldw], ldw = N rounded up to 4)
+    // instead of C.  splits == 1: the whole K range, C written directly.
+    int splits;
+    int kt_per;           // k-tiles per slice, in the kernel's own k-tile size
+    int ldw;
+    float* ws;
 };
+
+// The K range of one workgroup: k-tiles [kt0, kt0 + n) of KTB bytes, and the
+// bounds its masked loads test against (the slice end, or K itself for the
+// last slice).  last_full is the first k-tile that needs masking.
+struct KRange {
+    int kt0, n, ka_end, kb_end, last_full;
+};
+
+template <int KTB, bool SPLIT>
+__device__ __forceinline__ KRange k_range(const GemmArgs& p, int slice)
+{
+    constexpr int KPK = KTB / 64;
+    const int nkt = (p.KB + KPK - 1) / KPK;
+    KRange r;
+    if constexpr (!SPLIT) {
+        r.kt0 = 0;
+        r.n = nkt;
+        r.ka_end = p.KA_b;
+        r.kb_end = p.KB;
+        r.last_full = p.KA_b / KTB;
+        return r;
+    }
+    const int per = p.kt_per;
+    r.kt0 = slice * per;
+    const int kt_end = min(nkt, r.kt0 + per);
+    r.n = kt_end - r.kt0;
+    r.ka_end = min(p.KA_b, kt_end * KTB);
+    r.kb_end = min(p.KB, kt_end * KPK);
+    r.last_full = r.ka_end / KTB;
+    return r;
+}
+
+// Workgroup -> (output tile index, K slice): slices outermost, so the
+// workgroups running together share A rows and B columns of one K range.
+template <bool SPLIT>
+__device__ __forceinline__ int split_slice(const GemmArgs& p, int& wg)
+{
+    if constexpr (!SPLIT) {
+        wg = (int)blockIdx.x;
+        return 0;
+    }
+    const int G = p.tiles_m * p.tiles_n;
+    const int slice = (int)blockIdx.x / G;
+    wg = (int)blockIdx.x - slice * G;
+    return slice;
+}
 
 // Workgroup -> output tile.  Workgroups are dispatched round robin over the 8
 // XCDs, each with its own L2; renumber so that every XCD receives one
@@ -319,6 +373,46 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
 
 // Largest CH dividing MR whose staging (WAVES regions of CH*R rows) fits in
 // `avail` bytes of LDS.
+// Split-K: this wave's fp32 accumulators into plane `slice` of the partial
+// workspace, row-major with pitch ldw.  For one accumulator element the 64
+// lanes write whole runs of R consecutive floats of one or more rows.  Rows
+// past M fall outside the descriptor (dropped); columns past N are switched
+// off per lane.
+template <class AT, int MR, int NR>
+__device__ __forceinline__ void store_partial(const GemmArgs& p,
+                                              const typename AT::acc_t (&acc)[MR][NR], int slice,
+                                              int row_w, int col_w, int lane)
+{
+    constexpr int R = AT::R;
+    const rsrc_t rw = make_rsrc(p.ws + (int64_t)slice * p.M * p.ldw,
+                                (uint32_t)((int64_t)p.M * p.ldw * 4));
+    const int lc = lane % R;
+    const uint32_t pitch = (uint32_t)p.ldw * 4u;
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const int col = col_w + j * R + lc;
+            // byte offset of element 0; a lane past N gets kOOB, which stays
+            // past the bound with the row steps below added (they are under
+            // 32 rows, and the host keeps (M + 256) * pitch within 2^31).
+            // A branch-free select: one base per accumulator, not per element.
+            const uint32_t row0 = (uint32_t)(row_w + mi * R + AT::out_row(0, lane));
+            const uint32_t inb = 0u - (uint32_t)(col < p.N);
+            const uint32_t base = (((row0 * (uint32_t)p.ldw + (uint32_t)col) * 4u) & inb) |
+                                  (kOOB & ~inb);
+#pragma unroll
+            for (int e = 0; e < AT::NACC; ++e) {
+                // the rows of one accumulator's elements differ by constants
+                const uint32_t step = (uint32_t)(AT::out_row(e, lane) - AT::out_row(0, lane));
+                // through a scalar: hipcc's __builtin_bit_cast of a vector
+                // element lvalue reads element 0 (seen in the ISA)
+                const float v = acc[mi][j][e];
+                store4(rw, base + step * pitch, __float_as_uint(v));
+            }
+        }
+}
+
 constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
 {
     int ch = MR;
@@ -501,7 +595,7 @@ struct TiledShape {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int ST, int R, int KTB>
+template <int DT, int TM, int TN, int WM, int ST, int R, int KTB, bool SPLIT>
 __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 {
     using S = TiledShape<TM, TN, WM, ST, R, KTB>;
@@ -518,13 +612,13 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;     // wave row (M) and column (N)
-    int tm, tn;
-    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    int wg, tm, tn;
+    const int slice = split_slice<SPLIT>(p, wg);
+    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const int nkt = (p.KB + KPK - 1) / KPK;
-    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;   // first k-tile that needs masking
+    const KRange kr = k_range<KTB, SPLIT>(p, slice);
 
     // Descriptors rebased at this tile: rows past M and 16-column blocks past
     // ceil(N/16) fall outside and read as zero.
@@ -555,17 +649,19 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         for (int j = 0; j < NR; ++j)
             acc[mi][j] = zero_acc<AT>();
 
-    // A k-tile past the real K (kt >= nkt, or the K tail of the last one)
-    // loads through out-of-range offsets: zeros, and no memory traffic.
-    // Load op n (A DMAs first, then B fragments) belongs to part n % STEPS.
-    auto load = [&](int kt, int stage, int part) __attribute__((always_inline)) {
-        const bool mask = kt >= last_full;
+    // A k-tile past the end of this workgroup's K range (past K, or past its
+    // slice) loads through out-of-range offsets: zeros, and no memory
+    // traffic.  Load op n (A DMAs first, then B fragments) belongs to part
+    // n % STEPS.
+    auto load = [&](int kt_local, int stage, int part) __attribute__((always_inline)) {
+        const int kt = kr.kt0 + kt_local;
+        const bool mask = kt >= kr.last_full;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
             if (i % STEPS != part)
                 continue;
             uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
-            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(lds + stage * A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -581,7 +677,7 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
                     const int kb = kt * KPK + AT::b_half(s, q);
                     uint32_t off = b_lane + (uint32_t)(j * (R / 16) * p.KB + kb) * 1024u +
                                    ((uint32_t)AT::b_group(s, lane, q) << 8);
-                    if (mask && kb >= p.KB)
+                    if (mask && kb >= kr.kb_end)
                         off = kOOB;
                     breg[stage][j][s][q] = load16(rb, off);
                 }
@@ -604,8 +700,12 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
             for (int j = 0; j < NR; ++j)
                 acc[mi][j] = AT::mma(af[set][mi], breg[stage][j][s], acc[mi][j]);
     };
-    k_loop<ST, STEPS, S::LOADS, MR * NR, MR * P>(nkt, load, read, mma);
+    k_loop<ST, STEPS, S::LOADS, MR * NR, MR * P>(kr.n, load, read, mma);
 
+    if constexpr (SPLIT) {
+        store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
+        return;
+    }
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
         scale_a = *p.sa;
@@ -652,7 +752,7 @@ struct ABShape {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int WN, int ST, int R, int KTB>
+template <int DT, int TM, int TN, int WM, int WN, int ST, int R, int KTB, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 {
     using S = ABShape<TM, TN, WM, WN, ST, R, KTB>;
@@ -670,13 +770,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    int wg, tm, tn;
+    const int slice = split_slice<SPLIT>(p, wg);
+    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const int nkt = (p.KB + KPK - 1) / KPK;
-    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;
+    const KRange kr = k_range<KTB, SPLIT>(p, slice);
     const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
                                 (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
     const int nb0 = n0 >> 4;
@@ -714,15 +814,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
             acc[mi][j] = zero_acc<AT>();
 
     // Load op n (A DMAs first, then B DMAs) belongs to part n % STEPS.
-    auto load = [&](int kt, int stage, int part) __attribute__((always_inline)) {
-        const bool mask = kt >= last_full;
+    auto load = [&](int kt_local, int stage, int part) __attribute__((always_inline)) {
+        const int kt = kr.kt0 + kt_local;
+        const bool mask = kt >= kr.last_full;
         uint8_t* base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
             if (i % STEPS != part)
                 continue;
             uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
-            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -732,7 +833,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
             if ((A_DMA + i) % STEPS != part)
                 continue;
             uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
-            if (mask && kt * KPK + (int)b_half[i] >= p.KB)
+            if (mask && kt * KPK + (int)b_half[i] >= kr.kb_end)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -766,8 +867,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
             for (int j = 0; j < NR; ++j)
                 acc[mi][j] = AT::mma(af[set][mi], bf[set][j], acc[mi][j]);
     };
-    k_loop<ST, STEPS, S::LOADS, MR * NR, (MR + NR) * P>(nkt, load, read, mma);
+    k_loop<ST, STEPS, S::LOADS, MR * NR, (MR + NR) * P>(kr.n, load, read, mma);
 
+    if constexpr (SPLIT) {
+        store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
+        return;
+    }
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
         scale_a = *p.sa;
@@ -798,7 +903,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 // k-tile t must have landed (each wave: at most (ST-2) x LOADS of its loads
 // still in flight); at the end of half 2t only group 1 needs that much (its
 // next read is k-tile t, already complete), group 0 none.
-template <int DT, int TM, int TN, int ST, int R, int KTB>
+template <int DT, int TM, int TN, int ST, int R, int KTB, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 {
     using S = ABShape<TM, TN, 2, 4, ST, R, KTB>;
@@ -818,13 +923,13 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;     // wm = the group
     const bool g0 = wm == 0;
-    int tm, tn;
-    tile_coords<DG_GROUP_M>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    int wg, tm, tn;
+    const int slice = split_slice<SPLIT>(p, wg);
+    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const int nkt = (p.KB + KPK - 1) / KPK;
-    const int last_full = (p.KA_b % KTB) ? nkt - 1 : nkt;
+    const KRange kr = k_range<KTB, SPLIT>(p, slice);
     const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
                                 (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
     const int nb0 = n0 >> 4;
@@ -857,14 +962,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
         for (int j = 0; j < NR; ++j)
             acc[mi][j] = zero_acc<AT>();
 
-    // A k-tile past K loads through out-of-range offsets: zeros, no traffic.
-    auto load = [&](int kt, int stage) __attribute__((always_inline)) {
-        const bool mask = kt >= last_full;
+    // A k-tile past this workgroup's K range loads through out-of-range
+    // offsets: zeros, no traffic.
+    auto load = [&](int kt_local, int stage) __attribute__((always_inline)) {
+        const int kt = kr.kt0 + kt_local;
+        const bool mask = kt >= kr.last_full;
         uint8_t* base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
             uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
-            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= p.KA_b)
+            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -872,7 +979,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) {
             uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
-            if (mask && kt * KPK + (int)b_half[i] >= p.KB)
+            if (mask && kt * KPK + (int)b_half[i] >= kr.kb_end)
                 off = kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
@@ -921,7 +1028,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
     DG_STAGE_BARRIER((ST - 2) * LOADS);
     int stage = 0;           // = t % ST
     int pre = ST - 1;        // = (t + ST - 1) % ST
-    for (int t = 0; t < nkt; ++t) {
+    for (int t = 0; t < kr.n; ++t) {
         // half 2t
         if (g0) {
             load(t + ST - 1, pre);
@@ -948,6 +1055,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __syncthreads();
 
+    if constexpr (SPLIT) {
+        store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
+        return;
+    }
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
         scale_a = *p.sa;

@@ -65,6 +65,68 @@ hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStre
                            dim3(256), args, 0, s);
 }
 
+// Split-K reduction.  ws holds `splits` fp32 partial planes [M][ldw]; the
+// output is C[m][n] = bf16_rne(sum over s of ws[s][m][n]) with the planes
+// added in increasing s, a fixed order, so the result does not depend on
+// which workgroup of the GEMM finished first; e4m3 products are then scaled
+// as (x * sa) * sb, as in the one-pass epilogue.  One thread per 4
+// consecutive columns of one row; planes are read with 16-byte loads.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int splits, int M,
+                                                            int N, int ldw, uint16_t* C,
+                                                            int64_t ldc, const float* sa,
+                                                            const float* sb)
+{
+    const int q = ldw >> 2;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)M * q)
+        return;
+    const int row = (int)(t / q);
+    const int c0 = (int)(t - (int64_t)row * q) * 4;
+    const int64_t plane = (int64_t)M * ldw;
+    const float* src = ws + (int64_t)row * ldw + c0;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int s = 1; s < splits; ++s) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + s * plane);
+        acc[0] += v[0];
+        acc[1] += v[1];
+        acc[2] += v[2];
+        acc[3] += v[3];
+    }
+    float scale_a = 1.f, scale_b = 1.f;
+    if (sa) {
+        scale_a = *sa;
+        scale_b = *sb;
+    }
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v = acc[e];
+        if (sa)
+            v = (v * scale_a) * scale_b;
+        h[e] = bf16_rne(v);
+    }
+    uint16_t* dst = C + (int64_t)row * ldc + c0;
+    if (c0 + 4 <= N && ((uintptr_t)dst & 7u) == 0) {
+        const uint2 w = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        *reinterpret_cast<uint2*>(dst) = w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c0 + e < N)
+                dst[e] = h[e];
+    }
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,
+                                int64_t ldc, const float* sa, const float* sb, hipStream_t s)
+{
+    const int64_t threads = (int64_t)M * (ldw / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    void* args[] = {&ws, &splits, &M, &N, &ldw, &C, &ldc, &sa, &sb};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&splitk_reduce_kernel),
+                           dim3((unsigned)blocks), dim3(256), args, 0, s);
+}
+
 int ab_lds_bytes(int idx)
 {
     int i = 0;

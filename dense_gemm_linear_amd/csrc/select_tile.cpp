@@ -27,9 +27,22 @@ namespace dg {
 namespace {
 
 // Measured per-rung cost constants (calibrate.py): t_us = a * n_cu * K_bytes
-// / 1000 + b * n_cu + c, n_cu = ceil(tiles / CUs).
+// / 1000 + b * n_cu + g * MB + c, n_cu = ceil(tiles / CUs), MB = bytes of A,
+// B and C / 1e6.
 struct RungCalib {
     int dt, kernel, tm, tn, waves, atom, st, ktb;
+    float a, b, g, c;       // one-pass runs
+    float as, bs, gs, cs;   // split-K runs: fitted jointly with the split costs
+    int points;
+};
+// split-K costs beyond a rung's own time (calibrate.py)
+struct SplitCalib {
+    float d, r1, r0;
+    int points;
+};
+// skinny rungs: t_us = a * per_cu * MB per workgroup + b * MB in total + c
+struct SkinnyCalib {
+    int dt, tm, tn, waves;
     float a, b, c;
     int points;
 };
@@ -45,17 +58,23 @@ const RungCalib* find_calib(int dt, int kernel, int tm, int tn, int waves, int a
     return nullptr;
 }
 
-// Calibrated time of a tiled / A+B rung, or `fallback` if it was never measured.
+// Calibrated time of a tiled / A+B rung, or `fallback` if it was never
+// measured.  With split-K, K is one slice's K and every tile counts `split`
+// times.
 double calibrated_us(int dt, int kernel, int tm, int tn, int waves, int atom, int st, int ktb,
-                     int64_t M, int64_t N, int64_t K, int cus, double fallback)
+                     int64_t M, int64_t N, int64_t K, int cus, double fallback, int split = 1)
 {
     const RungCalib* r = find_calib(dt, kernel, tm, tn, waves, atom, st, ktb);
     if (!r)
         return fallback;
     const int e = dt == GEMM_BF16 ? 2 : 1;
-    const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+    const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn) * split;
     const double ncu = (double)((tiles + cus - 1) / cus);
-    return r->a * ncu * (double)K * e / 1000.0 + r->b * ncu + r->c;
+    // A, B and C bytes of the whole GEMM (K here is one slice's K)
+    const double mb = ((double)M * K * e * split + (double)N * K * e * split + 2.0 * M * N) / 1e6;
+    if (split > 1)
+        return r->as * ncu * (double)K * e / 1000.0 + r->bs * ncu + r->gs * mb + r->cs;
+    return r->a * ncu * (double)K * e / 1000.0 + r->b * ncu + r->g * mb + r->c;
 }
 
 struct Chip {
@@ -66,6 +85,11 @@ struct Chip {
     double hbm_bytes_per_s = 8.0e12 * 0.85;              // sustained fraction
     double cu_stream_bytes_per_clk = 48.0;               // one CU pulling from HBM
     int lds_per_cu = 160 * 1024;
+    // split-K: fp32 partial stores per CU, and the reduce kernel's launch gap
+    // and streaming rate (partials are read back from the Infinity Cache)
+    double partial_store_bytes_per_us_cu = 64.0 * 2.1e3;
+    double reduce_launch_us = 3.0;
+    double reduce_bytes_per_us = 6.0e6;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -102,7 +126,7 @@ void fill_common(gemm_tile& t, int kernel, int tm, int tn, int dt, int waves = 4
     t.lds_stages = stages;
 }
 
-bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const TiledRung& r,
+bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const TiledRung& r, int split,
                  const Chip& c, Cand& out)
 {
     const int tm = r.tm, tn = r.tn, waves = r.waves;
@@ -118,7 +142,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, cons
     const int e = dt == GEMM_BF16 ? 2 : 1;
     const int64_t nkt = cdiv(K * e, 128);
     const int64_t tiles_m = cdiv(M, tm), tiles_n = cdiv(N, tn);
-    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t tiles = tiles_m * tiles_n * split;
     const double flop_tile_kt = 2.0 * tm * tn * (128.0 / e);
     const double mfma = flop_tile_kt / (c.mfma_flop_per_clk_cu[dt] * atom_rate(dt, r.atom));
     // every wave reads its rows of A from LDS once per k-tile (the 4 wave
@@ -132,7 +156,8 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, cons
     double us = per_cu * tile_cyc / c.clock_hz * 1e6;
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
-    us = calibrated_us(dt, GEMM_KERNEL_TILED, tm, tn, waves, r.atom, r.st, r.ktb, M, N, K, cus, us);
+    us = calibrated_us(dt, GEMM_KERNEL_TILED, tm, tn, waves, r.atom, r.st, r.ktb, M, N, K, cus, us,
+                       split);
     fill_common(out.t, GEMM_KERNEL_TILED, tm, tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * tm * (double)tiles_n * tn);
     const int64_t rounds = cdiv(tiles, cus);
@@ -146,7 +171,7 @@ bool price_tiled(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, cons
 
 // A and B staged in LDS: each k-tile enters the workgroup once; waves read
 // their A and B fragments from LDS.
-bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const ABRung& r,
+bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const ABRung& r, int split,
               const Chip& c, Cand& out)
 {
     const int waves = r.wm * r.wn;
@@ -162,7 +187,7 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
     const int e = dt == GEMM_BF16 ? 2 : 1;
     const int64_t nkt = cdiv(K * e, 128);
     const int64_t tiles_m = cdiv(M, r.tm), tiles_n = cdiv(N, r.tn);
-    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t tiles = tiles_m * tiles_n * split;
     const double flop_tile_kt = 2.0 * r.tm * r.tn * (128.0 / e);
     const double mfma = flop_tile_kt / (c.mfma_flop_per_clk_cu[dt] * atom_rate(dt, r.atom));
     const double ldsc = ((double)r.wn * r.tm * 128 + (double)r.wm * r.tn * 128) / c.lds_bytes_per_clk;
@@ -175,7 +200,7 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
     const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
     us = std::max(us, bytes / c.hbm_bytes_per_s * 1e6) + 2.0;
     us = calibrated_us(dt, GEMM_KERNEL_TILED_AB, r.tm, r.tn, waves, r.atom, r.st, r.ktb, M, N, K,
-                       cus, us);
+                       cus, us, split);
     fill_common(out.t, GEMM_KERNEL_TILED_AB, r.tm, r.tn, dt, waves, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
     const int64_t rounds = cdiv(tiles, cus);
@@ -188,7 +213,7 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
 }
 
 // Ping-pong rungs: the A+B model with the 2 x 4 wave grid, unless calibrated.
-bool price_pp(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const PPRung& r,
+bool price_pp(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const PPRung& r, int split,
               const Chip& c, Cand& out)
 {
     const int lds = pp_lds_bytes(idx);
@@ -197,7 +222,7 @@ bool price_pp(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const P
     const int e = dt == GEMM_BF16 ? 2 : 1;
     const int64_t nkt = cdiv(K * e, r.ktb);
     const int64_t tiles_m = cdiv(M, r.tm), tiles_n = cdiv(N, r.tn);
-    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t tiles = tiles_m * tiles_n * split;
     const double mfma = 2.0 * r.tm * r.tn * ((double)r.ktb / e) / (c.mfma_flop_per_clk_cu[dt] * 0.98);
     const double vmem = (double)(r.tm + r.tn) * r.ktb / c.vmem_bytes_per_clk;
     const double per_kt = std::max(mfma, vmem) * 1.25;
@@ -210,7 +235,7 @@ bool price_pp(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const P
     if (!find_calib(dt, GEMM_KERNEL_TILED_PP, r.tm, r.tn, 8, r.atom, r.st, r.ktb))
         return false;
     us = calibrated_us(dt, GEMM_KERNEL_TILED_PP, r.tm, r.tn, 8, r.atom, r.st, r.ktb, M, N, K, cus,
-                       us);
+                       us, split);
     fill_common(out.t, GEMM_KERNEL_TILED_PP, r.tm, r.tn, dt, 8, r.atom, r.st, r.ktb);
     const double te = (double)M * N / ((double)tiles_m * r.tm * (double)tiles_n * r.tn);
     const int64_t rounds = cdiv(tiles, cus);
@@ -239,6 +264,12 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, const Skinny
     const int64_t per_cu = cdiv(nwg, cus);
     const double cu_bytes = per_cu * ((double)nb * 16 * K * e + (double)tm * K * e);
     us = std::max(us, cu_bytes / (c.cu_stream_bytes_per_clk * c.clock_hz) * 1e6) + 3.0;
+    for (const SkinnyCalib& k : kSkinnyCalib)
+        if (k.dt == dt && k.tm == tm && k.tn == tn && k.waves == r.waves) {
+            const double wg_mb = ((double)tn * K * e + (double)tm * K * e) / 1e6;
+            us = k.a * per_cu * wg_mb + k.b * hbm / 1e6 + k.c;
+            break;
+        }
     fill_common(out.t, GEMM_KERNEL_SKINNY, tm, tn, dt, r.waves);
     out.t.k_split = r.waves;
     const double te = (double)M * N / ((double)tm * (double)nwg * tn);
@@ -251,7 +282,45 @@ bool price_skinny(int64_t M, int64_t N, int64_t K, int dt, int cus, const Skinny
     return true;
 }
 
+// Split-K costs on top of the rung's own time for one slice of K: every
+// workgroup stores its fp32 partial tile, and the reduce kernel reads all
+// partial planes and writes C.
+double split_overhead_us(int64_t M, int64_t N, int tm, int tn, int64_t units, int S, int cus,
+                         const Chip& c)
+{
+    const double partial = (double)cdiv(units, cus) * tm * tn * 4;
+    const double reduced = (double)S * M * (double)(cdiv(N, 4) * 4) * 4 + 2.0 * M * N;
+    if (kSplitCalib.points > 0)
+        return kSplitCalib.d * partial / 1e6 + kSplitCalib.r1 * reduced / 1e6 + kSplitCalib.r0;
+    return partial / c.partial_store_bytes_per_us_cu + c.reduce_launch_us +
+           reduced / c.reduce_bytes_per_us;
+}
+
 }  // namespace
+
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int e, int ktb, int k_split)
+{
+    SplitPlan pl{1, 0, (int)(cdiv(N, 4) * 4), 0};
+    const int64_t nkt = cdiv(K * e, ktb);
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(k_split, nkt));
+    pl.kt_per = (int)cdiv(nkt, want);
+    pl.S = (int)cdiv(nkt, pl.kt_per);
+    pl.ws_bytes = pl.S > 1 ? (int64_t)pl.S * M * pl.ldw * 4 : 0;
+    return pl;
+}
+
+int rung_ktb(int kernel, int idx)
+{
+    if (idx < 0)
+        return 0;
+    if (kernel == GEMM_KERNEL_TILED && idx < (int)(sizeof kTiledLadder / sizeof kTiledLadder[0]))
+        return kTiledLadder[idx].ktb;
+    if (kernel == GEMM_KERNEL_TILED_AB && idx < (int)(sizeof kABLadder / sizeof kABLadder[0]))
+        return kABLadder[idx].ktb;
+    if (kernel == GEMM_KERNEL_TILED_PP && idx < (int)(sizeof kPPLadder / sizeof kPPLadder[0]))
+        return kPPLadder[idx].ktb;
+    return 0;
+}
 
 int tiled_vgpr_estimate(const TiledRung& r)
 {
@@ -306,8 +375,10 @@ bool skinny_supported(int tm, int tn, int waves)
     return false;
 }
 
-// Pick the fastest candidate under the model; fill `out`.
-void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* out)
+// Pick the fastest candidate under the model; fill `out`.  With a workspace
+// of ws_bytes, split-K variants of the tiled rungs whose partial planes fit
+// are candidates too (only for shapes with fewer tiles than CUs).
+void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, gemm_tile* out)
 {
     const Chip chip;
     Cand best{}, best_screened{};
@@ -327,31 +398,61 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, gemm_tile* ou
                 consider(cd);
         }
     }
+    const int e = dt == GEMM_BF16 ? 2 : 1;
+    static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    // one rung at every slice count: price(K of a slice, slices, candidate)
+    auto rung = [&](int tm, int tn, int ktb, auto price) {
+        for (int S : kSplits) {
+            const SplitPlan pl = split_plan(M, N, K, e, ktb, S);
+            if (S > 1) {
+                if (ws_bytes == 0 || pl.S != S || pl.kt_per < 2 ||
+                    cdiv(M, tm) * cdiv(N, tn) >= cus || pl.ws_bytes > (int64_t)ws_bytes ||
+                    !partial_plane_fits(M, pl.ldw))
+                    continue;
+            }
+            Cand cd;
+            const int64_t Ks = S > 1 ? (int64_t)pl.kt_per * ktb / e : K;
+            if (!price(Ks, S, cd))
+                continue;
+            if (S > 1) {
+                const int64_t units = cdiv(M, tm) * cdiv(N, tn) * S;
+                const double bytes = (double)M * K * e + (double)N * K * e + 2.0 * M * N;
+                cd.us = std::max(cd.us + split_overhead_us(M, N, tm, tn, units, S, cus, chip),
+                                 bytes / chip.hbm_bytes_per_s * 1e6);
+                cd.t.k_split = S;
+                cd.t.predicted_us = (float)cd.us;
+            }
+            consider(cd);
+        }
+    };
     int idx = 0;
     for (const TiledRung& r : kTiledLadder) {
-        Cand cd;
-        if (price_tiled(M, N, K, dt, cus, idx++, r, chip, cd))
-            consider(cd);
+        const int i = idx++;
+        rung(r.tm, r.tn, r.ktb, [&](int64_t Ks, int S, Cand& cd) {
+            return price_tiled(M, N, Ks, dt, cus, i, r, S, chip, cd);
+        });
     }
     idx = 0;
     for (const ABRung& r : kABLadder) {
-        Cand cd;
-        if (price_ab(M, N, K, dt, cus, idx++, r, chip, cd))
-            consider(cd);
+        const int i = idx++;
+        rung(r.tm, r.tn, r.ktb, [&](int64_t Ks, int S, Cand& cd) {
+            return price_ab(M, N, Ks, dt, cus, i, r, S, chip, cd);
+        });
     }
     idx = 0;
     for (const PPRung& r : kPPLadder) {
-        Cand cd;
-        if (price_pp(M, N, K, dt, cus, idx++, r, chip, cd))
-            consider(cd);
+        const int i = idx++;
+        rung(r.tm, r.tn, r.ktb, [&](int64_t Ks, int S, Cand& cd) {
+            return price_pp(M, N, Ks, dt, cus, i, r, S, chip, cd);
+        });
     }
     *out = have ? best.t : best_screened.t;
 }
 
 }  // namespace dg
 
-extern "C" gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
-                                   int32_t num_cus, gemm_tile* out)
+extern "C" gemm_status select_tile_ws(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                                      int32_t num_cus, size_t workspace_bytes, gemm_tile* out)
 {
     if (!out || M < 0 || N < 0 || K < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3) ||
         num_cus < 0)
@@ -367,6 +468,12 @@ extern "C" gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype d
         num_cus = cus;
     }
     dg::choose_tile(std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), std::max<int64_t>(K, 1),
-                    (int)dtype, num_cus, out);
+                    (int)dtype, num_cus, workspace_bytes, out);
     return GEMM_OK;
+}
+
+extern "C" gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                                   int32_t num_cus, gemm_tile* out)
+{
+    return select_tile_ws(M, N, K, dtype, num_cus, 0, out);
 }

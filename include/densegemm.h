@@ -91,6 +91,13 @@ typedef enum {
  *     = waves that split K in one workgroup: 4 for every (tile_m, tile_n),
  *     8 for tile_m, tile_n in {16, 32}, 16 for tile_m in {16, 32} with
  *     tile_n 16; k_split 0 means 4.
+ *   split-K (tiled, tiled_ab, tiled_pp with k_split = S > 1): the grid is
+ *     tiles x S workgroups; slice s multiplies k-tiles [s P, (s+1) P) with
+ *     P = ceil(k-tiles / S), so S is lowered to ceil(k-tiles / P) when
+ *     slices would be empty.  Each workgroup writes an fp32 partial tile to
+ *     a caller workspace, and a second kernel adds the slices in increasing
+ *     s (a fixed order: the result is the same on every run), scales (e4m3)
+ *     and rounds to bf16.  It needs the *_ws entry points.
  */
 typedef struct {
     int32_t kernel;      /* gemm_kernel */
@@ -99,7 +106,8 @@ typedef struct {
     int32_t tile_k;      /* elements of K per pipeline stage (k-tile); 0 = any */
     int32_t atom;        /* MFMA block edge: 16 or 32 (0 = 16) */
     int32_t waves;       /* waves per workgroup */
-    int32_t k_split;     /* skinny: waves splitting K (0 = 4) */
+    int32_t k_split;     /* skinny: waves splitting K (0 = 4); tiled kernels: K slices
+                            across workgroups (split-K, 0 or 1 = none, at most 64) */
     int32_t lds_stages;  /* k-tiles in the LDS ring (2 = ping-pong); 0 = any */
     float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */
     float wq_eff;        /* tiles / (ceil(tiles / CUs) * CUs) */
@@ -123,6 +131,28 @@ typedef struct {
  */
 gemm_status select_tile(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
                         gemm_tile* out);
+
+/*
+ * select_tile_ws -- select_tile, also weighing split-K variants of the tiled
+ * rungs whose fp32 partials fit in workspace_bytes (0: none, the same choice
+ * as select_tile).  Split-K is considered only when the output has fewer
+ * tiles than the device has CUs: the TraceLens page leaves Split-K and
+ * Stream-K out of its dimension-efficiency model ("Important
+ * considerations"), and the FlyDSL PR #1303 page routes shapes that cannot
+ * keep the CUs busy to a separate fallback; here the K slices fill the idle
+ * CUs.  Errors as for select_tile.
+ */
+gemm_status select_tile_ws(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
+                           size_t workspace_bytes, gemm_tile* out);
+
+/*
+ * gemm_workspace_bytes -- device workspace the *_ws entry points need to run
+ * `tile` on M x N x K: S * M * ldw * 4 bytes for a split-K tile (S slices
+ * after lowering, ldw = N rounded up to 4), 0 for any other tile.  Returns 0
+ * for tile == NULL, sizes <= 0, or a tile that names no rung.  Host only.
+ */
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                            const gemm_tile* tile);
 
 /*
  * shuffle_b_bytes -- size in bytes of the preshuffled weight for N x K.
@@ -200,6 +230,37 @@ gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* 
 gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
                             const float* scale_b, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
                             int64_t K, const gemm_tile* tile, void* stream);
+
+/*
+ * gemm_bf16_ws / gemm_fp8_scaled_ws -- gemm_bf16 / gemm_fp8_scaled with a
+ * caller-owned device workspace for split-K (see gemm_tile).
+ *
+ *   workspace        device, 16-byte aligned, workspace_bytes long; NULL
+ *                    allowed with workspace_bytes == 0.  Its contents on
+ *                    entry are ignored and on return are unspecified; calls
+ *                    that share one workspace must not overlap in time.
+ *   tile             NULL = select_tile_ws(..., workspace_bytes, ...);
+ *                    forced split-K tiles need gemm_workspace_bytes(tile).
+ *
+ * The product is the same as without split-K up to fp32 summation order:
+ * slice partials are fp32 and are added in a fixed order, so a given tile
+ * gives bitwise identical results on every run.  Two kernels are launched
+ * on `stream` (the GEMM, then the reduction); the library allocates nothing.
+ *
+ * Errors as for gemm_bf16 / gemm_fp8_scaled, plus INVALID_VALUE when
+ * workspace_bytes > 0 and workspace is NULL or not 16-byte aligned, or a
+ * forced split-K tile needs more than workspace_bytes (> 0); UNSUPPORTED when
+ * it needs a workspace and workspace_bytes == 0 (as the plain entry points
+ *  answer for such a tile) or (M + 256) * ldw * 4 bytes exceed 2 GiB.
+ */
+gemm_status gemm_bf16_ws(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* workspace,
+                         size_t workspace_bytes, void* stream);
+gemm_status gemm_fp8_scaled_ws(const uint8_t* A, int64_t lda, const void* Bs,
+                               const float* scale_a, const float* scale_b, uint16_t* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               const gemm_tile* tile, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * gemm_tile_check -- would `tile`, forced on gemm_bf16 (dtype GEMM_BF16) or

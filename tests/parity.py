@@ -61,8 +61,10 @@ def guard_untouched(buf: torch.Tensor, M: int, N: int, col0: int = 0) -> bool:
 
 
 def run(dt: str, A: np.ndarray, B: np.ndarray, tile=None, sa: float = 1.0, sb: float = 1.0,
-        ldc: int | None = None, col0: int = 0, guard: int = 16):
-    """Shuffle B on the device, run the GEMM, return (C bits [M, N], guard ok)."""
+        ldc: int | None = None, col0: int = 0, guard: int = 16, workspace=None):
+    """Shuffle B on the device, run the GEMM, return (C bits [M, N], guard ok).
+    workspace: a uint8 device tensor for split-K tiles (None: the binding
+    allocates one when a forced split-K tile needs it)."""
     M, K = A.shape
     N = B.shape[0]
     if dt == "bf16":
@@ -72,11 +74,11 @@ def run(dt: str, A: np.ndarray, B: np.ndarray, tile=None, sa: float = 1.0, sb: f
     Bs = dg.shuffle_b(Bd, dtype=dt)
     buf, C = alloc_c(M, N, ldc, guard, col0)
     if dt == "bf16":
-        dg.gemm_bf16(Ad, Bs, N, out=C, tile=tile)
+        dg.gemm_bf16(Ad, Bs, N, out=C, tile=tile, workspace=workspace)
     else:
         s_a = torch.tensor([sa], dtype=torch.float32, device="cuda")
         s_b = torch.tensor([sb], dtype=torch.float32, device="cuda")
-        dg.gemm_fp8_scaled(Ad, Bs, N, s_a, s_b, out=C, tile=tile)
+        dg.gemm_fp8_scaled(Ad, Bs, N, s_a, s_b, out=C, tile=tile, workspace=workspace)
     torch.cuda.synchronize()
     return host_bits(C), guard_untouched(buf, M, N, col0)
 

@@ -59,8 +59,9 @@ def test_shuffle_b_bytes_fp8_layout_size():
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 def test_select_tile_metrics_match_oracle(M, N, K, dt):
     t = dg.select_tile(M, N, K, dt, num_cus=256)
-    assert t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_SKINNY, dg.GEMM_KERNEL_TILED_AB)
-    if t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB):
+    tiled_kinds = (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB, dg.GEMM_KERNEL_TILED_PP)
+    assert t.kernel in tiled_kinds + (dg.GEMM_KERNEL_SKINNY,)
+    if t.kernel in tiled_kinds:
         assert t in dg.ladder_tiles(dt) or any(
             (t.kernel, t.tile_m, t.tile_n, t.waves, t.atom, t.lds_stages, t.tile_k) ==
             (r.kernel, r.tile_m, r.tile_n, r.waves, r.atom, r.lds_stages, r.tile_k)
@@ -104,7 +105,8 @@ def test_select_tile_routes_small_m_to_skinny():
     for M in (1, 8, 16):
         assert dg.select_tile(M, 11008, 4096, "bf16", 256).kernel == dg.GEMM_KERNEL_SKINNY
     assert dg.select_tile(4096, 4096, 4096, "bf16", 256).kernel in (dg.GEMM_KERNEL_TILED,
-                                                                    dg.GEMM_KERNEL_TILED_AB)
+                                                                    dg.GEMM_KERNEL_TILED_AB,
+                                                                    dg.GEMM_KERNEL_TILED_PP)
 
 
 def test_select_tile_errors():
@@ -181,3 +183,89 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     libs = {line.split()[-1] for line in maps if "libamdhip64" in line and "/" in line}
     assert len(libs) == 1, libs
+
+
+# ------------------------------------------------------------------ split-K
+def _ws_expected(M, N, K, e, ktb, k_split):
+    """Workspace of a split-K tile: S slices of ceil(k-tiles / S') k-tiles
+    (S' = k_split capped at the k-tile count, S lowered so none is empty),
+    each an fp32 plane M x ldw with ldw = N rounded up to 4."""
+    nkt = -(-K * e // ktb)
+    want = max(1, min(k_split, nkt))
+    per = -(-nkt // want)
+    S = -(-nkt // per)
+    ldw = -(-N // 4) * 4
+    return S * M * ldw * 4 if S > 1 else 0
+
+
+@pytest.mark.parametrize("dt,e", [("bf16", 2), ("fp8", 1)])
+def test_workspace_bytes_formula(dt, e):
+    rungs = [(dg.tiled(128, 128, 4, 32, 3, 128 // e), 128),
+             (dg.tiled_ab(256, 256, 8, 32, 4, 64 // e), 64),
+             (dg.tiled_pp(256, 256, 32, 4, 64 // e), 64)]
+    for tile, ktb in rungs:
+        for M, N in ((263, 270), (597, 1376), (1, 16)):
+            for K in (64, 128, 1088, 4096):
+                for S in (1, 2, 3, 7, 64):
+                    t = dg.with_split(tile, S)
+                    got = dg.workspace_bytes(M, N, K, dt, t)
+                    assert got == _ws_expected(M, N, K, e, ktb, S), (t.name, M, N, K)
+    assert dg.workspace_bytes(16, 64, 4096, dt, dg.skinny(16, 16)) == 0
+    assert dg.workspace_bytes(64, 64, 4096, dt, dg.with_split(dg.tiled(64, 64), 65)) == 0
+    assert dg.lib.gemm_workspace_bytes(64, 64, 64, 0, None) == 0
+
+
+def test_select_tile_ws_stays_within_budget():
+    shapes = CONFIG_SHAPES + [(597, 1376, 4096), (597, 4096, 1376), (1, 1376, 4096)]
+    for M, N, K in shapes:
+        for dt in ("bf16", "fp8"):
+            if dt == "fp8" and K % 64:
+                continue
+            plain = dg.select_tile(M, N, K, dt, 256)
+            for budget in (1 << 20, 16 << 20, 256 << 20):
+                t = dg.select_tile(M, N, K, dt, 256, workspace_bytes=budget)
+                assert dg.workspace_bytes(M, N, K, dt, t) <= budget, (M, N, K, dt, budget, t.name)
+                assert dg.tile_check(t, M, dt) == dg.GEMM_OK
+                if t.k_split > 1 and t.kernel != dg.GEMM_KERNEL_SKINNY:
+                    tiles = -(-M // t.tile_m) * -(-N // t.tile_n)
+                    assert tiles < 256, "split-K only for shapes with fewer tiles than CUs"
+                else:
+                    assert t == plain
+    # an under-filled shape (55 tiles of 128 x 128) is split when memory allows
+    t = dg.select_tile(597, 1376, 4096, "bf16", 256, workspace_bytes=256 << 20)
+    assert t.k_split > 1
+
+
+def test_split_k_argument_checks():
+    E = dg.GEMM_ERR_INVALID_VALUE
+    U = dg.GEMM_ERR_UNSUPPORTED
+    split = dg.with_split(dg.tiled(128, 128, 4, 32), 4).to_c()
+    need = dg.workspace_bytes(263, 270, 1040, "bf16", dg.Tile.from_c(split))
+    assert need > 0
+    ws = dg.lib.gemm_bf16_ws
+
+    def call(tile, w, nbytes):
+        return ws(PA, 1040, PB, PC, 270, 263, 270, 1040, tile, w, nbytes, None)
+    # the plain entry point cannot run a split-K tile
+    assert _bf16(PA, 1040, PB, PC, 270, 263, 270, 1040, ctypes.byref(split)) == U
+    assert call(ctypes.byref(split), None, 0) == U
+    assert call(ctypes.byref(split), 0x40000, need - 4) == E          # too small
+    assert call(ctypes.byref(split), 0x40008, need) == E              # not 16-byte aligned
+    assert call(None, None, 1024) == E                                # bytes without a pointer
+    for k in (-1, 65):
+        bad = dg.with_split(dg.tiled(128, 128, 4, 32), k).to_c()
+        assert call(ctypes.byref(bad), 0x40000, need) == U
+    f = dg.lib.gemm_fp8_scaled_ws
+    split8 = dg.with_split(dg.tiled(128, 128, 4, 32), 4).to_c()
+    assert f(PA, 1088, PB, 0x50000, 0x50010, PC, 270, 263, 270, 1088, ctypes.byref(split8), None,
+             0, None) == U
+    assert f(PA, 1088, PB, 0x50000, 0x50010, PC, 270, 263, 270, 1088, ctypes.byref(split8),
+             0x40000, 64, None) == E
+
+
+def test_split_k_rejects_planes_past_32_bit_offsets():
+    """(M + 256) * ldw * 4 > 2 GiB: a split-K tile is refused before any launch."""
+    t = dg.with_split(dg.tiled(64, 64), 2).to_c()
+    N = (1 << 31) // (4 * (1 + 256)) + 64
+    assert dg.lib.gemm_bf16_ws(PA, 4096, PB, PC, N, 1, N, 4096, ctypes.byref(t), 0x40000,
+                               1 << 40, None) == dg.GEMM_ERR_UNSUPPORTED
