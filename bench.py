@@ -216,7 +216,12 @@ def parse_tile(spec: str | None):
 
 
 def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True,
-              tile=None, setup=None, soak: float = 0.0, workspace=None):
+              tile=None, setup=None, soak: float = 0.0, workspace=None, graph: bool = False):
+    """W eager warm-up calls, then K timed calls with one HIP event pair
+    around them on the kernels' stream.  graph=True captures the K calls in
+    one HIP graph and times its replay (no host submission gaps between
+    short kernels); otherwise they are issued eagerly, optionally with an
+    event pair around each (per_launch)."""
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
@@ -242,6 +247,27 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    call(warmup + i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        del g
+        clock = clock_under_load(call, soak) if soak > 0 else None
+        return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "kernel_us": [], "tile": tile,
+                "shuffle_us": shuffle_us, "copies": copies, "clock": clock}
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)] if per_launch else []
@@ -404,6 +430,8 @@ def main(argv=None):
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of the "
                          "workload's GEMM, then of --copy-calibration 256) into "
                          "profiles/traffic_<workload>.json for --workload/--tile, and exit")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue the K timed calls eagerly instead of replaying them from one HIP graph")
     ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
                     help="split-K workspace handed to the library (0: no split-K)")
     ap.add_argument("--sweep", action="store_true",
@@ -428,11 +456,12 @@ def main(argv=None):
         return sweep(name, args.steps, args.warmup, args.workspace_mib)
     workspace = (torch.empty(args.workspace_mib << 20, dtype=torch.uint8, device="cuda")
                  if args.workspace_mib > 0 else None)
-    # No events between launches: the K calls run back to back, and the event
-    # pair around them gives the average launch duration (with split-K: of
-    # the GEMM and its reduction).
+    # No events between launches: the K calls run back to back (replayed from
+    # one HIP graph unless --eager), and the event pair around them gives the
+    # average launch duration (with split-K: of the GEMM and its reduction).
     r = run_timed(name, args.steps, args.warmup, tile=parse_tile(args.tile), soak=args.soak,
-                  copies=args.copies or None, per_launch=False, workspace=workspace)
+                  copies=args.copies or None, per_launch=False, workspace=workspace,
+                  graph=not args.eager)
     ms_per_step = r["total_ms"] / args.steps
     kern_avg = r["total_ms"] * 1e3 / args.steps
     bound = bound_of(M, N, K, dt)
@@ -465,7 +494,8 @@ def main(argv=None):
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "algorithmic_bytes": alg_bytes(M, N, K, dt),
                      "kernel_us_avg": round(kern_avg, 3),
-                     "timing": "HIP events around the K back-to-back calls on the kernels' stream"},
+                     "timing": ("HIP events around the K back-to-back calls on the kernels' stream"
+                                + ("" if args.eager else ", replayed from one HIP graph"))},
         "shuffle_b_us": round(r["shuffle_us"], 2),
     }
     if bound == "mfma":
