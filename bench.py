@@ -44,7 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 # The device code whose hash identifies "the kernel" a traffic measurement
 # belongs to: a measurement taken on other sources is not reported.
-KERNEL_SOURCES = ["device.hpp", "kernels.hpp", "tiled.inc", "tiled_bf16.hip", "tiled_fp8.hip",
+KERNEL_SOURCES = ["device.hpp", "kernels.hpp", "tiled_inst.hip",
                   "skinny.hip"]
 
 
@@ -340,6 +340,80 @@ def gemm_call(name: str, sets, scales, tile=None, workspace=None):
     return call
 
 
+def epilogue_compare(name: str, spec: str, reps: int, ws_mib: int) -> int:
+    """The fused epilogue against the same work done by a caller without it:
+    the plain GEMM, then the epilogue as torch elementwise ops on C.  Both
+    graph-timed; one JSON line.  spec: comma-separated parts of scale_m,
+    scale_n, bias, mul and at most one activation (relu, silu, gelu,
+    gelu_tanh)."""
+    import torch
+    import dense_gemm_linear_amd as dg
+    M, N, K, dt = WORKLOADS[name][:4]
+    parts = [p for p in spec.split(",") if p]
+    acts = [p for p in parts if p in dg.ACTIVATIONS and p != "none"]
+    unknown = [p for p in parts if p not in ("scale_m", "scale_n", "bias", "mul") and p not in acts]
+    if unknown or len(acts) > 1:
+        print(f"bench.py: bad --epilogue {spec!r}", file=sys.stderr)
+        return 2
+    act = acts[0] if acts else None
+    per_set = alg_bytes(M, N, K, dt) + (2 * M * N if "mul" in parts else 0)
+    copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
+    sets, (s_a, s_b), _ = gpu_setup(name, copies)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    kw = {}
+    if "scale_m" in parts:
+        kw["scale_m"] = torch.rand(M, device="cuda", generator=g) + 0.5
+    if "scale_n" in parts:
+        kw["scale_n"] = torch.rand(N, device="cuda", generator=g) + 0.5
+    if "bias" in parts:
+        kw["bias"] = torch.randn(N, device="cuda", generator=g).bfloat16()
+    muls = [torch.randn(M, N, device="cuda", generator=g).bfloat16() for _ in range(copies)] \
+        if "mul" in parts else None
+    workspace = torch.empty(max(ws_mib << 20, 16), dtype=torch.uint8, device="cuda")
+    torch_act = {"relu": torch.relu, "silu": torch.nn.functional.silu,
+                 "gelu": torch.nn.functional.gelu, "gelu_erf": torch.nn.functional.gelu,
+                 "gelu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh")}
+
+    def gemm(i, **extra):
+        a, bs, c = sets[i % copies]
+        if dt == "bf16":
+            dg.gemm_bf16(a, bs, N, out=c, workspace=workspace, **extra)
+        else:
+            dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, workspace=workspace, **extra)
+        return c
+
+    def fused(i):
+        extra = dict(kw)
+        if muls is not None:
+            extra["mul"] = muls[i % copies]
+        gemm(i, activation=act, **extra)
+
+    def unfused(i):
+        c = gemm(i)
+        y = c.float()
+        if "scale_m" in kw:
+            y = y * kw["scale_m"][:, None]
+        if "scale_n" in kw:
+            y = y * kw["scale_n"][None, :]
+        if "bias" in kw:
+            y = y + kw["bias"].float()[None, :]
+        if act:
+            y = torch_act[act](y)
+        if muls is not None:
+            y = y * muls[i % copies].float()
+        c.copy_(y.bfloat16())
+
+    t_plain = time_graph(lambda i: gemm(i), reps, trials=3)
+    t_fused = time_graph(fused, reps, trials=3)
+    t_unfused = time_graph(unfused, reps, trials=3)
+    print(json.dumps({"epilogue": spec, "workload": name,
+                      "tile": dg.select_tile(M, N, K, dt, workspace_bytes=workspace.numel()).name,
+                      "plain_gemm_us": round(t_plain, 3), "fused_us": round(t_fused, 3),
+                      "gemm_then_torch_epilogue_us": round(t_unfused, 3),
+                      "timing": f"hipGraph of {reps} calls, median of 3 replays"}), flush=True)
+    return 0
+
+
 def run_graph(name: str, reps: int, copies: int):
     """Decode-size kernels are shorter than a Python launch: time R launches
     captured in one HIP graph."""
@@ -432,6 +506,9 @@ def main(argv=None):
                          "profiles/traffic_<workload>.json for --workload/--tile, and exit")
     ap.add_argument("--eager", action="store_true",
                     help="issue the K timed calls eagerly instead of replaying them from one HIP graph")
+    ap.add_argument("--epilogue", default=None, metavar="PARTS",
+                    help="time the fused epilogue (e.g. silu,mul or gelu,bias or scale_m,scale_n) "
+                         "against the plain GEMM followed by torch elementwise ops")
     ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
                     help="split-K workspace handed to the library (0: no split-K)")
     ap.add_argument("--sweep", action="store_true",
@@ -454,6 +531,8 @@ def main(argv=None):
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
         return sweep(name, args.steps, args.warmup, args.workspace_mib)
+    if args.epilogue is not None:
+        return epilogue_compare(name, args.epilogue, args.steps, args.workspace_mib)
     workspace = (torch.empty(args.workspace_mib << 20, dtype=torch.uint8, device="cuda")
                  if args.workspace_mib > 0 else None)
     # No events between launches: the K calls run back to back (replayed from

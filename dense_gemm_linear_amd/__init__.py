@@ -38,7 +38,19 @@ GEMM_KERNEL_TILED_PP = 3
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
-           "gemm_bf16_ws", "gemm_fp8_scaled_ws")
+           "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex")
+
+# gemm_activation
+GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_SILU, GEMM_ACT_GELU_ERF, GEMM_ACT_GELU_TANH = 0, 1, 2, 3, 4
+ACTIVATIONS = {None: GEMM_ACT_NONE, "none": GEMM_ACT_NONE, "relu": GEMM_ACT_RELU,
+               "silu": GEMM_ACT_SILU, "gelu": GEMM_ACT_GELU_ERF, "gelu_erf": GEMM_ACT_GELU_ERF,
+               "gelu_tanh": GEMM_ACT_GELU_TANH}
+
+
+class GemmEpilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("scale_m", ctypes.c_void_p),
+                ("scale_n", ctypes.c_void_p), ("mul", ctypes.c_void_p),
+                ("ld_mul", ctypes.c_int64), ("activation", ctypes.c_int32)]
 
 
 class GemmTile(ctypes.Structure):
@@ -205,6 +217,13 @@ def _load_lib():
     lib.gemm_fp8_scaled_ws.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
                                        ctypes.POINTER(GemmTile), P, ctypes.c_size_t, P]
     lib.gemm_fp8_scaled_ws.restype = ctypes.c_int
+    lib.gemm_bf16_ex.argtypes = [P, I64, P, P, I64, I64, I64, I64, ctypes.POINTER(GemmTile),
+                                 ctypes.POINTER(GemmEpilogue), P, ctypes.c_size_t, P]
+    lib.gemm_bf16_ex.restype = ctypes.c_int
+    lib.gemm_fp8_scaled_ex.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64,
+                                       ctypes.POINTER(GemmTile), ctypes.POINTER(GemmEpilogue), P,
+                                       ctypes.c_size_t, P]
+    lib.gemm_fp8_scaled_ex.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
@@ -336,15 +355,53 @@ def _workspace(A, N: int, K: int, code: int, tile, workspace):
     return ws.data_ptr(), nbytes
 
 
-def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None, workspace=None):
+def _epilogue(A, N: int, bias, scale_m, scale_n, activation, mul):
+    """The gemm_epilogue struct for the given parts, or None when there are none."""
+    act = ACTIVATIONS[activation] if not isinstance(activation, int) else activation
+    if bias is None and scale_m is None and scale_n is None and mul is None and act == GEMM_ACT_NONE:
+        return None
+    torch = _torch()
+    M = A.shape[0]
+
+    def vec(name, t, n, dtypes):
+        if t.dim() != 1 or t.shape[0] != n or t.stride(0) != 1 or not t.is_cuda or t.dtype not in dtypes:
+            raise ValueError(f"{name} must be a contiguous device vector of {n} {dtypes[0]}")
+        return t.data_ptr()
+    e = GemmEpilogue()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    if bias is not None:
+        e.bias = vec("bias", bias, N, bf)
+    if scale_m is not None:
+        e.scale_m = vec("scale_m", scale_m, M, (torch.float32,))
+    if scale_n is not None:
+        e.scale_n = vec("scale_n", scale_n, N, (torch.float32,))
+    if mul is not None:
+        _check_rows("mul", mul)
+        if tuple(mul.shape) != (M, N) or mul.dtype not in bf:
+            raise ValueError("mul must be a bf16 [M, N] view")
+        e.mul = mul.data_ptr()
+        e.ld_mul = mul.stride(0)
+    e.activation = act
+    return e
+
+
+def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None, workspace=None, *, bias=None,
+              scale_m=None, scale_n=None, activation=None, mul=None):
     """C[M, N] = A[M, K] * B[N, K]^T with Bs = shuffle_b(B); returns C (bf16).
     workspace: a uint8 device tensor for split-K (then tile None lets the
-    library weigh split-K tiles that fit in it)."""
+    library weigh split-K tiles that fit in it).  Fused epilogue (all
+    optional): C = act(acc * scale_m[m] * scale_n[n] + bias[n]) * mul[m, n],
+    activation one of ACTIVATIONS; mul may be `out` itself."""
     _check_rows("A", A)
     C = _out(A, N, out)
     M, K = A.shape
     ws, nbytes = _workspace(A, N, K, GEMM_BF16, tile, workspace)
-    if ws is None:
+    epi = _epilogue(A, N, bias, scale_m, scale_n, activation, mul)
+    if epi is not None:
+        st = lib.gemm_bf16_ex(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0),
+                              M, N, K, _tile_ptr(tile), ctypes.byref(epi), ws, nbytes,
+                              _stream_ptr(A))
+    elif ws is None:
         st = lib.gemm_bf16(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0), M,
                            N, K, _tile_ptr(tile), _stream_ptr(A))
     else:
@@ -356,14 +413,23 @@ def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None, workspace=None)
 
 
 def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None = None,
-                    workspace=None):
+                    workspace=None, *, bias=None, scale_m=None, scale_n=None, activation=None,
+                    mul=None):
     """C = (A * B^T) * scale_a * scale_b for e4m3 A [M, K] and Bs = shuffle_b(B);
-    scale_a / scale_b are one-element float32 device tensors."""
+    scale_a / scale_b are one-element float32 device tensors.  The fused
+    epilogue parts are those of gemm_bf16 (scale_m / scale_n: per-token and
+    per-channel fp32 multipliers)."""
     _check_rows("A", A)
     C = _out(A, N, out)
     M, K = A.shape
     ws, nbytes = _workspace(A, N, K, GEMM_FP8_E4M3, tile, workspace)
-    if ws is None:
+    epi = _epilogue(A, N, bias, scale_m, scale_n, activation, mul)
+    if epi is not None:
+        st = lib.gemm_fp8_scaled_ex(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
+                                    scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
+                                    _tile_ptr(tile), ctypes.byref(epi), ws, nbytes,
+                                    _stream_ptr(A))
+    elif ws is None:
         st = lib.gemm_fp8_scaled(A.data_ptr(), A.stride(0), Bs.data_ptr(), scale_a.data_ptr(),
                                  scale_b.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
                                  _tile_ptr(tile), _stream_ptr(A))

@@ -18,7 +18,14 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdensegemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "select_tile.cpp", "misc.hip", "skinny.hip", "tiled_bf16.hip", "tiled_fp8.hip"]
+# (source, object name, extra defines): tiled_inst.hip is compiled once per
+# (element type, kernel variant, ladder family), so the instances build in
+# parallel translation units
+SOURCES = [("api.cpp", "api", []), ("select_tile.cpp", "select_tile", []), ("misc.hip", "misc", []),
+           ("skinny.hip", "skinny", [])] + \
+    [("tiled_inst.hip", f"tiled_d{d}_m{m}_f{f}",
+      [f"-DDG_INST_DT={d}", f"-DDG_INST_MODE={m}", f"-DDG_INST_FAMILY={f}"])
+     for d in (0, 1) for m in (0, 1, 2) for f in (0, 1)]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
@@ -37,14 +44,16 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
 
-    def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *FLAGS, *extra_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    def compile_one(entry) -> str:
+        src, name, defines = entry
+        obj = os.path.join(BUILD_DIR, name + ".o")
+        cmd = [cc, *FLAGS, *defines, *extra_flags, "-x", "hip", "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+            raise RuntimeError(f"hipcc failed on {name}:\n{r.stdout}\n{r.stderr}")
         if verbose and r.stderr.strip():
             print(r.stderr, file=sys.stderr)
         return obj

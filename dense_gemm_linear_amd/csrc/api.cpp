@@ -7,19 +7,17 @@
 
 namespace dg {
 
-hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s)
+hipError_t launch_tiled_rung(int kernel, int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
-    return dt == DT_BF16 ? launch_ab_bf16(idx, a, s) : launch_ab_fp8(idx, a, s);
-}
-
-hipError_t launch_pp(int dt, int idx, const GemmArgs& a, hipStream_t s)
-{
-    return dt == DT_BF16 ? launch_pp_bf16(idx, a, s) : launch_pp_fp8(idx, a, s);
-}
-
-hipError_t launch_tiled(int dt, int idx, const GemmArgs& a, hipStream_t s)
-{
-    return dt == DT_BF16 ? launch_tiled_bf16(idx, a, s) : launch_tiled_fp8(idx, a, s);
+    const int mode = a.splits > 1 ? MODE_SPLIT : (a.ep.on ? MODE_EPI : MODE_PLAIN);
+    const int fam = kernel == GEMM_KERNEL_TILED ? 0 : 1;
+#define DG_PICK(D, M, F) \
+    if (dt == D && mode == M && fam == F) return launch_inst_##D##_##M##_##F(kernel, idx, a, s);
+    DG_PICK(0, 0, 0) DG_PICK(0, 0, 1) DG_PICK(0, 1, 0) DG_PICK(0, 1, 1) DG_PICK(0, 2, 0)
+    DG_PICK(0, 2, 1) DG_PICK(1, 0, 0) DG_PICK(1, 0, 1) DG_PICK(1, 1, 0) DG_PICK(1, 1, 1)
+    DG_PICK(1, 2, 0) DG_PICK(1, 2, 1)
+#undef DG_PICK
+    return hipErrorInvalidValue;
 }
 
 namespace {
@@ -93,9 +91,33 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
     return *idx >= 0;
 }
 
+// The epilogue's arguments, checked; false if any is invalid.
+bool make_epilogue(const gemm_epilogue* e, int64_t N, Epilogue* out)
+{
+    memset(out, 0, sizeof *out);
+    if (!e)
+        return true;
+    if (e->activation < GEMM_ACT_NONE || e->activation > GEMM_ACT_GELU_TANH)
+        return false;
+    if (((uintptr_t)e->bias & 1u) || ((uintptr_t)e->scale_m & 3u) ||
+        ((uintptr_t)e->scale_n & 3u) || ((uintptr_t)e->mul & 1u))
+        return false;
+    if (e->mul && e->ld_mul < N)
+        return false;
+    out->bias = e->bias;
+    out->scale_m = e->scale_m;
+    out->scale_n = e->scale_n;
+    out->mul = e->mul;
+    out->ldmul = e->mul ? e->ld_mul : 0;
+    out->act = e->activation;
+    out->on = e->bias || e->scale_m || e->scale_n || e->mul || e->activation != GEMM_ACT_NONE;
+    return true;
+}
+
 gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const float* sa,
                      const float* sb, uint16_t* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                     const gemm_tile* tile, void* ws, size_t ws_bytes, void* stream)
+                     const gemm_tile* tile, const gemm_epilogue* epi, void* ws, size_t ws_bytes,
+                     void* stream)
 {
     const int e = dt == DT_BF16 ? 2 : 1;
     // ---- argument checks (no HIP call before this block ends)
@@ -112,6 +134,9 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         ((uintptr_t)C & 1u) != 0)
         return GEMM_ERR_INVALID_VALUE;
     if (ws_bytes > 0 && (!ws || !aligned16(ws)))
+        return GEMM_ERR_INVALID_VALUE;
+    Epilogue ep;
+    if (!make_epilogue(epi, N, &ep))
         return GEMM_ERR_INVALID_VALUE;
     if (K % (dt == DT_BF16 ? 16 : 64) != 0)
         return GEMM_ERR_UNSUPPORTED;
@@ -140,7 +165,7 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (K == 0)
-        return launch_zero_c(C, ldc, M, N, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+        return launch_zero_c(C, ldc, M, N, ep, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     if (!tile) {
         choose_tile(M, N, K, dt, cus, ws_bytes, &t);
         if (!resolve_tile(t, M, e, &idx))
@@ -170,17 +195,16 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     a.kt_per = pl.kt_per;
     a.ldw = pl.ldw;
     a.ws = pl.S > 1 ? static_cast<float*>(ws) : nullptr;
+    a.ep = ep;
     hipError_t err;
     if (t.kernel == GEMM_KERNEL_SKINNY) {
         err = launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
     } else {
         a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
         a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
-        err = t.kernel == GEMM_KERNEL_TILED_AB   ? launch_ab(dt, idx, a, s)
-              : t.kernel == GEMM_KERNEL_TILED_PP ? launch_pp(dt, idx, a, s)
-                                                 : launch_tiled(dt, idx, a, s);
+        err = launch_tiled_rung(t.kernel, dt, idx, a, s);
         if (err == hipSuccess && pl.S > 1)
-            err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, s);
+            err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, ep, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -194,7 +218,7 @@ gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* 
                       int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* stream)
 {
     return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, nullptr,
-                        0, stream);
+                        nullptr, 0, stream);
 }
 
 gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const float* scale_a,
@@ -202,14 +226,14 @@ gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const
                             int64_t K, const gemm_tile* tile, void* stream)
 {
     return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, nullptr,
-                        0, stream);
+                        nullptr, 0, stream);
 }
 
 gemm_status gemm_bf16_ws(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
                          int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* workspace,
                          size_t workspace_bytes, void* stream)
 {
-    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile,
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, nullptr,
                         workspace, workspace_bytes, stream);
 }
 
@@ -219,7 +243,26 @@ gemm_status gemm_fp8_scaled_ws(const uint8_t* A, int64_t lda, const void* Bs,
                                const gemm_tile* tile, void* workspace, size_t workspace_bytes,
                                void* stream)
 {
-    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile,
+    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, nullptr,
+                        workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_bf16_ex(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, const gemm_tile* tile,
+                         const gemm_epilogue* epilogue, void* workspace, size_t workspace_bytes,
+                         void* stream)
+{
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, epilogue,
+                        workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_fp8_scaled_ex(const uint8_t* A, int64_t lda, const void* Bs,
+                               const float* scale_a, const float* scale_b, uint16_t* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               const gemm_tile* tile, const gemm_epilogue* epilogue,
+                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    return dg::run_gemm(dg::DT_FP8, A, lda, Bs, scale_a, scale_b, C, ldc, M, N, K, tile, epilogue,
                         workspace, workspace_bytes, stream);
 }
 

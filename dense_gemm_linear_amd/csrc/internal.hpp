@@ -95,17 +95,20 @@ bool skinny_supported(int tm, int tn, int waves);
 // Launchers: return hipSuccess or the launch error.  Grids are computed from
 // the arguments; shapes are validated by the caller.
 // Launch rung `idx` of the tiled / AB ladder.
-hipError_t launch_tiled(int dt, int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_bf16(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_tiled_fp8(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab(int dt, int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_bf16(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_ab_fp8(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_pp(int dt, int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_pp_bf16(int idx, const GemmArgs& a, hipStream_t s);
-hipError_t launch_pp_fp8(int idx, const GemmArgs& a, hipStream_t s);
+// Tiled-kernel launchers, one per (element type, MODE_*, family) instance
+// file (tiled_inst.hip): family 0 is the tiled ladder, 1 the A+B and
+// ping-pong ladders (`kernel` picks which); idx is the rung's index.
+#define DG_DECL_INST(D, M, F) \
+    hipError_t launch_inst_##D##_##M##_##F(int kernel, int idx, const GemmArgs& a, hipStream_t s);
+DG_DECL_INST(0, 0, 0) DG_DECL_INST(0, 0, 1) DG_DECL_INST(0, 1, 0) DG_DECL_INST(0, 1, 1)
+DG_DECL_INST(0, 2, 0) DG_DECL_INST(0, 2, 1) DG_DECL_INST(1, 0, 0) DG_DECL_INST(1, 0, 1)
+DG_DECL_INST(1, 1, 0) DG_DECL_INST(1, 1, 1) DG_DECL_INST(1, 2, 0) DG_DECL_INST(1, 2, 1)
+#undef DG_DECL_INST
+// rung idx of `kernel` (tiled, A+B or ping-pong) for element type dt, in the
+// variant the arguments ask for (split-K, fused epilogue, or plain)
+hipError_t launch_tiled_rung(int kernel, int dt, int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
-hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s);
+hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, Epilogue ep, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
                             int64_t KB, int aligned, hipStream_t s);
 
@@ -140,7 +143,8 @@ int rung_ktb(int kernel, int idx);
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
                  gemm_tile* out);
 hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,
-                                int64_t ldc, const float* sa, const float* sb, hipStream_t s);
+                                int64_t ldc, const float* sa, const float* sb, Epilogue ep,
+                                hipStream_t s);
 // Split-K addresses a partial plane with 32-bit byte offsets, also for the
 // up to 256 rows a tile reaches past M (their stores are dropped by the
 // buffer bound): (M + 256) * ldw * 4 must stay within 2 GiB.

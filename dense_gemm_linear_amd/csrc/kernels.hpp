@@ -34,6 +34,95 @@
 namespace dg {
 
 enum { DT_BF16 = 0, DT_FP8 = 1 };
+// Kernel variants: one-pass with a plain bf16 epilogue, split-K (fp32
+// partials, the epilogue runs in the reduction), one-pass with the fused
+// epilogue.  Separate instances, so that no variant pays for another's code
+// in registers.
+enum { MODE_PLAIN = 0, MODE_SPLIT = 1, MODE_EPI = 2 };
+// activation codes (the values of gemm_activation)
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2, ACT_GELU_ERF = 3, ACT_GELU_TANH = 4 };
+
+// Fused epilogue, applied per output element in fp32 after the e4m3
+// per-tensor scales: v *= scale_m[row]; v *= scale_n[col]; v += bias[col];
+// v = act(v); v *= mul[row][col]; then bf16 rounding.  Every part is
+// optional (null pointer, ACT_NONE); `on` is set when any part is present.
+struct Epilogue {
+    const uint16_t* bias;    // bf16 [N]
+    const float* scale_m;    // fp32 [M]: per-row (per-token) multiplier
+    const float* scale_n;    // fp32 [N]: per-column (per-channel) multiplier
+    const uint16_t* mul;     // bf16 [M, ldmul]
+    int64_t ldmul;
+    int act;
+    int on;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// Activations from exponentials and reciprocals (the epilogue is unrolled
+// over every accumulator element, so the code per element must stay small).  SiLU is x * logistic(x); the tanh form of GELU is x * logistic(2u),
+// u = sqrt(2/pi) (x + 0.044715 x^3), since (1 + tanh u) / 2 = logistic(2u);
+// the erf form is x * Phi(x) with erf from Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7, far below
+// bf16 rounding): erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2),
+// t = 1 / (1 + p z), z >= 0, odd in z.
+// Activation classes, so that a launch evaluates only what its activation
+// needs (the class is fixed per launch; inside a class the code is
+// branch-free, so the unrolled epilogue has no per-element control flow):
+//   0: none, ReLU; 1: SiLU, tanh-form GELU (one exponential, one reciprocal);
+//   2: erf-form GELU.
+__device__ __forceinline__ int act_class(int act)
+{
+    return act == ACT_GELU_ERF ? 2 : (act == ACT_SILU || act == ACT_GELU_TANH) ? 1 : 0;
+}
+
+template <int C>
+__device__ __forceinline__ float activate_c(int act, float x)
+{
+    if constexpr (C == 0) {
+        return act == ACT_RELU ? fmaxf(x, 0.f) : x;
+    } else if constexpr (C == 1) {
+        const float z = act == ACT_GELU_TANH ? 1.5957691216057308f * (x + 0.044715f * x * x * x) : x;
+        return x * __frcp_rn(1.f + __expf(-z));
+    } else {
+        const float a = fabsf(x) * 0.70710678118654752f;
+        const float t = __frcp_rn(1.f + 0.3275911f * a);
+        const float poly =
+            t * (0.254829592f +
+                 t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+        return 0.5f * x * (1.f + copysignf(1.f - poly * __expf(-a * a), x));
+    }
+}
+
+__device__ __forceinline__ float activate(int act, float x)
+{
+    switch (act_class(act)) {
+    case 1:
+        return activate_c<1>(act, x);
+    case 2:
+        return activate_c<2>(act, x);
+    default:
+        return activate_c<0>(act, x);
+    }
+}
+
+// The epilogue of element (row, col); both must lie inside M x N (callers
+// clamp the padding elements they compute but never store).
+__device__ __forceinline__ float apply_epilogue(const Epilogue& ep, float v, int row, int col)
+{
+    if (ep.scale_m)
+        v *= ep.scale_m[row];
+    if (ep.scale_n)
+        v *= ep.scale_n[col];
+    if (ep.bias)
+        v += bf16_to_f32(ep.bias[col]);
+    v = activate(ep.act, v);
+    if (ep.mul)
+        v *= bf16_to_f32(ep.mul[(int64_t)row * ep.ldmul + col]);
+    return v;
+}
 
 // Tile rows per raster group, and whether workgroups are renumbered per XCD.
 #ifndef DG_GROUP_M
@@ -71,6 +160,7 @@ struct GemmArgs {
     int kt_per;           // k-tiles per slice, in the kernel's own k-tile size
     int ldw;
     float* ws;
+    Epilogue ep;
 };
 
 // The K range of one workgroup: k-tiles [kt0, kt0 + n) of KTB bytes, and the
@@ -269,6 +359,19 @@ __device__ __forceinline__ ADma a_dma_lane(int chunk, int lane, int64_t lda_b)
     return {row * (uint32_t)lda_b + col * 16, col * 16};
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded
+// at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Epilogue shared by the tiled kernels: scale (e4m3), round to bf16, stage a
 // wave's (MR*R) x (NR*R) accumulator block through its private LDS region
 // CH atom rows at a time, and store 16-byte row pieces ("GEMM Optimization
@@ -280,7 +383,7 @@ __device__ __forceinline__ ADma a_dma_lane(int chunk, int lane, int64_t lda_b)
 // address, so that all but one of its 16-byte pieces are aligned stores; the
 // one piece that straddles the segment ends (sh elements at the head, 8 - sh
 // at the tail) is written element by element.
-template <int DT, class AT, int MR, int NR, int CH, int SROW, int WCOLS>
+template <int DT, class AT, int MR, int NR, int CH, int SROW, int WCOLS, bool EPI>
 __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                                              const typename AT::acc_t (&acc)[MR][NR],
                                              uint8_t* stage, int m0, int rows, int col_w, int row0,
@@ -296,78 +399,136 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
     const uint32_t base_ph =
         (uint32_t)((((uintptr_t)p.C) >> 1) + (uint64_t)m0 * (uint64_t)p.ldc + (uint32_t)col_w) & 7u;
     const uint32_t ldc_ph = (uint32_t)p.ldc & 7u;
+    // Fused epilogue operands.  A lane's columns are the same for every
+    // element of accumulator column j, so the column scale and bias are
+    // loaded once per tile; row scales once per accumulator row; the
+    // multiplier as one batch of NACC loads before its values are used.
+    // (Loaded element by element between the LDS staging stores, each load
+    // waited for its own round trip.)  Indices past M or N are clamped: those
+    // elements are computed but never stored.
+    float col_scale[NR], col_bias[NR];
+    if constexpr (EPI) {
 #pragma unroll
-    for (int cc = 0; cc < MR / CH; ++cc) {
+        for (int j = 0; j < NR; ++j) {
+            const int col = min(col_w + j * R + lc, p.N - 1);
+            col_scale[j] = p.ep.scale_n ? p.ep.scale_n[col] : 1.f;
+            col_bias[j] = p.ep.bias ? bf16_to_f32(p.ep.bias[col]) : 0.f;
+        }
+    }
+    // chunks expanded at compile time: with a large epilogue the unroller
+    // may keep this loop (it holds a barrier), and a run-time chunk index
+    // would put the accumulators in scratch memory
+    auto chunks = [&](auto cls_c) __attribute__((always_inline)) {
+        constexpr int CLS = decltype(cls_c)::value;
+        static_for<MR / CH>([&](auto cc_c) __attribute__((always_inline)) {
+            constexpr int cc = decltype(cc_c)::value;
 #pragma unroll
-        for (int ml = 0; ml < CH; ++ml)
+            for (int ml = 0; ml < CH; ++ml) {
+                float row_scale[AT::NACC];
+                int grow[AT::NACC];
+                if constexpr (EPI) {
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
-#pragma unroll
-                for (int e = 0; e < AT::NACC; ++e) {
-                    float v = acc[cc * CH + ml][j][e];
-                    if constexpr (DT == DT_FP8)
-                        v = (v * scale_a) * scale_b;
-                    const int row = ml * R + AT::out_row(e, lane);
-                    const int col = j * R + lc;
-                    *reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2) = bf16_rne(v);
-                }
-        __syncthreads();
-#pragma unroll
-        for (int q0 = 0; q0 < PIECES; q0 += 64) {
-            const int q = q0 + lane;
-            if (PIECES % 64 == 0 || q < PIECES) {
-                const int prow = q / PPR, pc = q % PPR;
-                const int trow = row0 + cc * CH * R + prow;   // row within the tile
-                const uint32_t row_off = (uint32_t)((int64_t)trow * p.ldc + col_w);  // elements
-                const uint8_t* srow = stage + prow * SROW;
-                // elements before the row segment's first 16-byte boundary
-                const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
-                if (p.c_vec || sh == 0 || pc < PPR - 1) {
-                    const int o = (p.c_vec ? 0 : sh) + 8 * pc;     // staged column of the piece
-                    i32x4 v;
-                    if (p.c_vec || sh == 0) {
-                        v = *reinterpret_cast<const i32x4*>(srow + o * 2);
-                    } else {
-                        // 8 bf16 from a 2-byte aligned LDS offset: 5 dwords, funnel-shifted
-                        const uint32_t* d = reinterpret_cast<const uint32_t*>(srow + (o & ~1) * 2);
-                        const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
-                        const int odd = o & 1;
-                        v[0] = (int)(odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0);
-                        v[1] = (int)(odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1);
-                        v[2] = (int)(odd ? __builtin_amdgcn_alignbit(w3, w2, 16) : w2);
-                        v[3] = (int)(odd ? __builtin_amdgcn_alignbit(w4, w3, 16) : w3);
+                    for (int e = 0; e < AT::NACC; ++e) {
+                        grow[e] = min(m0 + row0 + (cc * CH + ml) * R + AT::out_row(e, lane), p.M - 1);
+                        row_scale[e] = p.ep.scale_m ? p.ep.scale_m[grow[e]] : 1.f;
                     }
-                    const int gcol = col_w + o;
-                    const uint32_t off = (row_off + (uint32_t)o) * 2u;
-                    if (gcol + 8 <= p.N) {
-                        store16(rc, off, v);
-                    } else {
+                }
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (gcol + e < p.N)
-                                store2(rc, off + 2 * e,
-                                       (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1))));
+                for (int j = 0; j < NR; ++j) {
+                    float mulv[AT::NACC];
+                    if constexpr (EPI) {
+                        const int col = min(col_w + j * R + lc, p.N - 1);
+#pragma unroll
+                        for (int e = 0; e < AT::NACC; ++e)
+                            mulv[e] = p.ep.mul ? bf16_to_f32(p.ep.mul[(int64_t)grow[e] * p.ep.ldmul + col])
+                                               : 1.f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < AT::NACC; ++e) {
+                        float v = acc[cc * CH + ml][j][e];
+                        if constexpr (DT == DT_FP8)
+                            v = (v * scale_a) * scale_b;
+                        if constexpr (EPI) {
+                            v = v * row_scale[e];
+                            v = v * col_scale[j];
+                            v = v + col_bias[j];
+                            v = activate_c<CLS>(p.ep.act, v) * mulv[e];
+                        }
+                        const int row = ml * R + AT::out_row(e, lane);
+                        const int col = j * R + lc;
+                        *reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2) = bf16_rne(v);
                     }
                 }
             }
-        }
-        if (!p.c_vec) {
-            // The straddling piece of every row: head [0, sh) and tail
-            // [sh + 8 (PPR-1), WCOLS), one element per lane per store.
-            constexpr int ELEMS = CH * R * 8;
+            __syncthreads();
 #pragma unroll
-            for (int u0 = 0; u0 < ELEMS; u0 += 64) {
-                const int u = u0 + lane;
-                const int prow = u >> 3, e = u & 7;
-                const int trow = row0 + cc * CH * R + prow;
-                const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
-                const int col = e < sh ? e : sh + 8 * (PPR - 1) + (e - sh);
-                if (sh != 0 && col_w + col < p.N)
-                    store2(rc, ((uint32_t)((int64_t)trow * p.ldc + col_w) + (uint32_t)col) * 2u,
-                           *reinterpret_cast<const uint16_t*>(stage + prow * SROW + col * 2));
+            for (int q0 = 0; q0 < PIECES; q0 += 64) {
+                const int q = q0 + lane;
+                if (PIECES % 64 == 0 || q < PIECES) {
+                    const int prow = q / PPR, pc = q % PPR;
+                    const int trow = row0 + cc * CH * R + prow;   // row within the tile
+                    const uint32_t row_off = (uint32_t)((int64_t)trow * p.ldc + col_w);  // elements
+                    const uint8_t* srow = stage + prow * SROW;
+                    // elements before the row segment's first 16-byte boundary
+                    const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
+                    if (p.c_vec || sh == 0 || pc < PPR - 1) {
+                        const int o = (p.c_vec ? 0 : sh) + 8 * pc;     // staged column of the piece
+                        i32x4 v;
+                        if (p.c_vec || sh == 0) {
+                            v = *reinterpret_cast<const i32x4*>(srow + o * 2);
+                        } else {
+                            // 8 bf16 from a 2-byte aligned LDS offset: 5 dwords, funnel-shifted
+                            const uint32_t* d = reinterpret_cast<const uint32_t*>(srow + (o & ~1) * 2);
+                            const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
+                            const int odd = o & 1;
+                            v[0] = (int)(odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0);
+                            v[1] = (int)(odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1);
+                            v[2] = (int)(odd ? __builtin_amdgcn_alignbit(w3, w2, 16) : w2);
+                            v[3] = (int)(odd ? __builtin_amdgcn_alignbit(w4, w3, 16) : w3);
+                        }
+                        const int gcol = col_w + o;
+                        const uint32_t off = (row_off + (uint32_t)o) * 2u;
+                        if (gcol + 8 <= p.N) {
+                            store16(rc, off, v);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (gcol + e < p.N)
+                                    store2(rc, off + 2 * e,
+                                           (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1))));
+                        }
+                    }
+                }
             }
-        }
-        __syncthreads();
+            if (!p.c_vec) {
+                // The straddling piece of every row: head [0, sh) and tail
+                // [sh + 8 (PPR-1), WCOLS), one element per lane per store.
+                constexpr int ELEMS = CH * R * 8;
+#pragma unroll
+                for (int u0 = 0; u0 < ELEMS; u0 += 64) {
+                    const int u = u0 + lane;
+                    const int prow = u >> 3, e = u & 7;
+                    const int trow = row0 + cc * CH * R + prow;
+                    const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
+                    const int col = e < sh ? e : sh + 8 * (PPR - 1) + (e - sh);
+                    if (sh != 0 && col_w + col < p.N)
+                        store2(rc, ((uint32_t)((int64_t)trow * p.ldc + col_w) + (uint32_t)col) * 2u,
+                               *reinterpret_cast<const uint16_t*>(stage + prow * SROW + col * 2));
+                }
+            }
+            __syncthreads();
+        });
+    };
+    if constexpr (EPI) {
+        const int cls = act_class(p.ep.act);
+        if (cls == 1)
+            chunks(std::integral_constant<int, 1>{});
+        else if (cls == 2)
+            chunks(std::integral_constant<int, 2>{});
+        else
+            chunks(std::integral_constant<int, 0>{});
+    } else {
+        chunks(std::integral_constant<int, 0>{});
     }
 }
 
@@ -595,7 +756,7 @@ struct TiledShape {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int ST, int R, int KTB, bool SPLIT>
+template <int DT, int TM, int TN, int WM, int ST, int R, int KTB, int MODE>
 __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 {
     using S = TiledShape<TM, TN, WM, ST, R, KTB>;
@@ -613,12 +774,12 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;     // wave row (M) and column (N)
     int wg, tm, tn;
-    const int slice = split_slice<SPLIT>(p, wg);
+    const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
     tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const KRange kr = k_range<KTB, SPLIT>(p, slice);
+    const KRange kr = k_range<KTB, MODE == MODE_SPLIT>(p, slice);
 
     // Descriptors rebased at this tile: rows past M and 16-column blocks past
     // ceil(N/16) fall outside and read as zero.
@@ -702,7 +863,7 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     };
     k_loop<ST, STEPS, S::LOADS, MR * NR, MR * P>(kr.n, load, read, mma);
 
-    if constexpr (SPLIT) {
+    if constexpr (MODE == MODE_SPLIT) {
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
         return;
     }
@@ -711,7 +872,7 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS, MODE == MODE_EPI>(
         p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
         scale_a, scale_b);
 }
@@ -752,7 +913,7 @@ struct ABShape {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int TM, int TN, int WM, int WN, int ST, int R, int KTB, bool SPLIT>
+template <int DT, int TM, int TN, int WM, int WN, int ST, int R, int KTB, int MODE>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 {
     using S = ABShape<TM, TN, WM, WN, ST, R, KTB>;
@@ -771,12 +932,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     const int wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int wg, tm, tn;
-    const int slice = split_slice<SPLIT>(p, wg);
+    const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
     tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const KRange kr = k_range<KTB, SPLIT>(p, slice);
+    const KRange kr = k_range<KTB, MODE == MODE_SPLIT>(p, slice);
     const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
                                 (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
     const int nb0 = n0 >> 4;
@@ -869,7 +1030,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     };
     k_loop<ST, STEPS, S::LOADS, MR * NR, (MR + NR) * P>(kr.n, load, read, mma);
 
-    if constexpr (SPLIT) {
+    if constexpr (MODE == MODE_SPLIT) {
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
         return;
     }
@@ -878,7 +1039,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS, MODE == MODE_EPI>(
         p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
         scale_a, scale_b);
 }
@@ -903,7 +1064,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 // k-tile t must have landed (each wave: at most (ST-2) x LOADS of its loads
 // still in flight); at the end of half 2t only group 1 needs that much (its
 // next read is k-tile t, already complete), group 0 none.
-template <int DT, int TM, int TN, int ST, int R, int KTB, bool SPLIT>
+template <int DT, int TM, int TN, int ST, int R, int KTB, int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 {
     using S = ABShape<TM, TN, 2, 4, ST, R, KTB>;
@@ -924,12 +1085,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
     const int wm = wave >> 2, wn = wave & 3;     // wm = the group
     const bool g0 = wm == 0;
     int wg, tm, tn;
-    const int slice = split_slice<SPLIT>(p, wg);
+    const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
     tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * TM;
     const int n0 = tn * TN;
     const int rows = min(TM, p.M - m0);
-    const KRange kr = k_range<KTB, SPLIT>(p, slice);
+    const KRange kr = k_range<KTB, MODE == MODE_SPLIT>(p, slice);
     const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
                                 (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
     const int nb0 = n0 >> 4;
@@ -1055,7 +1216,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __syncthreads();
 
-    if constexpr (SPLIT) {
+    if constexpr (MODE == MODE_SPLIT) {
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
         return;
     }
@@ -1064,7 +1225,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
         scale_a = *p.sa;
         scale_b = *p.sb;
     }
-    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS>(
+    store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS, MODE == MODE_EPI>(
         p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
         scale_a, scale_b);
 }
@@ -1077,7 +1238,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 // once per batch), and reads A straight from global (small; it stays in L2).
 // Partial sums are reduced in LDS in a fixed order: deterministic, no
 // workspace.
-template <int DT, int MR, int NB, int W>
+template <int DT, int MR, int NB, int W, bool EPI>
 __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs p)
 {
     constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);   // k-tiles per batch
@@ -1193,6 +1354,8 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs p)
                     float v = s[i];
                     if constexpr (DT == DT_FP8)
                         v = (v * scale_a) * scale_b;
+                    if constexpr (EPI)
+                        v = apply_epilogue(p.ep, v, row, col);
                     p.C[(int64_t)row * p.ldc + col] = bf16_rne(v);
                 }
             }

@@ -38,11 +38,15 @@ __global__ __launch_bounds__(256) void shuffle_b_kernel(const uint8_t* B, int64_
     *reinterpret_cast<i32x4*>(Bs + u * 16) = v;
 }
 
-__global__ __launch_bounds__(256) void zero_c_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N)
+// K == 0: the empty sum is 0; with an epilogue, C = bf16(epilogue(0)).
+__global__ __launch_bounds__(256) void zero_c_kernel(uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                                                     Epilogue ep)
 {
     const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
-        C[(i / N) * ldc + (i % N)] = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / N, col = i % N;
+        C[row * ldc + col] = ep.on ? bf16_rne(apply_epilogue(ep, 0.f, (int)row, (int)col)) : 0;
+    }
 }
 
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
@@ -55,12 +59,12 @@ hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_
                            dim3(256), args, 0, s);
 }
 
-hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t s)
+hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, Epilogue ep, hipStream_t s)
 {
     int64_t blocks = (M * N + 255) / 256;
     if (blocks > 65536)
         blocks = 65536;
-    void* args[] = {&C, &ldc, &M, &N};
+    void* args[] = {&C, &ldc, &M, &N, &ep};
     return hipLaunchKernel(reinterpret_cast<const void*>(&zero_c_kernel), dim3((unsigned)blocks),
                            dim3(256), args, 0, s);
 }
@@ -74,7 +78,7 @@ hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStre
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int splits, int M,
                                                             int N, int ldw, uint16_t* C,
                                                             int64_t ldc, const float* sa,
-                                                            const float* sb)
+                                                            const float* sb, Epilogue ep)
 {
     const int q = ldw >> 2;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -103,6 +107,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int
         float v = acc[e];
         if (sa)
             v = (v * scale_a) * scale_b;
+        if (ep.on)
+            v = apply_epilogue(ep, v, row, min(c0 + e, N - 1));
         h[e] = bf16_rne(v);
     }
     uint16_t* dst = C + (int64_t)row * ldc + c0;
@@ -118,11 +124,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int
 }
 
 hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,
-                                int64_t ldc, const float* sa, const float* sb, hipStream_t s)
+                                int64_t ldc, const float* sa, const float* sb, Epilogue ep,
+                                hipStream_t s)
 {
     const int64_t threads = (int64_t)M * (ldw / 4);
     const int64_t blocks = (threads + 255) / 256;
-    void* args[] = {&ws, &splits, &M, &N, &ldw, &C, &ldc, &sa, &sb};
+    void* args[] = {&ws, &splits, &M, &N, &ldw, &C, &ldc, &sa, &sb, &ep};
     return hipLaunchKernel(reinterpret_cast<const void*>(&splitk_reduce_kernel),
                            dim3((unsigned)blocks), dim3(256), args, 0, s);
 }

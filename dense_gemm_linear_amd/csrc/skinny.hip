@@ -7,7 +7,9 @@ template <int DT, int MR, int NB, int W>
 hipError_t go(const GemmArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((a.nblk + NB - 1) / NB));
-    return launch_args(&gemm_skinny_kernel<DT, MR, NB, W>, grid, dim3(64 * W), a, s);
+    if (a.ep.on)
+        return launch_args(&gemm_skinny_kernel<DT, MR, NB, W, true>, grid, dim3(64 * W), a, s);
+    return launch_args(&gemm_skinny_kernel<DT, MR, NB, W, false>, grid, dim3(64 * W), a, s);
 }
 
 template <int DT>

@@ -1,0 +1,74 @@
+// Instantiations of the tiled kernels for one (element type, variant,
+// family), chosen by the build: DG_INST_DT (DT_BF16 / DT_FP8), DG_INST_MODE
+// (MODE_PLAIN / MODE_SPLIT / MODE_EPI) and DG_INST_FAMILY (0: the tiled
+// ladder, 1: the A+B and ping-pong ladders).  The build compiles this file
+// once per combination, in parallel; each defines launch_inst_<dt>_<mode>_<family>,
+// which launches rung idx of its ladders.
+#include "internal.hpp"
+
+#if !defined(DG_INST_DT) || !defined(DG_INST_MODE) || !defined(DG_INST_FAMILY)
+#error "tiled_inst.hip is compiled with -DDG_INST_DT, -DDG_INST_MODE and -DDG_INST_FAMILY"
+#endif
+
+#define DG_INST_PASTE_(d, m, f) launch_inst_##d##_##m##_##f
+#define DG_INST_PASTE(d, m, f) DG_INST_PASTE_(d, m, f)
+#define DG_INST_FN DG_INST_PASTE(DG_INST_DT, DG_INST_MODE, DG_INST_FAMILY)
+
+namespace dg {
+namespace {
+constexpr int DT = DG_INST_DT;
+constexpr int MODE = DG_INST_MODE;
+
+// split-K: tiles x slices workgroups
+dim3 grid_of(const GemmArgs& a)
+{
+    return dim3((unsigned)(a.tiles_m * a.tiles_n * (MODE == MODE_SPLIT ? a.splits : 1)));
+}
+
+#if DG_INST_FAMILY == 0
+template <int TM, int TN, int WM, int ST, int R, int KTB>
+hipError_t go(const GemmArgs& a, hipStream_t s)
+{
+    return launch_args(&gemm_tiled_kernel<DT, TM, TN, WM, ST, R, KTB, MODE>, grid_of(a),
+                       dim3(TiledShape<TM, TN, WM, ST, R, KTB>::THREADS), a, s);
+}
+#else
+template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
+hipError_t go_ab(const GemmArgs& a, hipStream_t s)
+{
+    return launch_args(&gemm_ab_kernel<DT, TM, TN, WM, WN, ST, R, KTB, MODE>, grid_of(a),
+                       dim3(ABShape<TM, TN, WM, WN, ST, R, KTB>::THREADS), a, s);
+}
+template <int TM, int TN, int ST, int R, int KTB>
+hipError_t go_pp(const GemmArgs& a, hipStream_t s)
+{
+    return launch_args(&gemm_pp_kernel<DT, TM, TN, ST, R, KTB, MODE>, grid_of(a), dim3(512), a, s);
+}
+#endif
+}  // namespace
+
+hipError_t DG_INST_FN(int kernel, int idx, const GemmArgs& a, hipStream_t s)
+{
+    int i = 0;
+#if DG_INST_FAMILY == 0
+    (void)kernel;
+#define DG_CASE(M_, N_, W_, ST_, R_, KTB_) \
+    if (idx == i++) return go<M_, N_, W_ / 4, ST_, R_, KTB_>(a, s);
+    DG_TILED_LADDER(DG_CASE)
+#undef DG_CASE
+#else
+    if (kernel == GEMM_KERNEL_TILED_AB) {
+#define DG_CASE(M_, N_, WM_, WN_, ST_, R_, KTB_) \
+    if (idx == i++) return go_ab<M_, N_, WM_, WN_, ST_, R_, KTB_>(a, s);
+        DG_AB_LADDER(DG_CASE)
+#undef DG_CASE
+    } else {
+#define DG_CASE(M_, N_, ST_, R_, KTB_) \
+    if (idx == i++) return go_pp<M_, N_, ST_, R_, KTB_>(a, s);
+        DG_PP_LADDER(DG_CASE)
+#undef DG_CASE
+    }
+#endif
+    return hipErrorInvalidValue;
+}
+}  // namespace dg

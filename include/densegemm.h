@@ -99,6 +99,50 @@ typedef enum {
  *     s (a fixed order: the result is the same on every run), scales (e4m3)
  *     and rounds to bf16.  It needs the *_ws entry points.
  */
+/* Activation of the fused epilogue (see gemm_epilogue). */
+typedef enum {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,       /* max(x, 0) */
+    GEMM_ACT_SILU = 2,       /* x / (1 + exp(-x)) */
+    GEMM_ACT_GELU_ERF = 3,   /* x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) */
+    GEMM_ACT_GELU_TANH = 4   /* x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */
+} gemm_activation;
+
+/*
+ * gemm_epilogue -- work fused into the GEMM's output stage (optional parts;
+ * NULL / GEMM_ACT_NONE leave a part out).  For output element (m, n), after
+ * the fp32 sum (and, for e4m3, its per-tensor scales sa, sb):
+ *     v = v * scale_m[m]            per-row (per-token) fp32 multiplier
+ *     v = v * scale_n[n]            per-column (per-channel) fp32 multiplier
+ *     v = v + bias[n]               bf16 bias
+ *     v = act(v)                    activation
+ *     v = v * mul[m][n]             bf16 elementwise multiplier, e.g. the "up"
+ *                                   projection for SiLU(gate) * up
+ *     C[m][n] = bf16 round-to-nearest-even of v
+ * all in fp32.  The Funlib GEMM page lists fused bias and activation as the
+ * way to cut intermediate memory traffic (its feed-forward block applies
+ * GELU between two GEMMs); the "GEMM Optimization Guide" page counts
+ * per-token fp32 scales for M and N in its fp8 byte model (section 8.2); the
+ * TraceLens GEMM page's GPT-3-XL table has an addmm with bias.
+ *
+ *   bias     device bf16 [N], 2-byte aligned
+ *   scale_m  device fp32 [M], 4-byte aligned
+ *   scale_n  device fp32 [N], 4-byte aligned
+ *   mul      device bf16 [M, ld_mul], ld_mul >= N, 2-byte aligned; it may be
+ *            C itself (same pointer and ld_mul == ldc: C = act(...) * C in
+ *            place); any other overlap with C is undefined
+ *   activation  a gemm_activation
+ * All are read-only for the call and owned by the caller.
+ */
+typedef struct {
+    const uint16_t* bias;
+    const float* scale_m;
+    const float* scale_n;
+    const uint16_t* mul;
+    int64_t ld_mul;
+    int32_t activation;
+} gemm_epilogue;
+
 typedef struct {
     int32_t kernel;      /* gemm_kernel */
     int32_t tile_m;
@@ -261,6 +305,24 @@ gemm_status gemm_fp8_scaled_ws(const uint8_t* A, int64_t lda, const void* Bs,
                                int64_t ldc, int64_t M, int64_t N, int64_t K,
                                const gemm_tile* tile, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * gemm_bf16_ex / gemm_fp8_scaled_ex -- the *_ws entry points with a fused
+ * epilogue (gemm_epilogue; NULL = none, the same as *_ws).  K == 0 gives
+ * C = bf16(epilogue(0)).
+ *
+ * Errors as for *_ws, plus INVALID_VALUE for an activation outside
+ * gemm_activation, misaligned epilogue pointers, mul with ld_mul < N.
+ */
+gemm_status gemm_bf16_ex(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, const gemm_tile* tile,
+                         const gemm_epilogue* epilogue, void* workspace, size_t workspace_bytes,
+                         void* stream);
+gemm_status gemm_fp8_scaled_ex(const uint8_t* A, int64_t lda, const void* Bs,
+                               const float* scale_a, const float* scale_b, uint16_t* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               const gemm_tile* tile, const gemm_epilogue* epilogue,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gemm_tile_check -- would `tile`, forced on gemm_bf16 (dtype GEMM_BF16) or

@@ -56,6 +56,10 @@ def _load():
     lib.orc_gemm_points.argtypes = [ctypes.c_int, P, I64, P, I64, I64, ctypes.c_double,
                                     P, P, I64, P]
     lib.orc_gemm_points.restype = None
+    lib.orc_activation.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.orc_activation.restype = ctypes.c_double
+    lib.orc_epilogue.argtypes = [P, I64, I64, P, P, P, ctypes.c_int, P, I64]
+    lib.orc_epilogue.restype = None
     lib.orc_shuffle_b_bytes.argtypes = [I64, I64, ctypes.c_int]
     lib.orc_shuffle_b_bytes.restype = I64
     lib.orc_shuffle_b.argtypes = [P, I64, I64, I64, ctypes.c_int, P]
@@ -191,3 +195,30 @@ def dim_eff(M: int, N: int, mt_m: int, mt_n: int, num_cus: int):
     _load().orc_dim_eff(M, N, mt_m, mt_n, num_cus, ctypes.addressof(t), ctypes.addressof(te),
                         ctypes.addressof(we), ctypes.addressof(de))
     return t.value, te.value, we.value, de.value
+
+
+# activation codes of orc_activation (the same numbering as the library's)
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3, 4
+
+
+def activation(act: int, x) -> np.ndarray:
+    """orc_activation elementwise on an array (fp64)."""
+    lib = _load()
+    x = np.asarray(x, np.float64)
+    return np.vectorize(lambda v: lib.orc_activation(act, float(v)), otypes=[np.float64])(x)
+
+
+def epilogue(C, scale_m=None, scale_n=None, bias=None, act: int = ACT_NONE, mul=None):
+    """orc_epilogue on a copy of the fp64 product C [M, N]: scales (fp32
+    arrays), bias (bf16 bits [N]), activation, mul (bf16 bits [M, >= N])."""
+    lib = _load()
+    out = np.ascontiguousarray(C, np.float64).copy()
+    M, N = out.shape
+    sm = None if scale_m is None else _c(scale_m, np.float32)
+    sn = None if scale_n is None else _c(scale_n, np.float32)
+    bs = None if bias is None else _c(bias, np.uint16)
+    ml = None if mul is None else _c(mul, np.uint16)
+    lib.orc_epilogue(_ptr(out), M, N, None if sm is None else _ptr(sm),
+                     None if sn is None else _ptr(sn), None if bs is None else _ptr(bs), act,
+                     None if ml is None else _ptr(ml), 0 if ml is None else ml.shape[1])
+    return out

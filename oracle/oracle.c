@@ -18,12 +18,17 @@
  *     fp32 value to the output type; the conversion is read as IEEE RNE);
  *   - the B preshuffle follows section 12.1 of the same page, read in bytes:
  *     (N/16, K/kpack, 4, 16, kpack) with kpack = 16 bytes, padded rows zero;
+ *   - the fused epilogue (per-row / per-column scales, bias, activation,
+ *     elementwise multiplier) is applied to the fp64 product in that order;
  *   - tile_eff / wq_eff / dim_eff follow the TraceLens page, "Tile quantization
  *     efficiency", "Wave quantization efficiency" and "How it's calculated".
  *
  * Built with -O2 -fno-fast-math -ffp-contract=off so that the fp64 loop is
  * evaluated exactly as written (no reassociation, no fused multiply-add).
  */
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -261,6 +266,57 @@ void orc_gemm_points(int dtype, const void *A, int64_t lda, const void *B, int64
             acc += elem(dtype, A, ms[i] * lda + k) * elem(dtype, B, ns[i] * ldb + k);
         out[i] = acc * scale;
     }
+}
+
+/* ---------------------------------------------------------- fused epilogue */
+
+/* Activations, each its textbook definition in fp64 (libm exp, erf, tanh):
+ *   0 none; 1 ReLU max(x, 0); 2 SiLU x * logistic(x) = x / (1 + e^-x);
+ *   3 GELU x * Phi(x) = x/2 (1 + erf(x / sqrt 2)), Phi the standard normal CDF
+ *     (the GELU of the Funlib GEMM page's feed-forward block, read as the
+ *     exact form);
+ *   4 its tanh approximation x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+double orc_activation(int act, double x)
+{
+    switch (act) {
+    case 1:
+        return x > 0.0 ? x : 0.0;
+    case 2:
+        return x / (1.0 + exp(-x));
+    case 3:
+        return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+    case 4:
+        return 0.5 * x * (1.0 + tanh(sqrt(2.0 / M_PI) * (x + 0.044715 * x * x * x)));
+    default:
+        return x;
+    }
+}
+
+/* The fused epilogue on an fp64 product C [M, N] (row-major, already times
+ * the per-tensor e4m3 scales), in place, element by element in this order:
+ *   v = C[m][n]; v *= scale_m[m]; v *= scale_n[n]; v += bias[n];
+ *   v = act(v); v *= mul[m][n]
+ * Every part is optional (NULL).  bias and mul are bf16 bits.  Readings: the
+ * Funlib GEMM page names fused bias and activation; the "GEMM Optimization
+ * Guide" page (section 8.2) counts fp32 per-token scales for both M and N;
+ * the TraceLens GEMM page's addmm adds a bias per output column. */
+void orc_epilogue(double *C, int64_t M, int64_t N, const float *scale_m, const float *scale_n,
+                  const uint16_t *bias, int act, const uint16_t *mul, int64_t ld_mul)
+{
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double v = C[m * N + n];
+            if (scale_m)
+                v *= (double)scale_m[m];
+            if (scale_n)
+                v *= (double)scale_n[n];
+            if (bias)
+                v += orc_bf16_to_f64(bias[n]);
+            v = orc_activation(act, v);
+            if (mul)
+                v *= orc_bf16_to_f64(mul[m * ld_mul + n]);
+            C[m * N + n] = v;
+        }
 }
 
 /* ------------------------------------------------------- B preshuffle layout */

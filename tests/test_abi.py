@@ -269,3 +269,35 @@ def test_split_k_rejects_planes_past_32_bit_offsets():
     N = (1 << 31) // (4 * (1 + 256)) + 64
     assert dg.lib.gemm_bf16_ws(PA, 4096, PB, PC, N, 1, N, 4096, ctypes.byref(t), 0x40000,
                                1 << 40, None) == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_epilogue_argument_checks():
+    """Bad epilogue arguments are rejected before any launch."""
+    E = dg.GEMM_ERR_INVALID_VALUE
+    f = dg.lib.gemm_bf16_ex
+
+    def call(epi):
+        return f(PA, 64, PB, PC, 64, 64, 64, 64, None, ctypes.byref(epi), None, 0, None)
+    e = dg.GemmEpilogue()
+    e.activation = 5
+    assert call(e) == E
+    e.activation = -1
+    assert call(e) == E
+    e.activation = dg.GEMM_ACT_SILU
+    e.bias = 0x50001                      # bf16 bias not 2-byte aligned
+    assert call(e) == E
+    e.bias = None
+    e.scale_m = 0x50002                   # fp32 scales not 4-byte aligned
+    assert call(e) == E
+    e.scale_m = None
+    e.scale_n = 0x50006
+    assert call(e) == E
+    e.scale_n = None
+    e.mul = 0x50000
+    e.ld_mul = 63                         # ld_mul < N
+    assert call(e) == E
+    g = dg.lib.gemm_fp8_scaled_ex
+    e.ld_mul = 64
+    e.activation = 9
+    assert g(PA, 128, PB, 0x40000, 0x40010, PC, 64, 8, 64, 128, None, ctypes.byref(e), None, 0,
+             None) == E
