@@ -122,6 +122,11 @@ WORKLOADS = {
     "bf16_tp8_up_597x1376x4096": (597, 1376, 4096, "bf16", "normal", 1.0, "normal", 0.02, 61),
     "bf16_tp8_decode_1x1376x4096": (1, 1376, 4096, "bf16", "normal", 1.0, "normal", 0.02, 62),
     "bf16_tp8_down_597x4096x1376": (597, 4096, 1376, "bf16", "normal", 1.0, "normal", 0.02, 63),
+    # GPT-3-XL training GEMMs (batch 5 x 2048 tokens, d_model 2048, d_ff 8192):
+    # forward up projection, and the backward dX (K = d_ff) and dW (K = tokens)
+    "bf16_gpt3xl_fwd_10240x8192x2048": (10240, 8192, 2048, "bf16", "normal", 1.0, "normal", 0.02, 81),
+    "bf16_gpt3xl_dgrad_10240x2048x8192": (10240, 2048, 8192, "bf16", "normal", 1.0, "normal", 0.02, 82),
+    "bf16_gpt3xl_wgrad_8192x2048x10240": (8192, 2048, 10240, "bf16", "normal", 1.0, "normal", 1.0, 83),
     "fp8_4096cube": (4096, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 5),
     "fp8_tp8_up_597x1376x4096": (597, 1376, 4096, "fp8", "normal", 1.0, "normal", 1.0, 64),
     "fp8_32x4096": (32, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 51),
@@ -414,6 +419,33 @@ def epilogue_compare(name: str, spec: str, reps: int, ws_mib: int) -> int:
     return 0
 
 
+def backward_prep(reps: int) -> int:
+    """The memory-bound steps the backward GEMMs add, at GPT-3-XL sizes,
+    graph-timed: transpose_2d of dY [10240, 8192] (the A of dW), shuffle_b_t
+    of W [8192, 2048] (the B of dX) and of X [10240, 2048] (the B of dW).
+    Bytes = read + written."""
+    import torch
+    import dense_gemm_linear_amd as dg
+    T, D, F = 10240, 2048, 8192
+    g = torch.Generator(device="cuda").manual_seed(3)
+    dY = torch.randn(T, F, device="cuda", generator=g).bfloat16()
+    W = torch.randn(F, D, device="cuda", generator=g).bfloat16()
+    X = torch.randn(T, D, device="cuda", generator=g).bfloat16()
+    dYt = torch.empty(F, T, dtype=torch.bfloat16, device="cuda")
+    Ws = torch.empty(dg.shuffle_b_bytes(D, F), dtype=torch.uint8, device="cuda")
+    Xs = torch.empty(dg.shuffle_b_bytes(D, T), dtype=torch.uint8, device="cuda")
+    out = {}
+    for label, call, nbytes in (
+            ("transpose_dY_10240x8192", lambda i: dg.transpose(dY, out=dYt), 2 * dY.numel() * 2),
+            ("shuffle_b_t_W_8192x2048", lambda i: dg.shuffle_b_t(W, out=Ws), W.numel() * 2 + Ws.numel()),
+            ("shuffle_b_t_X_10240x2048", lambda i: dg.shuffle_b_t(X, out=Xs), X.numel() * 2 + Xs.numel())):
+        us = time_graph(call, reps, trials=3)
+        out[label] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    print(json.dumps({"backward_prep": out, "timing": f"hipGraph of {reps} calls, median of 3"}),
+          flush=True)
+    return 0
+
+
 def run_graph(name: str, reps: int, copies: int):
     """Decode-size kernels are shorter than a Python launch: time R launches
     captured in one HIP graph."""
@@ -509,6 +541,8 @@ def main(argv=None):
     ap.add_argument("--epilogue", default=None, metavar="PARTS",
                     help="time the fused epilogue (e.g. silu,mul or gelu,bias or scale_m,scale_n) "
                          "against the plain GEMM followed by torch elementwise ops")
+    ap.add_argument("--backward-prep", action="store_true",
+                    help="time transpose_2d and shuffle_b_t on the GPT-3-XL backward operands")
     ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
                     help="split-K workspace handed to the library (0: no split-K)")
     ap.add_argument("--sweep", action="store_true",
@@ -531,6 +565,8 @@ def main(argv=None):
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
         return sweep(name, args.steps, args.warmup, args.workspace_mib)
+    if args.backward_prep:
+        return backward_prep(args.steps)
     if args.epilogue is not None:
         return epilogue_compare(name, args.epilogue, args.steps, args.workspace_mib)
     workspace = (torch.empty(args.workspace_mib << 20, dtype=torch.uint8, device="cuda")

@@ -38,7 +38,8 @@ GEMM_KERNEL_TILED_PP = 3
 
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
-           "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex")
+           "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex", "shuffle_b_t",
+           "transpose_2d")
 
 # gemm_activation
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_SILU, GEMM_ACT_GELU_ERF, GEMM_ACT_GELU_TANH = 0, 1, 2, 3, 4
@@ -224,6 +225,10 @@ def _load_lib():
                                        ctypes.POINTER(GemmTile), ctypes.POINTER(GemmEpilogue), P,
                                        ctypes.c_size_t, P]
     lib.gemm_fp8_scaled_ex.restype = ctypes.c_int
+    lib.shuffle_b_t.argtypes = [P, I64, P, I64, I64, ctypes.c_int, P]
+    lib.shuffle_b_t.restype = ctypes.c_int
+    lib.transpose_2d.argtypes = [P, I64, P, I64, I64, I64, ctypes.c_int32, P]
+    lib.transpose_2d.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
@@ -317,6 +322,60 @@ def shuffle_b(B, dtype=None, out=None):
     if st != GEMM_OK:
         raise GemmError("shuffle_b", st)
     return out
+
+
+def shuffle_b_t(Bt, dtype=None, out=None):
+    """The preshuffled weight of B = Bt^T, from Bt [K, N] (bf16 or e4m3): the
+    same bytes as shuffle_b(Bt.T) without materialising the transpose."""
+    torch = _torch()
+    _check_rows("Bt", Bt)
+    code = _tensor_dtype_code(Bt) if dtype is None else _dtype_code(dtype)
+    K, N = Bt.shape
+    nbytes = shuffle_b_bytes(N, K, code)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=Bt.device)
+    elif out.numel() * out.element_size() < nbytes:
+        raise ValueError("out is too small")
+    st = lib.shuffle_b_t(Bt.data_ptr(), Bt.stride(0), out.data_ptr(), N, K, code, _stream_ptr(Bt))
+    if st != GEMM_OK:
+        raise GemmError("shuffle_b_t", st)
+    return out
+
+
+def transpose(X, out=None):
+    """X^T of a 2-D device tensor of 1- or 2-byte elements, into a new (or the
+    given [cols, rows]) tensor of the same dtype."""
+    torch = _torch()
+    _check_rows("X", X)
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=X.dtype, device=X.device)
+    else:
+        _check_rows("out", out)
+        if tuple(out.shape) != (cols, rows) or out.element_size() != X.element_size():
+            raise ValueError("out must be [cols, rows] with X's element size")
+    st = lib.transpose_2d(X.data_ptr(), X.stride(0), out.data_ptr(), out.stride(0), rows, cols,
+                          X.element_size(), _stream_ptr(X))
+    if st != GEMM_OK:
+        raise GemmError("transpose_2d", st)
+    return out
+
+
+def grad_input(dY, W, out=None, Ws_t=None, **kw):
+    """dX = dY W for a linear layer Y = X W^T (bf16): the GEMM C = A B^T with
+    A = dY [M, N_out] and B = W^T, preshuffled by shuffle_b_t(W) (pass it as
+    Ws_t to reuse it across calls).  Extra keywords go to gemm_bf16."""
+    Bs = shuffle_b_t(W) if Ws_t is None else Ws_t
+    return gemm_bf16(dY, Bs, W.shape[1], out=out, **kw)
+
+
+def grad_weight(dY, X, out=None, **kw):
+    """dW = dY^T X for a linear layer Y = X W^T (bf16): A = transpose(dY)
+    [N_out, M] and B = X^T, preshuffled by shuffle_b_t(X); the sum runs over
+    the M tokens, so M is this GEMM's K and follows its contract (a multiple
+    of 16; pad the token dimension with zero rows otherwise).  Extra keywords
+    go to gemm_bf16."""
+    return gemm_bf16(transpose(dY), shuffle_b_t(X), X.shape[1], out=out, **kw)
 
 
 def _out(A, N, out):

@@ -310,6 +310,50 @@ gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
+gemm_status shuffle_b_t(const void* Bt, int64_t ldbt, void* Bs, int64_t N, int64_t K,
+                        gemm_dtype dtype, void* stream)
+{
+    if (N < 0 || K < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return GEMM_ERR_INVALID_VALUE;
+    if (N == 0 || K == 0)
+        return GEMM_OK;
+    const int64_t e = dtype == GEMM_BF16 ? 2 : 1;
+    if (!Bt || !Bs || ldbt < N || !dg::aligned16(Bs) || ((uintptr_t)Bt % e) != 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (K % (dtype == GEMM_BF16 ? 16 : 64) != 0)
+        return GEMM_ERR_UNSUPPORTED;
+    if (((K * e + 63) / 64 * 64 / e + 63) / 64 > 65535)    // k tiles: the grid's second axis
+        return GEMM_ERR_UNSUPPORTED;
+    int cus = 0;
+    gemm_status st = dg::device_info(&cus);
+    if (st != GEMM_OK)
+        return st;
+    hipError_t err = dg::launch_shuffle_bt(Bt, ldbt, static_cast<uint8_t*>(Bs), N, K, (int)e,
+                                           reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t rows,
+                         int64_t cols, int32_t elem_bytes, void* stream)
+{
+    if (rows < 0 || cols < 0 || (elem_bytes != 1 && elem_bytes != 2))
+        return GEMM_ERR_INVALID_VALUE;
+    if (rows == 0 || cols == 0)
+        return GEMM_OK;
+    if (!src || !dst || ld_src < cols || ld_dst < rows || ((uintptr_t)src % elem_bytes) != 0 ||
+        ((uintptr_t)dst % elem_bytes) != 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if ((rows + 63) / 64 > 65535 || (cols + 63) / 64 > INT32_MAX)
+        return GEMM_ERR_UNSUPPORTED;
+    int cus = 0;
+    gemm_status st = dg::device_info(&cus);
+    if (st != GEMM_OK)
+        return st;
+    hipError_t err = dg::launch_transpose(src, ld_src, dst, ld_dst, rows, cols, elem_bytes,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 gemm_status gemm_tile_check(const gemm_tile* tile, int64_t M, gemm_dtype dtype)
 {
     if (!tile || M < 0 || (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))

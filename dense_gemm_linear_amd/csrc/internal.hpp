@@ -108,6 +108,10 @@ DG_DECL_INST(1, 1, 0) DG_DECL_INST(1, 1, 1) DG_DECL_INST(1, 2, 0) DG_DECL_INST(1
 // variant the arguments ask for (split-K, fused epilogue, or plain)
 hipError_t launch_tiled_rung(int kernel, int dt, int idx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int dt, int tm, int tn, int waves, const GemmArgs& a, hipStream_t s);
+hipError_t launch_transpose(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                            int64_t rows, int64_t cols, int elem_bytes, hipStream_t s);
+hipError_t launch_shuffle_bt(const void* Bt, int64_t ldbt, uint8_t* Bs, int64_t N, int64_t K,
+                             int elem_bytes, hipStream_t s);
 hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, Epilogue ep, hipStream_t s);
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
                             int64_t KB, int aligned, hipStream_t s);

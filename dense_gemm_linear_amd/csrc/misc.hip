@@ -49,6 +49,162 @@ __global__ __launch_bounds__(256) void zero_c_kernel(uint16_t* C, int64_t ldc, i
     }
 }
 
+// ---------------------------------------------------------------------------
+// Transposes through LDS, for the backward GEMMs: dX = dY W needs B = W^T
+// preshuffled (shuffle_b_t), dW = dY^T X needs A = dY^T (transpose_2d) and
+// B = X^T preshuffled (shuffle_b_t).  A workgroup of 256 threads moves one
+// 64 x 64 tile: it reads 64 source rows along their contiguous axis
+// (consecutive lanes, consecutive elements), writes them into LDS with the
+// axes swapped (rows padded by one element so a column walk spreads over the
+// banks), and writes out along the other axis.  Elements past the source
+// edges read as zero.
+// vec: the source base and row pitch are 16-byte aligned; a tile wholly
+// inside the source then moves in 16-byte pieces (two or one per thread),
+// all issued before any is used, others element by element.
+template <typename T>
+__device__ __forceinline__ void load_tile_swapped(const T* src, int64_t ld, int64_t rows,
+                                                  int64_t cols, int64_t r0, int64_t c0,
+                                                  T (*t)[65], bool vec)
+{
+    const int tid = threadIdx.x;
+    constexpr int CH = 16 / (int)sizeof(T);          // elements per 16-byte piece
+    constexpr int PER = 64 * 64 / CH / 256;          // pieces per thread
+    if (vec && r0 + 64 <= rows && c0 + 64 <= cols) {
+        i32x4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + 256 * k;
+            const int r = q / (64 / CH), cp = q % (64 / CH);
+            v[k] = *reinterpret_cast<const i32x4*>(src + (r0 + r) * ld + c0 + cp * CH);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + 256 * k;
+            const int r = q / (64 / CH), cp = q % (64 / CH);
+            T e[CH];
+            __builtin_memcpy(e, &v[k], 16);
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                t[cp * CH + j][r] = e[j];                    // t[col][row]
+        }
+    } else {
+        const int c = tid & 63;
+        for (int i = tid >> 6; i < 64; i += 4) {
+            const int64_t r = r0 + i, cc = c0 + c;
+            t[c][i] = (r < rows && cc < cols) ? src[r * ld + cc] : T(0);   // t[col][row]
+        }
+    }
+    __syncthreads();
+}
+
+// dst[c][r] = src[r][c]; grid (col tiles, row tiles).
+// vec_src / vec_dst: base and pitch 16-byte aligned (see load_tile_swapped).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t ld_src, T* dst,
+                                                        int64_t ld_dst, int64_t rows, int64_t cols,
+                                                        int vec_src, int vec_dst)
+{
+    __shared__ T t[64][65];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    load_tile_swapped(src, ld_src, rows, cols, r0, c0, t, vec_src != 0);
+    const int tid = threadIdx.x;
+    constexpr int CH = 16 / (int)sizeof(T);
+    constexpr int PER = 64 * 64 / CH / 256;
+    if (vec_dst && r0 + 64 <= rows && c0 + 64 <= cols) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + 256 * k;
+            const int c = q / (64 / CH), rp = q % (64 / CH);   // dst row c0 + c
+            T e[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                e[j] = t[c][rp * CH + j];
+            *reinterpret_cast<i32x4*>(dst + (c0 + c) * ld_dst + r0 + rp * CH) =
+                __builtin_bit_cast(i32x4, e);
+        }
+        return;
+    }
+    const int x = tid & 63;
+    for (int i = tid >> 6; i < 64; i += 4) {
+        const int64_t dr = c0 + i, dc = r0 + x;     // dst row = src column
+        if (dr < cols && dc < rows)
+            dst[dr * ld_dst + dc] = t[i][x];
+    }
+}
+
+// shuffle_b of B [N, K] given its transpose Bt [K, N] (Bt[k][n] = B[n][k]):
+// the tile of Bt at (k0e, n0e) holds B[n0e + n][k0e + k] at t[n][k] after the
+// swap, and each thread writes whole 16-byte units of the preshuffled
+// layout (the same units, in the same order within a 1 KiB block, as
+// shuffle_b_kernel).  Grid (tiles over the 16-padded N, tiles over the
+// 64-byte-padded K).
+template <typename T>
+__global__ __launch_bounds__(256) void shuffle_bt_kernel(const T* Bt, int64_t ldbt, uint8_t* Bs,
+                                                         int64_t N, int64_t K, int64_t KB, int vec)
+{
+    __shared__ T t[64][65];
+    constexpr int E = (int)sizeof(T);
+    constexpr int KP = 16 / E;                 // elements per 16-byte unit
+    const int64_t n0e = (int64_t)blockIdx.x * 64, k0e = (int64_t)blockIdx.y * 64;
+    load_tile_swapped(Bt, ldbt, K, N, k0e, n0e, t, vec != 0);
+    const int64_t nrows = (N + 15) / 16 * 16;
+    constexpr int UNITS = 64 * 64 * E / 16;    // 16-byte units in the tile
+    for (int q = threadIdx.x; q < UNITS; q += 256) {
+        const int nl = q & 15, g = (q >> 4) & 3, rest = q >> 6;
+        const int n_local = (rest & 3) * 16 + nl;
+        const int k_local = (rest >> 2) * (64 / E) + g * KP;
+        const int64_t n = n0e + n_local;
+        const int64_t kbyte = (k0e + k_local) * E;
+        if (n >= nrows || kbyte >= KB * 64)
+            continue;
+        T v[KP];
+#pragma unroll
+        for (int j = 0; j < KP; ++j)
+            v[j] = t[n_local][k_local + j];
+        const int64_t u = (((n >> 4) * KB + (kbyte >> 6)) * 4 + ((kbyte >> 4) & 3)) * 16 + (n & 15);
+        *reinterpret_cast<i32x4*>(Bs + u * 16) = __builtin_bit_cast(i32x4, v);
+    }
+}
+
+hipError_t launch_transpose(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                            int64_t rows, int64_t cols, int elem_bytes, hipStream_t s)
+{
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    int vs = ((uintptr_t)src % 16 == 0) && (ld_src * elem_bytes) % 16 == 0;
+    int vd = ((uintptr_t)dst % 16 == 0) && (ld_dst * elem_bytes) % 16 == 0;
+    if (elem_bytes == 2) {
+        const uint16_t* a = static_cast<const uint16_t*>(src);
+        uint16_t* b = static_cast<uint16_t*>(dst);
+        void* args[] = {&a, &ld_src, &b, &ld_dst, &rows, &cols, &vs, &vd};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&transpose_kernel<uint16_t>), grid,
+                               dim3(256), args, 0, s);
+    }
+    const uint8_t* a = static_cast<const uint8_t*>(src);
+    uint8_t* b = static_cast<uint8_t*>(dst);
+    void* args[] = {&a, &ld_src, &b, &ld_dst, &rows, &cols, &vs, &vd};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&transpose_kernel<uint8_t>), grid,
+                           dim3(256), args, 0, s);
+}
+
+hipError_t launch_shuffle_bt(const void* Bt, int64_t ldbt, uint8_t* Bs, int64_t N, int64_t K,
+                             int elem_bytes, hipStream_t s)
+{
+    const int64_t KB = (K * elem_bytes + 63) / 64;
+    const int64_t nrows = (N + 15) / 16 * 16;
+    const dim3 grid((unsigned)((nrows + 63) / 64), (unsigned)((KB * 64 / elem_bytes + 63) / 64));
+    int vec = ((uintptr_t)Bt % 16 == 0) && (ldbt * elem_bytes) % 16 == 0;
+    if (elem_bytes == 2) {
+        const uint16_t* a = static_cast<const uint16_t*>(Bt);
+        void* args[] = {&a, &ldbt, &Bs, &N, &K, (void*)&KB, &vec};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&shuffle_bt_kernel<uint16_t>), grid,
+                               dim3(256), args, 0, s);
+    }
+    const uint8_t* a = static_cast<const uint8_t*>(Bt);
+    void* args[] = {&a, &ldbt, &Bs, &N, &K, (void*)&KB, &vec};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&shuffle_bt_kernel<uint8_t>), grid,
+                           dim3(256), args, 0, s);
+}
+
 hipError_t launch_shuffle_b(const uint8_t* B, int64_t ldb_b, uint8_t* Bs, int64_t N, int64_t K_b,
                             int64_t KB, int aligned, hipStream_t s)
 {

@@ -228,6 +228,36 @@ gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K
                       void* stream);
 
 /*
+ * shuffle_b_t -- shuffle_b of B [N, K] given its transpose: Bt is row-major
+ * [K, ldbt] (device, ldbt >= N, element-aligned), element (k, n) being
+ * B[n][k].  Writes exactly the Bs that shuffle_b(B) writes.  It serves the
+ * backward GEMMs of a linear layer Y = X W^T ("TraceLens GEMM analysis"
+ * page, backward pass and the GPT-3-XL table): dX = dY W is C = A B^T with
+ * A = dY and B = W^T, so Bs = shuffle_b_t(W); dW = dY^T X takes B = X^T,
+ * Bs = shuffle_b_t(X) (with A = dY^T from transpose_2d).  One memory-bound
+ * kernel that transposes 64 x 64 tiles through LDS.
+ *
+ * Errors as for shuffle_b, with ldbt < N -> INVALID_VALUE.
+ */
+gemm_status shuffle_b_t(const void* Bt, int64_t ldbt, void* Bs, int64_t N, int64_t K,
+                        gemm_dtype dtype, void* stream);
+
+/*
+ * transpose_2d -- dst[c][r] = src[r][c] for r < rows, c < cols: src row-major
+ * [rows, ld_src], dst row-major [cols, ld_dst] (device, element-aligned,
+ * ld_src >= cols, ld_dst >= rows, not overlapping); elem_bytes 1 (e4m3) or 2
+ * (bf16).  The weight-gradient GEMM dW = dY^T X contracts over tokens, the
+ * strided dimension of both dY and X; the A operand must have K contiguous,
+ * so dY is transposed first.  Memory-bound, 64 x 64 tiles through LDS.
+ *
+ * Errors: INVALID_VALUE (negative sizes, null pointers with work, pitches,
+ * misalignment, elem_bytes), UNSUPPORTED (more than 65535 x 64 rows), HIP.
+ * rows == 0 or cols == 0: no work.
+ */
+gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t rows,
+                         int64_t cols, int32_t elem_bytes, void* stream);
+
+/*
  * gemm_bf16 -- C[m][n] = bf16( sum_k A[m][k] * B[n][k] ), fp32 accumulation,
  * C overwritten (no alpha/beta, no bias).
  *

@@ -56,6 +56,8 @@ def _load():
     lib.orc_gemm_points.argtypes = [ctypes.c_int, P, I64, P, I64, I64, ctypes.c_double,
                                     P, P, I64, P]
     lib.orc_gemm_points.restype = None
+    lib.orc_transpose.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64]
+    lib.orc_transpose.restype = None
     lib.orc_activation.argtypes = [ctypes.c_int, ctypes.c_double]
     lib.orc_activation.restype = ctypes.c_double
     lib.orc_epilogue.argtypes = [P, I64, I64, P, P, P, ctypes.c_int, P, I64]
@@ -222,3 +224,19 @@ def epilogue(C, scale_m=None, scale_n=None, bias=None, act: int = ACT_NONE, mul=
                      None if sn is None else _ptr(sn), None if bs is None else _ptr(bs), act,
                      None if ml is None else _ptr(ml), 0 if ml is None else ml.shape[1])
     return out
+
+
+def transpose(X) -> np.ndarray:
+    """orc_transpose of a 2-D uint8 / uint16 array: a new array X^T."""
+    lib = _load()
+    X = np.ascontiguousarray(X)
+    rows, cols = X.shape
+    out = np.empty((cols, rows), X.dtype)
+    lib.orc_transpose(_ptr(X), cols, rows, cols, X.dtype.itemsize, _ptr(out), rows)
+    return out
+
+
+def shuffle_b_t(Bt, elem_bytes: int) -> np.ndarray:
+    """The preshuffled layout of B given Bt = B^T ([K, N]): orc_shuffle_b of
+    orc_transpose(Bt)."""
+    return shuffle_b(transpose(Bt), elem_bytes)

@@ -268,6 +268,21 @@ void orc_gemm_points(int dtype, const void *A, int64_t lda, const void *B, int64
     }
 }
 
+/* --------------------------------------------------------------- transposes */
+
+/* dst[c][r] = src[r][c] for r < rows, c < cols (elements of elem_bytes bytes;
+ * row pitches in elements).  Used for the backward GEMMs of a linear layer
+ * ("TraceLens GEMM analysis" page, backward pass): dW = dY^T X has to see dY
+ * with the token dimension contiguous. */
+void orc_transpose(const uint8_t *src, int64_t ld_src, int64_t rows, int64_t cols, int elem_bytes,
+                   uint8_t *dst, int64_t ld_dst)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            memcpy(dst + (c * ld_dst + r) * elem_bytes, src + (r * ld_src + c) * elem_bytes,
+                   (size_t)elem_bytes);
+}
+
 /* ---------------------------------------------------------- fused epilogue */
 
 /* Activations, each its textbook definition in fp64 (libm exp, erf, tanh):

@@ -301,3 +301,24 @@ def test_epilogue_argument_checks():
     e.activation = 9
     assert g(PA, 128, PB, 0x40000, 0x40010, PC, 64, 8, 64, 128, None, ctypes.byref(e), None, 0,
              None) == E
+
+
+def test_transpose_and_shuffle_b_t_argument_checks():
+    E = dg.GEMM_ERR_INVALID_VALUE
+    U = dg.GEMM_ERR_UNSUPPORTED
+    t = dg.lib.transpose_2d
+    assert t(PA, 64, PB, 64, 0, 64, 2, None) == dg.GEMM_OK           # empty
+    assert t(PA, 64, PB, 64, -1, 64, 2, None) == E
+    assert t(PA, 64, PB, 64, 64, 64, 4, None) == E                  # elem_bytes
+    assert t(None, 64, PB, 64, 64, 64, 2, None) == E
+    assert t(PA, 63, PB, 64, 64, 64, 2, None) == E                  # ld_src < cols
+    assert t(PA, 64, PB, 63, 64, 64, 2, None) == E                  # ld_dst < rows
+    assert t(PA + 1, 64, PB, 64, 64, 64, 2, None) == E              # misaligned bf16
+    assert t(PA, 64, PB, 65536 * 64, 65536 * 64, 64, 1, None) == U  # too many row tiles
+    s = dg.lib.shuffle_b_t
+    assert s(PA, 64, PB, 64, 0, 0, None) == dg.GEMM_OK
+    assert s(PA, 63, PB, 64, 64, 0, None) == E                      # ldbt < N
+    assert s(PA, 64, PB + 8, 64, 64, 0, None) == E                  # Bs not 16-byte aligned
+    assert s(PA + 1, 64, PB, 64, 64, 0, None) == E                  # Bt not 2-byte aligned
+    assert s(PA, 64, PB, 64, 40, 0, None) == U                      # bf16 K % 16
+    assert s(PA, 64, PB, 64, 96, 1, None) == U                      # e4m3 K % 64
