@@ -217,7 +217,7 @@ def parse_tile(spec: str | None):
         return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k, k_split)
     if kind == "pp":
         return dg.tiled_pp(tm, tn, atom, stages, tile_k, k_split)
-    return dg.skinny(tm, tn)
+    return dg.skinny(tm, tn, waves)
 
 
 def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per_launch=True,

@@ -136,7 +136,32 @@ def fit(paths):
     return rungs, (coef[-3:], n_split), skinny
 
 
-def emit(fits, path):
+def measured_best(paths):
+    """Per swept shape, the fastest measured tile: (dt, M, N, K, tile fields)."""
+    wl = workloads()
+    best = {}
+    for p in paths:
+        for line in open(p):
+            d = json.loads(line)
+            key = d["sweep"]
+            if key not in best or d["kernel_us_median"] < best[key][1]:
+                best[key] = (d["tile"], d["kernel_us_median"])
+    out = []
+    for name, (tile, us) in sorted(best.items()):
+        M, N, K, dt = wl[name][:4]
+        m = SKINNY.match(tile)
+        if m:
+            w = int(m.group(3) or 4)
+            f = (1, int(m.group(1)), int(m.group(2)), 0, 16, w, w, 0)
+        else:
+            r = parse(tile)
+            f = (r["kernel"], r["tm"], r["tn"], r["tile_k"], r["atom"], r["waves"], r["k_split"],
+                 r["stages"])
+        out.append((0 if dt == "bf16" else 1, M, N, K, f, us, tile))
+    return out
+
+
+def emit(fits, path, table=()):
     rungs, ((d_st, r1, r0), n_split), skinny = fits
     lines = ["// Generated by calibrate.py from measured MI355X tile sweeps; do not edit.",
              "// {dtype, kernel, tile_m, tile_n, waves, atom, stages, k-tile bytes, a, b, g, c,",
@@ -159,6 +184,14 @@ def emit(fits, path):
         d = 0 if dt == "bf16" else 1
         lines.append(f"    {{{d}, {tm}, {tn}, {w}, {a:.5f}f, {b:.5f}f, {c:.5f}f, {n}}},")
     lines.append("};")
+    lines += ["// measured best tile per swept shape, used for exact matches:",
+              "// {dtype, M, N, K, kernel, tile_m, tile_n, tile_k, atom, waves, k_split, lds_stages,",
+              "//  measured us}",
+              "static const MeasuredBest kMeasuredBest[] = {"]
+    for d, M, N, K, (kern, tm, tn, tk, atom, w, ks, st), us, name in table:
+        lines.append(f"    {{{d}, {M}, {N}, {K}, {kern}, {tm}, {tn}, {tk}, {atom}, {w}, {ks}, {st}, "
+                     f"{us:.3f}f}},   // {name}")
+    lines.append("};")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -166,7 +199,7 @@ def emit(fits, path):
 if __name__ == "__main__":
     paths = sys.argv[1:] or [os.path.join(HERE, "calibration", "mi355x_sweep.jsonl")]
     fits = fit(paths)
-    emit(fits, os.path.join(HERE, "csrc", "calibration.inc"))
+    emit(fits, os.path.join(HERE, "csrc", "calibration.inc"), measured_best(paths))
     (d_st, r1, r0), n = fits[1]
     print(f"{len(fits[0])} rungs, {len(fits[2])} skinny rungs calibrated; split-K from {n} points: "
           f"{d_st:.3f} us per MB of partials per CU, {r1:.3f} us per MB reduced, {r0:.2f} us launch")

@@ -1241,7 +1241,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 template <int DT, int MR, int NB, int W, bool EPI>
 __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs p)
 {
-    constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);   // k-tiles per batch
+    // k-tiles per batch; 16 waves of 1024 threads have 128 VGPRs each, which
+    // two batches of 4 k-tiles of fragments would exceed
+    constexpr int U = W >= 16 ? (MR == 1 ? 2 : 1) : (MR == 1 ? 4 : (MR == 2 ? 2 : 1));
     __shared__ f32x4 red[W][MR * NB][64];
 
     const int tid = threadIdx.x;

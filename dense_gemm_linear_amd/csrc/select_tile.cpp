@@ -46,6 +46,13 @@ struct SkinnyCalib {
     float a, b, c;
     int points;
 };
+// the fastest tile measured on a swept shape
+struct MeasuredBest {
+    int dt;
+    int64_t M, N, K;
+    int kernel, tm, tn, tile_k, atom, waves, k_split, stages;
+    float us;
+};
 #include "calibration.inc"
 
 const RungCalib* find_calib(int dt, int kernel, int tm, int tn, int waves, int atom, int st,
@@ -377,8 +384,57 @@ bool skinny_supported(int tm, int tn, int waves)
 
 // Pick the fastest candidate under the model; fill `out`.  With a workspace
 // of ws_bytes, split-K variants of the tiled rungs whose partial planes fit
-// are candidates too (only for shapes with fewer tiles than CUs).
+// are candidates too, for tiles that would leave at least half the CUs idle
+// (with more, the slices add rounds instead of filling idle CUs).
+void choose_tile_model(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                       gemm_tile* out);
+
+// A shape measured on this chip (calibration.inc) gets its measured best tile
+// when the device has the CU count the sweep ran on and the workspace covers
+// it; any other shape is priced by the model.
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, gemm_tile* out)
+{
+    if (cus == 256) {
+        const int e = dt == GEMM_BF16 ? 2 : 1;
+        for (const MeasuredBest& b : kMeasuredBest) {
+            if (b.dt != dt || b.M != M || b.N != N || b.K != K)
+                continue;
+            gemm_tile t;
+            memset(&t, 0, sizeof t);
+            t.kernel = b.kernel;
+            t.tile_m = b.tm;
+            t.tile_n = b.tn;
+            t.tile_k = b.tile_k;
+            t.atom = b.atom;
+            t.waves = b.waves;
+            t.k_split = b.k_split;
+            t.lds_stages = b.stages;
+            if (b.kernel != GEMM_KERNEL_SKINNY && b.k_split > 1) {
+                int ktb = 0;
+                const int idx = b.kernel == GEMM_KERNEL_TILED_AB   ? ab_rung(b.tm, b.tn, b.waves, b.atom, b.stages, b.tile_k * e)
+                                : b.kernel == GEMM_KERNEL_TILED_PP ? pp_rung(b.tm, b.tn, b.waves, b.atom, b.stages, b.tile_k * e)
+                                                                   : tiled_rung(b.tm, b.tn, b.waves, b.atom, b.stages, b.tile_k * e);
+                ktb = rung_ktb(b.kernel, idx);
+                if (ktb == 0 || split_plan(M, N, K, e, ktb, b.k_split).ws_bytes > (int64_t)ws_bytes)
+                    break;   // the measured best needs more workspace: use the model
+            }
+            const int64_t tiles_m = cdiv(M, b.tm), tiles_n = cdiv(N, b.tn);
+            const int64_t units = b.kernel == GEMM_KERNEL_SKINNY ? cdiv(cdiv(N, 16), b.tn / 16)
+                                                                 : tiles_m * tiles_n * std::max(1, b.k_split);
+            t.tile_eff = b.kernel == GEMM_KERNEL_SKINNY
+                             ? (float)((double)M * N / ((double)b.tm * units * b.tn))
+                             : (float)((double)M * N / ((double)tiles_m * b.tm * (double)tiles_n * b.tn));
+            t.wq_eff = (float)((double)units / ((double)cdiv(units, cus) * cus));
+            t.predicted_us = b.us;
+            *out = t;
+            return;
+        }
+    }
+    choose_tile_model(M, N, K, dt, cus, ws_bytes, out);
+}
+
+void choose_tile_model(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                       gemm_tile* out)
 {
     const Chip chip;
     Cand best{}, best_screened{};
@@ -406,7 +462,7 @@ void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_byt
             const SplitPlan pl = split_plan(M, N, K, e, ktb, S);
             if (S > 1) {
                 if (ws_bytes == 0 || pl.S != S || pl.kt_per < 2 ||
-                    cdiv(M, tm) * cdiv(N, tn) >= cus || pl.ws_bytes > (int64_t)ws_bytes ||
+                    2 * cdiv(M, tm) * cdiv(N, tn) > cus || pl.ws_bytes > (int64_t)ws_bytes ||
                     !partial_plane_fits(M, pl.ldw))
                     continue;
             }
