@@ -102,13 +102,14 @@ bool make_epilogue(const gemm_epilogue* e, int64_t N, Epilogue* out)
     if (((uintptr_t)e->bias & 1u) || ((uintptr_t)e->scale_m & 3u) ||
         ((uintptr_t)e->scale_n & 3u) || ((uintptr_t)e->mul & 1u))
         return false;
-    if (e->mul && e->ld_mul < N)
+    if (e->mul && (e->ld_mul < N || e->ld_mul * 2 > (INT64_C(1) << 22)))
         return false;
     out->bias = e->bias;
     out->scale_m = e->scale_m;
     out->scale_n = e->scale_n;
     out->mul = e->mul;
     out->ldmul = e->mul ? e->ld_mul : 0;
+    out->mul_vec = e->mul && ((uintptr_t)e->mul & 15u) == 0 && e->ld_mul % 8 == 0;
     out->act = e->activation;
     out->on = e->bias || e->scale_m || e->scale_n || e->mul || e->activation != GEMM_ACT_NONE;
     return true;

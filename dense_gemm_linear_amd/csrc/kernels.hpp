@@ -54,6 +54,7 @@ struct Epilogue {
     int64_t ldmul;
     int act;
     int on;
+    int mul_vec;             // mul and ldmul allow 16-byte row pieces
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h)
@@ -402,10 +403,10 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
     // Fused epilogue operands.  A lane's columns are the same for every
     // element of accumulator column j, so the column scale and bias are
     // loaded once per tile; row scales once per accumulator row; the
-    // multiplier as one batch of NACC loads before its values are used.
-    // (Loaded element by element between the LDS staging stores, each load
-    // waited for its own round trip.)  Indices past M or N are clamped: those
-    // elements are computed but never stored.
+    // multiplier through LDS, one block per chunk (below).  (Loaded element
+    // by element between the LDS staging stores, each load waited for its
+    // own round trip.)  Indices past M or N are clamped: those elements are
+    // computed but never stored.
     float col_scale[NR], col_bias[NR];
     if constexpr (EPI) {
 #pragma unroll
@@ -422,41 +423,80 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
         constexpr int CLS = decltype(cls_c)::value;
         static_for<MR / CH>([&](auto cc_c) __attribute__((always_inline)) {
             constexpr int cc = decltype(cc_c)::value;
+            if constexpr (EPI) {
+                // The multiplier block of this chunk, the same [CH R][WCOLS]
+                // shape as the staged C chunk, goes into this wave's staging
+                // area first, all loads in flight at once; the staging loop
+                // then reads each element from LDS and writes the result
+                // over it.  Rows past M fall outside the descriptor.
+                if (p.ep.mul) {
+                    const rsrc_t rm = make_rsrc(
+                        p.ep.mul + (int64_t)m0 * p.ep.ldmul,
+                        (uint32_t)(((int64_t)(rows - 1) * p.ep.ldmul + p.N) * 2));
+                    if (p.ep.mul_vec) {
+                        constexpr int NQ = (PIECES + 63) / 64;
+                        i32x4 mv[NQ];
+#pragma unroll
+                        for (int k = 0; k < NQ; ++k) {
+                            const int q = 64 * k + lane;
+                            if (PIECES % 64 == 0 || q < PIECES) {
+                                const int prow = q / PPR, pc = q % PPR;
+                                const uint32_t trow = (uint32_t)(row0 + cc * CH * R + prow);
+                                mv[k] = load16(rm, (trow * (uint32_t)p.ep.ldmul + (uint32_t)col_w +
+                                                    8u * (uint32_t)pc) * 2u);
+                            }
+                        }
+#pragma unroll
+                        for (int k = 0; k < NQ; ++k) {
+                            const int q = 64 * k + lane;
+                            if (PIECES % 64 == 0 || q < PIECES) {
+                                const int prow = q / PPR, pc = q % PPR;
+                                *reinterpret_cast<i32x4*>(stage + prow * SROW + pc * 16) = mv[k];
+                            }
+                        }
+                    } else {
+                        for (int idx = lane; idx < CH * R * WCOLS; idx += 64) {
+                            const int prow = idx / WCOLS, c = idx % WCOLS;
+                            const uint32_t trow = (uint32_t)(row0 + cc * CH * R + prow);
+                            *reinterpret_cast<uint16_t*>(stage + prow * SROW + c * 2) =
+                                __builtin_amdgcn_raw_buffer_load_b16(
+                                    rm, (int)((trow * (uint32_t)p.ep.ldmul + (uint32_t)(col_w + c)) * 2u),
+                                    0, 0);
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
 #pragma unroll
             for (int ml = 0; ml < CH; ++ml) {
                 float row_scale[AT::NACC];
-                int grow[AT::NACC];
                 if constexpr (EPI) {
 #pragma unroll
                     for (int e = 0; e < AT::NACC; ++e) {
-                        grow[e] = min(m0 + row0 + (cc * CH + ml) * R + AT::out_row(e, lane), p.M - 1);
-                        row_scale[e] = p.ep.scale_m ? p.ep.scale_m[grow[e]] : 1.f;
+                        const int grow =
+                            min(m0 + row0 + (cc * CH + ml) * R + AT::out_row(e, lane), p.M - 1);
+                        row_scale[e] = p.ep.scale_m ? p.ep.scale_m[grow] : 1.f;
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
-                    float mulv[AT::NACC];
-                    if constexpr (EPI) {
-                        const int col = min(col_w + j * R + lc, p.N - 1);
-#pragma unroll
-                        for (int e = 0; e < AT::NACC; ++e)
-                            mulv[e] = p.ep.mul ? bf16_to_f32(p.ep.mul[(int64_t)grow[e] * p.ep.ldmul + col])
-                                               : 1.f;
-                    }
 #pragma unroll
                     for (int e = 0; e < AT::NACC; ++e) {
                         float v = acc[cc * CH + ml][j][e];
                         if constexpr (DT == DT_FP8)
                             v = (v * scale_a) * scale_b;
+                        const int row = ml * R + AT::out_row(e, lane);
+                        const int col = j * R + lc;
+                        uint16_t* sp = reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2);
                         if constexpr (EPI) {
                             v = v * row_scale[e];
                             v = v * col_scale[j];
                             v = v + col_bias[j];
-                            v = activate_c<CLS>(p.ep.act, v) * mulv[e];
+                            v = activate_c<CLS>(p.ep.act, v);
+                            if (p.ep.mul)
+                                v = v * bf16_to_f32(*sp);
                         }
-                        const int row = ml * R + AT::out_row(e, lane);
-                        const int col = j * R + lc;
-                        *reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2) = bf16_rne(v);
+                        *sp = bf16_rne(v);
                     }
                 }
             }

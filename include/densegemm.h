@@ -342,7 +342,8 @@ gemm_status gemm_fp8_scaled_ws(const uint8_t* A, int64_t lda, const void* Bs,
  * C = bf16(epilogue(0)).
  *
  * Errors as for *_ws, plus INVALID_VALUE for an activation outside
- * gemm_activation, misaligned epilogue pointers, mul with ld_mul < N.
+ * gemm_activation, misaligned epilogue pointers, mul with ld_mul < N or a row
+ * pitch above 4 MiB.
  */
 gemm_status gemm_bf16_ex(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
                          int64_t M, int64_t N, int64_t K, const gemm_tile* tile,

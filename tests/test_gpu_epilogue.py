@@ -217,3 +217,19 @@ def test_k_zero_applies_epilogue_to_zero():
                            oracle.ACT_GELU_ERF, parts["mul"])
     check_epi_close("bf16", host_bits(C), want, np.zeros((M, N)), 0, parts, 1.0, "K=0")
     del A, B
+
+
+@pytest.mark.parametrize("N", [272, 270], ids=["mul_16B_rows", "mul_2B_rows"])
+@pytest.mark.parametrize("tile", [dg.tiled(128, 256, 4, 32), dg.tiled_ab(256, 256, 8, 32),
+                                  dg.tiled_pp(256, 256), dg.tiled(64, 64)],
+                         ids=lambda t: t.name)
+@pytest.mark.parametrize("inplace", [False, True], ids=["mul", "mul_in_place"])
+def test_mul_staging_paths(tile, N, inplace):
+    """The multiplier goes through the staging area in 16-byte row pieces when
+    its base and row pitch allow (N % 8 == 0 here), else element by element."""
+    M, K = 300, 192
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=37)
+    parts = make_parts(M, N, True, 8, parts=("bias", "mul"))
+    C, ok = run_epi("bf16", A, B, parts, "relu", tile, inplace=inplace)
+    assert ok
+    check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], f"{tile.name} N={N}")
