@@ -380,10 +380,13 @@ __device__ __forceinline__ void static_for(F&& f)
 // column predicate keeps a row's padding and the next row intact.
 //
 // C rows need not start on a 16-byte boundary (odd ldc, or an unaligned C):
-// each staged row segment is cut at the 16-byte boundaries of its absolute
-// address, so that all but one of its 16-byte pieces are aligned stores; the
-// one piece that straddles the segment ends (sh elements at the head, 8 - sh
-// at the tail) is written element by element.
+// a row segment whose first element sits at element phase ph (mod 8) of its
+// absolute address is staged ph elements to the right (the row pitch has 8
+// elements of slack), so staged 16-byte piece k is the k-th aligned 16-byte
+// piece of C that the segment touches.  Pieces 1 .. PPR-1 are whole: one LDS
+// read and one aligned store each.  Piece 0 (8 - ph elements at the head) and
+// piece PPR (ph at the tail) are shared with the neighbouring segments and
+// are written element by element.
 template <int DT, class AT, int MR, int NR, int CH, int SROW, int WCOLS, bool EPI>
 __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                                              const typename AT::acc_t (&acc)[MR][NR],
@@ -400,6 +403,10 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
     const uint32_t base_ph =
         (uint32_t)((((uintptr_t)p.C) >> 1) + (uint64_t)m0 * (uint64_t)p.ldc + (uint32_t)col_w) & 7u;
     const uint32_t ldc_ph = (uint32_t)p.ldc & 7u;
+    // phase of row `trow` of the tile; 0 on every row when p.c_vec
+    auto row_phase = [&](int trow) __attribute__((always_inline)) {
+        return (int)((base_ph + (uint32_t)trow * ldc_ph) & 7u);
+    };
     // Fused epilogue operands.  A lane's columns are the same for every
     // element of accumulator column j, so the column scale and bias are
     // loaded once per tile; row scales once per accumulator row; the
@@ -433,7 +440,7 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                     const rsrc_t rm = make_rsrc(
                         p.ep.mul + (int64_t)m0 * p.ep.ldmul,
                         (uint32_t)(((int64_t)(rows - 1) * p.ep.ldmul + p.N) * 2));
-                    if (p.ep.mul_vec) {
+                    if (p.ep.mul_vec && p.c_vec) {
                         constexpr int NQ = (PIECES + 63) / 64;
                         i32x4 mv[NQ];
 #pragma unroll
@@ -455,10 +462,12 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                             }
                         }
                     } else {
+                        // staged at the row's phase, as the C values are
                         for (int idx = lane; idx < CH * R * WCOLS; idx += 64) {
                             const int prow = idx / WCOLS, c = idx % WCOLS;
                             const uint32_t trow = (uint32_t)(row0 + cc * CH * R + prow);
-                            *reinterpret_cast<uint16_t*>(stage + prow * SROW + c * 2) =
+                            const int ph = row_phase((int)trow);
+                            *reinterpret_cast<uint16_t*>(stage + prow * SROW + (c + ph) * 2) =
                                 __builtin_amdgcn_raw_buffer_load_b16(
                                     rm, (int)((trow * (uint32_t)p.ep.ldmul + (uint32_t)(col_w + c)) * 2u),
                                     0, 0);
@@ -479,14 +488,15 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < NR; ++j) {
+                for (int e = 0; e < AT::NACC; ++e) {
+                    const int row = ml * R + AT::out_row(e, lane);
+                    const int ph = row_phase(row0 + cc * CH * R + row);
 #pragma unroll
-                    for (int e = 0; e < AT::NACC; ++e) {
+                    for (int j = 0; j < NR; ++j) {
                         float v = acc[cc * CH + ml][j][e];
                         if constexpr (DT == DT_FP8)
                             v = (v * scale_a) * scale_b;
-                        const int row = ml * R + AT::out_row(e, lane);
-                        const int col = j * R + lc;
+                        const int col = j * R + lc + ph;
                         uint16_t* sp = reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2);
                         if constexpr (EPI) {
                             v = v * row_scale[e];
@@ -509,25 +519,13 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                     const int trow = row0 + cc * CH * R + prow;   // row within the tile
                     const uint32_t row_off = (uint32_t)((int64_t)trow * p.ldc + col_w);  // elements
                     const uint8_t* srow = stage + prow * SROW;
-                    // elements before the row segment's first 16-byte boundary
-                    const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
-                    if (p.c_vec || sh == 0 || pc < PPR - 1) {
-                        const int o = (p.c_vec ? 0 : sh) + 8 * pc;     // staged column of the piece
-                        i32x4 v;
-                        if (p.c_vec || sh == 0) {
-                            v = *reinterpret_cast<const i32x4*>(srow + o * 2);
-                        } else {
-                            // 8 bf16 from a 2-byte aligned LDS offset: 5 dwords, funnel-shifted
-                            const uint32_t* d = reinterpret_cast<const uint32_t*>(srow + (o & ~1) * 2);
-                            const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
-                            const int odd = o & 1;
-                            v[0] = (int)(odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0);
-                            v[1] = (int)(odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1);
-                            v[2] = (int)(odd ? __builtin_amdgcn_alignbit(w3, w2, 16) : w2);
-                            v[3] = (int)(odd ? __builtin_amdgcn_alignbit(w4, w3, 16) : w3);
-                        }
-                        const int gcol = col_w + o;
-                        const uint32_t off = (row_off + (uint32_t)o) * 2u;
+                    const int ph = row_phase(trow);
+                    if (ph == 0 || pc < PPR - 1) {
+                        const int k = pc + (ph != 0);               // staged piece
+                        const i32x4 v = *reinterpret_cast<const i32x4*>(srow + k * 16);
+                        const int col = 8 * k - ph;                 // its first column
+                        const int gcol = col_w + col;
+                        const uint32_t off = (row_off + (uint32_t)col) * 2u;
                         if (gcol + 8 <= p.N) {
                             store16(rc, off, v);
                         } else {
@@ -541,19 +539,19 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                 }
             }
             if (!p.c_vec) {
-                // The straddling piece of every row: head [0, sh) and tail
-                // [sh + 8 (PPR-1), WCOLS), one element per lane per store.
+                // The shared pieces of every row: head columns [0, 8 - ph),
+                // tail columns [WCOLS - ph, WCOLS), one element per lane.
                 constexpr int ELEMS = CH * R * 8;
 #pragma unroll
                 for (int u0 = 0; u0 < ELEMS; u0 += 64) {
                     const int u = u0 + lane;
                     const int prow = u >> 3, e = u & 7;
                     const int trow = row0 + cc * CH * R + prow;
-                    const int sh = (int)((8u - ((base_ph + (uint32_t)trow * ldc_ph) & 7u)) & 7u);
-                    const int col = e < sh ? e : sh + 8 * (PPR - 1) + (e - sh);
-                    if (sh != 0 && col_w + col < p.N)
+                    const int ph = row_phase(trow);
+                    const int col = e < 8 - ph ? e : WCOLS - 8 + e;
+                    if (ph != 0 && col_w + col < p.N)
                         store2(rc, ((uint32_t)((int64_t)trow * p.ldc + col_w) + (uint32_t)col) * 2u,
-                               *reinterpret_cast<const uint16_t*>(stage + prow * SROW + col * 2));
+                               *reinterpret_cast<const uint16_t*>(stage + prow * SROW + (col + ph) * 2));
                 }
             }
             __syncthreads();

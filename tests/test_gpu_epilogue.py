@@ -46,13 +46,14 @@ def make_parts(M, N, exact: bool, seed: int, parts=("scale_m", "scale_n", "bias"
     return d
 
 
-def run_epi(dt, A, B, parts, act, tile=None, sa=1.0, sb=1.0, workspace=None, inplace=False):
+def run_epi(dt, A, B, parts, act, tile=None, sa=1.0, sb=1.0, workspace=None, inplace=False,
+            ldc=None, col0=0):
     M, K = A.shape
     N = B.shape[0]
     Ad = dev_bf16(A) if dt == "bf16" else dev_u8(A)
     Bd = dev_bf16(B) if dt == "bf16" else dev_u8(B)
     Bs = dg.shuffle_b(Bd, dtype=dt)
-    buf, C = alloc_c(M, N)
+    buf, C = alloc_c(M, N, ldc, col0=col0)
     kw = {}
     if "scale_m" in parts:
         kw["scale_m"] = torch.from_numpy(parts["scale_m"]).cuda()
@@ -76,7 +77,7 @@ def run_epi(dt, A, B, parts, act, tile=None, sa=1.0, sb=1.0, workspace=None, inp
         dg.gemm_fp8_scaled(Ad, Bs, N, s_a, s_b, out=C, tile=tile, workspace=workspace,
                            activation=act, **kw)
     torch.cuda.synchronize()
-    return host_bits(C), guard_untouched(buf, M, N)
+    return host_bits(C), guard_untouched(buf, M, N, col0)
 
 
 def oracle_epi(dt, A, B, parts, act, sa=1.0, sb=1.0):
@@ -233,3 +234,19 @@ def test_mul_staging_paths(tile, N, inplace):
     C, ok = run_epi("bf16", A, B, parts, "relu", tile, inplace=inplace)
     assert ok
     check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], f"{tile.name} N={N}")
+
+
+@pytest.mark.parametrize("tile", [dg.tiled(128, 256, 4, 32), dg.tiled_ab(256, 256, 8, 32),
+                                  dg.tiled_pp(256, 256), dg.tiled(64, 64)],
+                         ids=lambda t: t.name)
+@pytest.mark.parametrize("inplace", [False, True], ids=["mul", "mul_in_place"])
+def test_mul_with_odd_c_pitch(tile, inplace):
+    """C rows at odd 2-byte phases: the multiplier is staged at each row's
+    phase, element by element, also when its own rows are 16-byte aligned
+    (a separate multiplier with N % 8 == 0), and when it is C itself."""
+    M, N, K = 300, 272, 192
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=38)
+    parts = make_parts(M, N, True, 9)
+    C, ok = run_epi("bf16", A, B, parts, "relu", tile, inplace=inplace, ldc=N + 5, col0=3)
+    assert ok
+    check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], f"{tile.name} odd pitch")

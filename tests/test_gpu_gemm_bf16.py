@@ -162,6 +162,25 @@ def test_guard_band_and_ldc(M, N, ldc_extra, col0):
     check_exact(C, oracle_full("bf16", A, B), f"ldc+{ldc_extra} col0={col0}")
 
 
+ODD_PITCH_TILES = [dg.tiled(64, 64), dg.tiled(256, 128, 8), dg.tiled(128, 128, 4, 32),
+                   dg.tiled(128, 256, 4, 32), dg.tiled(256, 256, 8, 32), dg.tiled_ab(256, 128, 4),
+                   dg.tiled_ab(256, 128, 8, 32), dg.tiled_ab(128, 128, 4, 32),
+                   dg.tiled_ab(256, 256, 8, 32), dg.tiled_pp(256, 256)]
+
+
+@pytest.mark.parametrize("ldc_extra,col0", [(1, 0), (4, 3), (0, 7), (6, 2)])
+@pytest.mark.parametrize("tile", ODD_PITCH_TILES, ids=lambda t: t.name)
+def test_odd_pitch_every_family(tile, ldc_extra, col0):
+    """C rows at every 2-byte phase: each row segment is staged at its own
+    phase, whole 16-byte pieces go out aligned and the two shared end pieces
+    element by element.  Three column tiles and a ragged one, three row tiles."""
+    M, N, K = 530, 2 * 256 + 45, 96
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=ldc_extra + 10 * col0)
+    C, ok = run("bf16", A, B, tile=tile, ldc=N + col0 + ldc_extra, col0=col0)
+    assert ok, "wrote outside the M x N view"
+    check_exact(C, oracle_full("bf16", A, B), f"{tile.name} ldc+{ldc_extra} col0={col0}")
+
+
 def test_repeatable():
     M, N, K = 597, 11008, 512
     A, B = datagen.make_bf16_pair(M, N, K, "normal", "normal", config=77)

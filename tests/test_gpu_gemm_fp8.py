@@ -107,3 +107,16 @@ def test_guard_band_odd_ldc():
         C, ok = run("fp8", A, B, ldc=ldc, col0=col0)
         assert ok
         check_exact(C, oracle_full("fp8", A, B), f"ldc={ldc} col0={col0}")
+
+
+@pytest.mark.parametrize("tile", [dg.tiled(128, 128, 4, 32), dg.tiled_ab(256, 256, 8, 32),
+                                  dg.tiled_pp(256, 256)], ids=lambda t: t.name)
+def test_odd_pitch_large_tiles(tile):
+    """Rows at odd 2-byte phases on the large e4m3 rungs, several tiles and a
+    ragged edge in both directions."""
+    M, N, K = 530, 2 * 256 + 45, 192
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=5, smallint=True)
+    for ldc, col0 in ((N + 1, 0), (N + 10, 5)):
+        C, ok = run("fp8", A, B, tile=tile, sa=0.5, sb=2.0, ldc=ldc, col0=col0)
+        assert ok
+        check_exact(C, oracle_full("fp8", A, B, 0.5, 2.0), f"{tile.name} ldc={ldc} col0={col0}")
