@@ -153,6 +153,13 @@ def make_inputs(name: str):
     return A, B, s_a, s_b
 
 
+def cold_copies(per_set: float) -> int:
+    """Operand sets whose total exceeds twice the Infinity Cache, so that a
+    rotation over them reads every operand from HBM (small shards included:
+    each set is touched again only after the others have passed through)."""
+    return max(1, int(2 * MALL_BYTES // per_set) + 1)
+
+
 def gpu_setup(name: str, copies: int):
     import numpy as np
     import torch
@@ -230,9 +237,8 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
-    if copies is None:   # enough operand sets to exceed twice the Infinity Cache
-        per_set = alg_bytes(M, N, K, dt)
-        copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
+    if copies is None:
+        copies = cold_copies(alg_bytes(M, N, K, dt))
     if setup is None:
         setup = gpu_setup(name, copies)
     sets, (s_a, s_b), shuffle_us = setup
@@ -362,7 +368,7 @@ def epilogue_compare(name: str, spec: str, reps: int, ws_mib: int) -> int:
         return 2
     act = acts[0] if acts else None
     per_set = alg_bytes(M, N, K, dt) + (2 * M * N if "mul" in parts else 0)
-    copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
+    copies = cold_copies(per_set)
     sets, (s_a, s_b), _ = gpu_setup(name, copies)
     g = torch.Generator(device="cuda").manual_seed(7)
     kw = {}
@@ -653,9 +659,7 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> in
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
-    per_set = alg_bytes(M, N, K, dt)
-    copies = max(1, min(8, int(2 * MALL_BYTES // per_set) + 1))
-    setup = gpu_setup(name, copies)
+    setup = gpu_setup(name, cold_copies(alg_bytes(M, N, K, dt)))
     tiles = dg.all_tiles(M, dt)
     # split-K variants of the rungs that leave CUs idle, one per distinct
     # slice count after the library lowers it

@@ -35,6 +35,15 @@ __device__ __forceinline__ i32x4 load16(rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+// The same with the non-temporal cache hint (bit 1 of the cache-policy
+// operand, `nt` on gfx950), for data read exactly once: a decode weight
+// streamed from HBM.  Measured on MI355X with cold operands, the skinny
+// kernel's weight stream is 4-12 % faster with it.
+__device__ __forceinline__ i32x4 load16_nt(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+
 __device__ __forceinline__ void store16(rsrc_t r, uint32_t off, i32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);

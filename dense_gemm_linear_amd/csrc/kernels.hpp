@@ -1273,7 +1273,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs p)
 // waves split K; each streams its K range of the preshuffled B once, with two
 // batches of U k-tiles of loads in flight (the next batch is issued before
 // the current one is consumed, so the HBM latency is paid once per wave, not
-// once per batch), and reads A straight from global (small; it stays in L2).
+// once per batch; B with the non-temporal hint, as no other workgroup reads
+// it), and reads A straight from global (small; it stays in L2).
 // Partial sums are reduced in LDS in a fixed order: deterministic, no
 // workspace.
 template <int DT, int MR, int NB, int W, bool EPI>
@@ -1321,7 +1322,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs p)
                     uint32_t off = (uint32_t)(j * p.KB + kb) * 1024u + lane * 16;
                     if (!kv || kb >= p.KB)
                         off = kOOB;
-                    bv[set][u][j][c] = load16(rb, off);
+                    bv[set][u][j][c] = load16_nt(rb, off);   // each B byte is read once
                 }
 #pragma unroll
             for (int mi = 0; mi < MR; ++mi)
