@@ -9,6 +9,7 @@ import functools
 
 import numpy as np
 import pytest
+import torch
 
 import datagen
 import dense_gemm_linear_amd as dg
@@ -71,14 +72,24 @@ def test_small_shapes_full(shape):
     check_exact(C, oracle_full("bf16", A, B), f"{shape} smallint")
 
 
+BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selector
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("smallint", [False, True], ids=["general", "smallint"])
-def test_workload_shapes_sampled(name, smallint):
+@pytest.mark.parametrize("ws", [0, BENCH_WORKSPACE], ids=["no_ws", "bench_ws"])
+def test_workload_shapes_sampled(name, smallint, ws):
+    """ws = 0: the library's choice without a workspace; bench_ws: the tile
+    bench.py times (chosen with its 64 MiB workspace), run only where that
+    choice differs."""
     M, N, K, da, sa, db, sb, cfg = WORKLOADS[name]
+    tile = dg.select_tile(M, N, K, "bf16", workspace_bytes=ws)
+    if ws and tile.name == dg.select_tile(M, N, K, "bf16").name:
+        pytest.skip("the workspace does not change the tile: covered by no_ws")
     A, B = inputs(M, N, K, da, sa, db, sb, cfg, smallint)
-    print(f"[gemm_bf16 {name} {M}x{N}x{K} smallint={smallint} tile="
-          f"{dg.select_tile(M, N, K, 'bf16').name}]", flush=True)
-    C, ok = run("bf16", A, B)
+    print(f"[gemm_bf16 {name} {M}x{N}x{K} smallint={smallint} tile={tile.name}]", flush=True)
+    workspace = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda") if ws else None
+    C, ok = run("bf16", A, B, workspace=workspace)
     assert ok
     rows, cols = sample_lines(M), sample_lines(N)
     ms, ns, vals, absv = oracle_lines("bf16", A, B, rows, cols)

@@ -8,6 +8,7 @@ with the scales applied, plus the per-element bound of parity.py.
 """
 import numpy as np
 import pytest
+import torch
 
 import datagen
 import dense_gemm_linear_amd as dg
@@ -36,16 +37,24 @@ def test_small_shapes_full(shape):
         check_exact(C, oracle_full("fp8", A, B, s1, s2), f"{shape} smallint scales {s1},{s2}")
 
 
+BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selector
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("smallint", [False, True], ids=["general", "smallint"])
-def test_workload_shapes_sampled(name, smallint):
+@pytest.mark.parametrize("ws", [0, BENCH_WORKSPACE], ids=["no_ws", "bench_ws"])
+def test_workload_shapes_sampled(name, smallint, ws):
+    """ws as in the bf16 test: the bench's tile is run where it differs."""
     M, N, K, cfg = WORKLOADS[name]
+    tile = dg.select_tile(M, N, K, "fp8", workspace_bytes=ws)
+    if ws and tile.name == dg.select_tile(M, N, K, "fp8").name:
+        pytest.skip("the workspace does not change the tile: covered by no_ws")
     A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=cfg, smallint=smallint)
     if smallint:
         sa, sb = 2.0 ** -3, 2.0 ** 2
-    print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint} tile="
-          f"{dg.select_tile(M, N, K, 'fp8').name}]", flush=True)
-    C, ok = run("fp8", A, B, sa=sa, sb=sb)
+    print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint} tile={tile.name}]", flush=True)
+    workspace = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda") if ws else None
+    C, ok = run("fp8", A, B, sa=sa, sb=sb, workspace=workspace)
     assert ok
     rows, cols = sample_lines(M), sample_lines(N)
     ms, ns, vals, absv = oracle_lines("fp8", A, B, rows, cols, scale=sa * sb)
