@@ -20,6 +20,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "internal.hpp"
 
 namespace dg {
@@ -392,7 +395,8 @@ void choose_tile_model(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t 
 // A shape measured on this chip (calibration.inc) gets its measured best tile
 // when the device has the CU count the sweep ran on and the workspace covers
 // it; any other shape is priced by the model.
-void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, gemm_tile* out)
+void choose_tile_uncached(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                          gemm_tile* out)
 {
     if (cus == 256) {
         const int e = dt == GEMM_BF16 ? 2 : 1;
@@ -503,6 +507,54 @@ void choose_tile_model(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t 
         });
     }
     *out = have ? best.t : best_screened.t;
+}
+
+// The choice is a pure function of its arguments, so it is kept per
+// (M, N, K, dtype, CUs, workspace bytes): pricing the ladder costs several
+// microseconds of host time, as long as a decode kernel runs.  At most
+// kCacheMax shapes are kept (the table is emptied when it fills).
+namespace {
+struct ShapeKey {
+    int64_t M, N, K;
+    int dt, cus;
+    size_t ws;
+    bool operator==(const ShapeKey& o) const
+    {
+        return M == o.M && N == o.N && K == o.K && dt == o.dt && cus == o.cus && ws == o.ws;
+    }
+};
+struct ShapeHash {
+    size_t operator()(const ShapeKey& k) const
+    {
+        uint64_t h = 1469598103934665603ull;   // FNV-1a over the fields
+        const uint64_t f[6] = {(uint64_t)k.M, (uint64_t)k.N, (uint64_t)k.K, (uint64_t)k.dt,
+                               (uint64_t)k.cus, (uint64_t)k.ws};
+        for (uint64_t v : f)
+            h = (h ^ v) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+constexpr size_t kCacheMax = 4096;
+std::mutex g_cache_mu;
+std::unordered_map<ShapeKey, gemm_tile, ShapeHash> g_cache;
+}  // namespace
+
+void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, gemm_tile* out)
+{
+    const ShapeKey key{M, N, K, dt, cus, ws_bytes};
+    {
+        std::lock_guard<std::mutex> lock(g_cache_mu);
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            *out = it->second;
+            return;
+        }
+    }
+    choose_tile_uncached(M, N, K, dt, cus, ws_bytes, out);
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    if (g_cache.size() >= kCacheMax)
+        g_cache.clear();
+    g_cache.emplace(key, *out);
 }
 
 }  // namespace dg

@@ -168,7 +168,10 @@ typedef struct {
  * pad the output past 1.25x its real area unless nothing else fits (FlyDSL
  * PR #1303 page, autotuner changes), checks the LDS and register budget
  * ("GEMM Optimization Guide" page, sections 2.4 and 10), and routes small M
- * to the skinny kernel.  Ties are broken by a fixed order.
+ * to the skinny kernel.  Ties are broken by a fixed order.  The choice is
+ * kept per (M, N, K, dtype, CU count, workspace bytes) in a table shared by
+ * all threads (mutex-guarded, at most 4096 shapes, emptied when full), so a
+ * repeated shape costs a lookup instead of pricing the ladder.
  *
  * Returns GEMM_ERR_INVALID_VALUE for out == NULL or negative sizes,
  * GEMM_ERR_HIP when num_cus == 0 and the device query fails.

@@ -322,3 +322,20 @@ def test_transpose_and_shuffle_b_t_argument_checks():
     assert s(PA + 1, 64, PB, 64, 64, 0, None) == E                  # Bt not 2-byte aligned
     assert s(PA, 64, PB, 64, 40, 0, None) == U                      # bf16 K % 16
     assert s(PA, 64, PB, 64, 96, 1, None) == U                      # e4m3 K % 64
+
+
+def test_select_tile_cache_consistent():
+    """select_tile keeps its choice per shape; repeated calls, and calls after
+    the table has filled (4096 shapes) and been emptied, give the same tile."""
+    shapes = [(m, n, k) for m in (1, 48, 597, 4096) for n in (1376, 4095, 11008) for k in (512, 4096)]
+    first = {s: dg.select_tile(*s, "bf16", 256) for s in shapes}
+    for i in range(4200):                      # more distinct shapes than the table holds
+        dg.select_tile(1 + i, 64 + (i % 7), 128, "bf16", 256)
+    for s in shapes:
+        again = dg.select_tile(*s, "bf16", 256)
+        assert again.name == first[s].name and again.predicted_us == first[s].predicted_us, s
+    # the workspace size is part of the key
+    a = dg.select_tile(48, 4096, 4096, "bf16", 256)
+    b = dg.select_tile(48, 4096, 4096, "bf16", 256, workspace_bytes=64 << 20)
+    assert a.kernel == dg.GEMM_KERNEL_SKINNY and b.k_split > 1
+    assert dg.select_tile(48, 4096, 4096, "bf16", 256).name == a.name
