@@ -12,7 +12,9 @@ Measurement:
   * W untimed warm-up calls, then exactly K calls bracketed by
     torch.cuda.synchronize() on both sides, timed with HIP events on the
     stream the kernels run on (torch's current stream); the calls run back
-    to back, so total time / K is the average launch duration.
+    to back, so total time / K is the average launch duration.  The K calls
+    are replayed from one HIP graph, behind a short spin kernel so that the
+    start event is reached after the graph has been submitted.
   * The K calls rotate over enough copies of (A, Bs, C) to exceed twice the
     256 MB Infinity Cache, so every call reads its operands from HBM.
   * `roofline`: algorithmic flops (2MNK, "GEMM Optimization Guide" page,
@@ -269,6 +271,7 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_stream()
         wall0 = time.perf_counter()
         t0.record()
         g.replay()
@@ -304,6 +307,16 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     }
 
 
+def hold_stream(stream=None):
+    """Enqueue about a millisecond of device work (a bounded spin kernel) on
+    the stream, ahead of a timed graph replay: the GPU then reaches the start
+    event only after the host has submitted the graph, so the event pair times
+    the kernels back to back and not the host's submission of the graph."""
+    import torch
+    with torch.cuda.stream(stream or torch.cuda.current_stream()):
+        torch.cuda._sleep(2_000_000)
+
+
 def time_graph(call, reps: int, trials: int = 1) -> float:
     """Per-launch time of `call` (launches only: no allocation, no memset,
     the kernels write every output element themselves) from R calls captured
@@ -327,6 +340,7 @@ def time_graph(call, reps: int, trials: int = 1) -> float:
     per = []
     for _ in range(trials):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_stream()
         t0.record()
         g.replay()
         t1.record()
