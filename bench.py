@@ -320,25 +320,30 @@ def hold_stream(stream=None):
 def time_graph(call, reps: int, trials: int = 1) -> float:
     """Per-launch time of `call` (launches only: no allocation, no memset,
     the kernels write every output element themselves) from R calls captured
-    in one HIP graph: the median over `trials` replays of replay time / R.
-    Kernels shorter than a Python launch are timed without the host's
-    submission gaps this way."""
+    in one HIP graph: the median over `trials` graphs of replay time / R.
+    Each trial has a graph of its own over the next R operand sets (call(i)
+    takes set i mod the number of copies), replayed once, so a small
+    workload's trials do not re-read the sets the previous one left in the
+    Infinity Cache.  Kernels shorter than a Python launch are timed without
+    the host's submission gaps this way."""
     import torch
     for i in range(3):
         call(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
+    graphs = []
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(reps):
-                call(i)
+    for t in range(trials):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(reps):
+                    call(3 + t * reps + i)
+        graphs.append(g)
     torch.cuda.current_stream().wait_stream(s)
-    g.replay()
     torch.cuda.synchronize()
     per = []
-    for _ in range(trials):
+    for g in graphs:
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         hold_stream()
         t0.record()
@@ -346,7 +351,7 @@ def time_graph(call, reps: int, trials: int = 1) -> float:
         t1.record()
         torch.cuda.synchronize()
         per.append(t0.elapsed_time(t1) * 1e3 / reps)
-    del g
+    del graphs
     return sorted(per)[len(per) // 2]
 
 
