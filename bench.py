@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -132,6 +133,17 @@ WORKLOADS = {
     "fp8_4096cube": (4096, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 5),
     "fp8_tp8_up_597x1376x4096": (597, 1376, 4096, "fp8", "normal", 1.0, "normal", 1.0, 64),
     "fp8_32x4096": (32, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 51),
+    # held out of the selector's calibration (their sweeps are kept apart, in
+    # calibration/mi355x_holdout.jsonl): how well it prices shapes it never saw
+    "bf16_256x4096x4096": (256, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 91),
+    "bf16_2048x4096x4096": (2048, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 92),
+    "bf16_1024x14336x4096": (1024, 14336, 4096, "bf16", "normal", 1.0, "normal", 0.02, 93),
+    "bf16_1024x4096x14336": (1024, 4096, 14336, "bf16", "normal", 1.0, "normal", 0.02, 94),
+    "bf16_16x14336x4096": (16, 14336, 4096, "bf16", "normal", 1.0, "normal", 0.02, 95),
+    "bf16_4x4096x11008": (4, 4096, 11008, "bf16", "normal", 1.0, "normal", 0.02, 96),
+    "bf16_8192x1024x1024": (8192, 1024, 1024, "bf16", "normal", 1.0, "normal", 0.02, 97),
+    "bf16_333x5000x2048": (333, 5000, 2048, "bf16", "normal", 1.0, "normal", 0.02, 98),
+    "fp8_1024x14336x4096": (1024, 14336, 4096, "fp8", "normal", 1.0, "normal", 1.0, 99),
 }
 HEADLINE = "bf16_4096cube"
 DECODE = "bf16_llama_decode"
@@ -573,11 +585,16 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
+    ap.add_argument("--regret", default=None, metavar="SWEEP_JSONL",
+                    help="host only: the selector's pick against the fastest tile of every workload "
+                         "in a --sweep output file")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
               "(the sharded design is described, not built).", file=sys.stderr)
         return 2
+    if args.regret:               # host-only: reads sweep lines, prices with the library
+        return regret_report(args.regret, args.workspace_mib)
     if args.traffic_summary:      # host-only: parses counter files
         return traffic_summary(args.workload, args.tile, *args.traffic_summary)
     import torch
@@ -668,6 +685,39 @@ def main(argv=None):
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(name)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def regret_report(path: str, ws_mib: int = WORKSPACE_MIB) -> int:
+    """The selector's pick (at 256 CUs, with a ws_mib workspace) against the
+    fastest tile of each workload in a `--sweep` output file: one JSON line per
+    workload and a summary.  Host only."""
+    import dense_gemm_linear_amd as dg
+    res = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith('{"sweep":'):
+                d = json.loads(line)
+                res.setdefault(d["sweep"], {})[d["tile"]] = d["kernel_us_median"]
+    regrets = []
+    for name in sorted(res):
+        r = res[name]
+        M, N, K, dt = WORKLOADS[name][:4]
+        t = dg.select_tile(M, N, K, dt, CUS, workspace_bytes=ws_mib << 20)
+        best = min(r, key=r.get)
+        got = r.get(t.name)
+        reg = round(got / r[best], 4) if got else None
+        regrets.append(reg)
+        print(json.dumps({"workload": name, "selected": t.name, "selected_us": got, "best": best,
+                          "best_us": r[best], "regret": reg}))
+    known = [x for x in regrets if x is not None]
+    print(json.dumps({"regret_summary": path, "workloads": len(regrets),
+                      "at_best": sum(1 for x in known if x == 1.0),
+                      "within_5pct": sum(1 for x in known if x <= 1.05),
+                      "worst": max(known) if known else None,
+                      "geomean": round(math.exp(sum(math.log(x) for x in known) / len(known)), 4)
+                      if known else None,
+                      "unmeasured_picks": regrets.count(None)}))
     return 0
 
 
