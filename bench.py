@@ -133,6 +133,15 @@ WORKLOADS = {
     "fp8_4096cube": (4096, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 5),
     "fp8_tp8_up_597x1376x4096": (597, 1376, 4096, "fp8", "normal", 1.0, "normal", 1.0, 64),
     "fp8_32x4096": (32, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 51),
+    # more small-M shapes for the selector's calibration of the skinny rungs
+    "bf16_1x4096x4096": (1, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 71),
+    "bf16_2x8192x8192": (2, 8192, 8192, "bf16", "normal", 1.0, "normal", 0.02, 72),
+    "bf16_16x4096x4096": (16, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 73),
+    "bf16_32x11008x4096": (32, 11008, 4096, "bf16", "normal", 1.0, "normal", 0.02, 74),
+    "bf16_64x4096x4096": (64, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 75),
+    "bf16_1x28672x8192": (1, 28672, 8192, "bf16", "normal", 1.0, "normal", 0.02, 76),
+    "bf16_12x2048x8192": (12, 2048, 8192, "bf16", "normal", 1.0, "normal", 0.02, 77),
+    "fp8_8x11008x4096": (8, 11008, 4096, "fp8", "normal", 1.0, "normal", 1.0, 78),
     # held out of the selector's calibration (their sweeps are kept apart, in
     # calibration/mi355x_holdout.jsonl): how well it prices shapes it never saw
     "bf16_256x4096x4096": (256, 4096, 4096, "bf16", "normal", 1.0, "normal", 0.02, 91),

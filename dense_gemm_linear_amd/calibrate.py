@@ -61,6 +61,12 @@ def split_plan(M, N, K, e, ktb, k_split):
     return math.ceil(nkt / per), per, math.ceil(N / 4) * 4
 
 
+# select_tile drops a tile whose padded output exceeds this multiple of the
+# real one (unless nothing else fits); the fit uses the same rule, so a rung's
+# cost model is fitted on the shapes where it competes
+PAD_LIMIT = 1.25
+
+
 def load_points(paths):
     """(rung key, features, split features, t) per tiled sweep line and
     (skinny key, features, t) per skinny line."""
@@ -87,6 +93,8 @@ def load_points(paths):
             ktb = r["tile_k"] * e
             key = (dt, r["kernel"], r["tm"], r["tn"], r["waves"], r["atom"], r["stages"], ktb)
             tiles = math.ceil(M / r["tm"]) * math.ceil(N / r["tn"])
+            if tiles * r["tm"] * r["tn"] > PAD_LIMIT * M * N:
+                continue   # screened out by select_tile's padding rule: not a candidate here
             S, per, ldw = split_plan(M, N, K, e, ktb, r["k_split"])
             kbytes = K * e if S == 1 else per * ktb
             ncu = math.ceil(tiles * S / CUS)
