@@ -39,7 +39,7 @@ GEMM_KERNEL_TILED_PP = 3
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
            "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex", "shuffle_b_t",
-           "transpose_2d")
+           "transpose_2d", "gemm_plan")
 
 # gemm_activation
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_SILU, GEMM_ACT_GELU_ERF, GEMM_ACT_GELU_TANH = 0, 1, 2, 3, 4
@@ -229,6 +229,10 @@ def _load_lib():
     lib.shuffle_b_t.restype = ctypes.c_int
     lib.transpose_2d.argtypes = [P, I64, P, I64, I64, I64, ctypes.c_int32, P]
     lib.transpose_2d.restype = ctypes.c_int
+    lib.gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int32, ctypes.c_size_t,
+                              ctypes.POINTER(GemmTile), ctypes.POINTER(GemmTile),
+                              ctypes.POINTER(I64)]
+    lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
@@ -268,6 +272,17 @@ def select_tile(M: int, N: int, K: int, dtype="bf16", num_cus: int = 0,
 def workspace_bytes(M: int, N: int, K: int, dtype, tile: Tile) -> int:
     """Device workspace `tile` needs on M x N x K (0 unless it splits K)."""
     return int(lib.gemm_workspace_bytes(M, N, K, _dtype_code(dtype), ctypes.byref(tile.to_c())))
+
+
+def plan(M: int, N: int, K: int, dtype="bf16", num_cus: int = 256, workspace_bytes: int = 0):
+    """The launches a GEMM with tile=None makes: (first tile, second tile or
+    None, columns of the first launch)."""
+    a, b, n = GemmTile(), GemmTile(), ctypes.c_int64(0)
+    st = lib.gemm_plan(M, N, K, _dtype_code(dtype), num_cus, workspace_bytes, ctypes.byref(a),
+                       ctypes.byref(b), ctypes.byref(n))
+    if st != GEMM_OK:
+        raise GemmError("gemm_plan", st)
+    return Tile.from_c(a), (Tile.from_c(b) if n.value < N else None), n.value
 
 
 def tile_check(tile: Tile, M: int, dtype="bf16") -> int:

@@ -115,6 +115,115 @@ bool make_epilogue(const gemm_epilogue* e, int64_t N, Epilogue* out)
     return true;
 }
 
+// One GEMM launch (and its split-K reduction) of a resolved tile.
+hipError_t launch_gemm(int dt, const gemm_tile& t, int idx, const SplitPlan& pl, const void* A,
+                       int64_t lda, const void* Bs, const float* sa, const float* sb, uint16_t* C,
+                       int64_t ldc, int64_t M, int64_t N, int64_t K, const Epilogue& ep, void* ws,
+                       hipStream_t s)
+{
+    const int e = dt == DT_BF16 ? 2 : 1;
+    GemmArgs a;
+    memset(&a, 0, sizeof a);
+    a.A = static_cast<const uint8_t*>(A);
+    a.Bs = static_cast<const uint8_t*>(Bs);
+    a.C = C;
+    a.sa = sa;
+    a.sb = sb;
+    a.lda_b = lda * e;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.KA_b = (int)(K * e);
+    a.KB = (int)((K * e + 63) / 64);
+    a.nkt = (a.KB + 1) / 2;
+    a.tail = (a.KA_b % 128) != 0;
+    a.nblk = (int)((N + 15) / 16);
+    a.c_vec = (((uintptr_t)C & 15u) == 0) && (ldc % 8 == 0);
+    a.splits = pl.S;
+    a.kt_per = pl.kt_per;
+    a.ldw = pl.ldw;
+    a.ws = pl.S > 1 ? static_cast<float*>(ws) : nullptr;
+    a.ep = ep;
+    if (t.kernel == GEMM_KERNEL_SKINNY)
+        return launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
+    a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
+    a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
+    hipError_t err = launch_tiled_rung(t.kernel, dt, idx, a, s);
+    if (err == hipSuccess && pl.S > 1)
+        err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, ep, s);
+    return err;
+}
+
+// Columns of the first of two launches when the chosen one-pass tiled tile
+// would run a last round of tiles that fills at most a quarter of the CUs
+// after two or more full rounds (0: one launch).  The first launch takes the
+// columns whose tiles fill the full rounds exactly or nearly; the second the
+// rest.
+int64_t tail_split_columns(const gemm_tile& t, const SplitPlan& pl, int64_t M, int64_t N, int cus)
+{
+    if (t.kernel == GEMM_KERNEL_SKINNY || pl.S > 1 || cus <= 0)
+        return 0;
+    const int64_t tiles_m = (M + t.tile_m - 1) / t.tile_m;
+    const int64_t tiles_n = (N + t.tile_n - 1) / t.tile_n;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t full = tiles / cus, left = tiles % cus;
+    if (full < 2 || left == 0 || 4 * left > cus)
+        return 0;
+    const int64_t n_main = full * cus / tiles_m * t.tile_n;
+    return n_main > 0 && n_main < N ? n_main : 0;
+}
+
+// The launches of a GEMM whose tile the library chooses: one tile for all
+// N columns, or, when the chosen one-pass tile would leave a last round of
+// tiles that fills at most a quarter of the CUs (tail_split_columns), the
+// columns that fill whole rounds with it and the rest as a second GEMM with a
+// tile chosen for that narrower shape -- if that second GEMM costs less than
+// the stray round.  Measured on MI355X: the stray round costs about 40 % of a
+// round (its tiles start while the last full round drains), and a small GEMM
+// at least about 6 us (launch, cold prologue, epilogue), more than the model
+// gives it.  False if a chosen tile names no rung (never, for the selector's
+// own choices).
+struct AutoPlan {
+    gemm_tile t1, t2;
+    int idx1, idx2;
+    SplitPlan pl1, pl2;
+    int64_t n1;    // columns of the first launch; N: a single launch
+};
+
+bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, AutoPlan* ap)
+{
+    const int e = dt == DT_BF16 ? 2 : 1;
+    memset(ap, 0, sizeof *ap);
+    ap->n1 = N;
+    choose_tile(M, N, K, dt, cus, ws_bytes, &ap->t1);
+    if (!resolve_tile(ap->t1, M, e, &ap->idx1))
+        return false;
+    ap->pl1 = tile_split(ap->t1, ap->idx1, M, N, K, e);
+    if (ap->pl1.ws_bytes > (int64_t)ws_bytes)
+        return false;
+    const int64_t n1 = tail_split_columns(ap->t1, ap->pl1, M, N, cus);
+    if (n1 == 0)
+        return true;
+    gemm_tile t2;
+    int idx2 = -1;
+    choose_tile(M, N - n1, K, dt, cus, ws_bytes, &t2);
+    const int64_t tiles = ((M + ap->t1.tile_m - 1) / ap->t1.tile_m) *
+                          ((N + ap->t1.tile_n - 1) / ap->t1.tile_n);
+    const double round_us = ap->t1.predicted_us / (double)((tiles + cus - 1) / cus);
+    constexpr double kMinGemmUs = 6.0;
+    if (!resolve_tile(t2, M, e, &idx2) ||
+        std::max((double)t2.predicted_us, kMinGemmUs) >= 0.4 * round_us)
+        return true;
+    const SplitPlan pl2 = tile_split(t2, idx2, M, N - n1, K, e);
+    if (pl2.ws_bytes > (int64_t)ws_bytes)
+        return true;
+    ap->t2 = t2;
+    ap->idx2 = idx2;
+    ap->pl2 = pl2;
+    ap->n1 = n1;
+    return true;
+}
+
 gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const float* sa,
                      const float* sb, uint16_t* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                      const gemm_tile* tile, const gemm_epilogue* epi, void* ws, size_t ws_bytes,
@@ -168,45 +277,34 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     if (K == 0)
         return launch_zero_c(C, ldc, M, N, ep, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     if (!tile) {
-        choose_tile(M, N, K, dt, cus, ws_bytes, &t);
-        if (!resolve_tile(t, M, e, &idx))
+        AutoPlan ap;
+        if (!plan_auto(M, N, K, dt, cus, ws_bytes, &ap))
             return GEMM_ERR_UNSUPPORTED;   // the selector names only rungs that exist
-        pl = tile_split(t, idx, M, N, K, e);
-        if (pl.ws_bytes > (int64_t)ws_bytes)
-            return GEMM_ERR_UNSUPPORTED;   // the selector keeps within the workspace
+        t = ap.t1;
+        idx = ap.idx1;
+        pl = ap.pl1;
+        if (ap.n1 < N) {
+            const int64_t n1 = ap.n1;
+            const int64_t be = 64 * ((K * e + 63) / 64) * 16;   // Bs bytes per 16 columns
+            Epilogue ep2 = ep;
+            if (ep2.bias)
+                ep2.bias += n1;
+            if (ep2.scale_n)
+                ep2.scale_n += n1;
+            if (ep2.mul) {
+                ep2.mul += n1;
+                ep2.mul_vec = ((uintptr_t)ep2.mul & 15u) == 0 && ep2.ldmul % 8 == 0;
+            }
+            hipError_t err =
+                launch_gemm(dt, t, idx, pl, A, lda, Bs, sa, sb, C, ldc, M, n1, K, ep, ws, s);
+            if (err == hipSuccess)
+                err = launch_gemm(dt, ap.t2, ap.idx2, ap.pl2, A, lda,
+                                  static_cast<const uint8_t*>(Bs) + n1 / 16 * be, sa, sb, C + n1,
+                                  ldc, M, N - n1, K, ep2, ws, s);
+            return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+        }
     }
-    GemmArgs a;
-    memset(&a, 0, sizeof a);
-    a.A = static_cast<const uint8_t*>(A);
-    a.Bs = static_cast<const uint8_t*>(Bs);
-    a.C = C;
-    a.sa = sa;
-    a.sb = sb;
-    a.lda_b = lda * e;
-    a.ldc = ldc;
-    a.M = (int)M;
-    a.N = (int)N;
-    a.KA_b = (int)(K * e);
-    a.KB = (int)((K * e + 63) / 64);
-    a.nkt = (a.KB + 1) / 2;
-    a.tail = (a.KA_b % 128) != 0;
-    a.nblk = (int)((N + 15) / 16);
-    a.c_vec = (((uintptr_t)C & 15u) == 0) && (ldc % 8 == 0);
-    a.splits = pl.S;
-    a.kt_per = pl.kt_per;
-    a.ldw = pl.ldw;
-    a.ws = pl.S > 1 ? static_cast<float*>(ws) : nullptr;
-    a.ep = ep;
-    hipError_t err;
-    if (t.kernel == GEMM_KERNEL_SKINNY) {
-        err = launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
-    } else {
-        a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
-        a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
-        err = launch_tiled_rung(t.kernel, dt, idx, a, s);
-        if (err == hipSuccess && pl.S > 1)
-            err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, ep, s);
-    }
+    const hipError_t err = launch_gemm(dt, t, idx, pl, A, lda, Bs, sa, sb, C, ldc, M, N, K, ep, ws, s);
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -353,6 +451,22 @@ gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_
     hipError_t err = dg::launch_transpose(src, ld_src, dst, ld_dst, rows, cols, elem_bytes,
                                           reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
+                      size_t workspace_bytes, gemm_tile* first, gemm_tile* second,
+                      int64_t* first_columns)
+{
+    if (!first || !second || !first_columns || M <= 0 || N <= 0 || K <= 0 || num_cus <= 0 ||
+        (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
+        return GEMM_ERR_INVALID_VALUE;
+    dg::AutoPlan ap;
+    if (!dg::plan_auto(M, N, K, (int)dtype, num_cus, workspace_bytes, &ap))
+        return GEMM_ERR_UNSUPPORTED;
+    *first = ap.t1;
+    *second = ap.t2;
+    *first_columns = ap.n1;
+    return GEMM_OK;
 }
 
 gemm_status gemm_tile_check(const gemm_tile* tile, int64_t M, gemm_dtype dtype)

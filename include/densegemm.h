@@ -269,8 +269,10 @@ gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_
  *   Bs  device, the weight B [N, K] preshuffled by shuffle_b(..., GEMM_BF16).
  *   C   device, bf16 bits, row-major [M, ldc], ldc >= N, 2-byte aligned; only
  *       the M x N region is written (columns N..ldc-1 are untouched).
- *   tile  NULL = select_tile(M, N, K, GEMM_BF16, <device CUs>); otherwise a
- *         forced configuration, validated against the shape.
+ *   tile  NULL = select_tile(M, N, K, GEMM_BF16, <device CUs>), or the two
+ *         launches over column ranges gemm_plan describes when that tile
+ *         would leave a nearly empty last round; otherwise a forced
+ *         configuration, validated against the shape (always one launch).
  *
  * The fp32 sum is rounded to bf16 to nearest, ties to even ("GEMM
  * Optimization Guide" page, section 7.1, direct-store epilogue: the
@@ -316,8 +318,9 @@ gemm_status gemm_fp8_scaled(const uint8_t* A, int64_t lda, const void* Bs, const
  *                    allowed with workspace_bytes == 0.  Its contents on
  *                    entry are ignored and on return are unspecified; calls
  *                    that share one workspace must not overlap in time.
- *   tile             NULL = select_tile_ws(..., workspace_bytes, ...);
- *                    forced split-K tiles need gemm_workspace_bytes(tile).
+ *   tile             NULL = select_tile_ws(..., workspace_bytes, ...) (or
+ *                    gemm_plan's two launches, as for gemm_bf16); forced
+ *                    split-K tiles need gemm_workspace_bytes(tile).
  *
  * The product is the same as without split-K up to fp32 summation order:
  * slice partials are fp32 and are added in a fixed order, so a given tile
@@ -357,6 +360,29 @@ gemm_status gemm_fp8_scaled_ex(const uint8_t* A, int64_t lda, const void* Bs,
                                int64_t ldc, int64_t M, int64_t N, int64_t K,
                                const gemm_tile* tile, const gemm_epilogue* epilogue,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemm_plan -- the launches gemm_bf16 / gemm_fp8_scaled (and their _ws / _ex
+ * forms with `workspace_bytes`) make for an M x N x K GEMM when the caller
+ * passes tile == NULL, on a device with num_cus compute units.  Pure host
+ * function, no device access.
+ *
+ * Usually one launch: *first = select_tile_ws(...), *first_columns = N and
+ * *second zeroed.  When the chosen one-pass tiled tile would run two or more
+ * full rounds of tiles over the CUs and then a last round that fills at most
+ * a quarter of them (wave quantization, TraceLens GEMM analysis page), the
+ * columns [0, *first_columns) that fill whole rounds run with *first and the
+ * rest as a second GEMM with *second, chosen for that narrower shape -- if
+ * its cost, at least about 6 us, is below 40 % of one round's, what such a
+ * stray round measured on MI355X.  Both launches are enqueued on the caller's
+ * stream, in that order; the outputs they write are disjoint.
+ *
+ * GEMM_ERR_INVALID_VALUE for a NULL output, M, N or K <= 0, num_cus <= 0 or
+ * an unknown dtype.
+ */
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
+                      size_t workspace_bytes, gemm_tile* first, gemm_tile* second,
+                      int64_t* first_columns);
 
 /*
  * gemm_tile_check -- would `tile`, forced on gemm_bf16 (dtype GEMM_BF16) or

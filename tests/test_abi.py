@@ -339,3 +339,25 @@ def test_select_tile_cache_consistent():
     b = dg.select_tile(48, 4096, 4096, "bf16", 256, workspace_bytes=64 << 20)
     assert a.kernel == dg.GEMM_KERNEL_SKINNY and b.k_split > 1
     assert dg.select_tile(48, 4096, 4096, "bf16", 256).name == a.name
+
+
+def test_gemm_plan_splits_a_stray_last_round():
+    """gemm_plan: lm_head's 788 tiles of 256 x 256 (3 full rounds + 20) run
+    as 49152 columns with that tile and 1105 with their own; shapes whose
+    rounds are full, or whose rounds are too short to pay a second launch,
+    run as one."""
+    first, second, n1 = dg.plan(1024, 50257, 512, "bf16", 256, 0)
+    assert (first.tile_m, first.tile_n, n1) == (256, 256, 49152)
+    assert second is not None and dg.tile_check(second, 1024, "bf16") == dg.GEMM_OK
+    assert first.name == dg.select_tile(1024, 50257, 512, "bf16", 256).name
+    for shape in ((4096, 4096, 4096), (512, 50257, 256), (1, 11008, 4096), (597, 11008, 4096)):
+        f, s, n = dg.plan(*shape, "bf16", 256, 0)
+        assert s is None and n == shape[1], shape
+        assert f.name == dg.select_tile(*shape, "bf16", 256).name
+    P = dg.lib.gemm_plan
+    t1, t2, n = dg.GemmTile(), dg.GemmTile(), ctypes.c_int64()
+    for bad in ((0, 16, 16, 0, 256), (16, 16, 16, 0, 0), (16, 16, 16, 7, 256)):
+        M, N, K, dt, cus = bad
+        assert P(M, N, K, dt, cus, 0, ctypes.byref(t1), ctypes.byref(t2), ctypes.byref(n)) == \
+            dg.GEMM_ERR_INVALID_VALUE
+    assert P(16, 16, 16, 0, 256, 0, None, ctypes.byref(t2), ctypes.byref(n)) == dg.GEMM_ERR_INVALID_VALUE

@@ -236,6 +236,20 @@ def test_mul_staging_paths(tile, N, inplace):
     check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], f"{tile.name} N={N}")
 
 
+@pytest.mark.parametrize("inplace", [False, True], ids=["mul", "mul_in_place"])
+def test_epilogue_across_two_launches(inplace):
+    """1024 x 50257 x 512 runs as two GEMMs over column ranges (the chosen
+    tile's last round would be nearly empty, gemm_plan): the second one's
+    bias, column scales and multiplier start at the first's last column."""
+    M, N, K = 1024, 50257, 512
+    assert dg.plan(M, N, K, "bf16", 256, 0)[1] is not None, "shape no longer splits"
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=212)
+    parts = make_parts(M, N, True, 13)
+    C, ok = run_epi("bf16", A, B, parts, "relu", None, inplace=inplace)
+    assert ok
+    check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], "epilogue across two launches")
+
+
 @pytest.mark.parametrize("tile", [dg.tiled(128, 256, 4, 32), dg.tiled_ab(256, 256, 8, 32),
                                   dg.tiled_pp(256, 256), dg.tiled(64, 64)],
                          ids=lambda t: t.name)

@@ -192,6 +192,29 @@ def test_odd_pitch_every_family(tile, ldc_extra, col0):
     check_exact(C, oracle_full("bf16", A, B), f"{tile.name} ldc+{ldc_extra} col0={col0}")
 
 
+@functools.lru_cache(maxsize=1)
+def lmhead_smallint():
+    """Small-integer lm_head inputs and their oracle product (shared by cases)."""
+    A, B = datagen.make_bf16_pair(1024, 50257, 512, "smallint", "smallint", config=211)
+    return A, B, oracle_full("bf16", A, B)
+
+
+@pytest.mark.parametrize("ldc_extra,col0", [(0, 0), (3, 1)])
+def test_ragged_last_round_two_launches(ldc_extra, col0):
+    """1024 x 50257 x 512 (lm_head): the chosen 256 x 256 tile would run 3
+    full rounds of 256 tiles and a fourth of 20, so the library runs the first
+    49152 columns with it and the other 1105 as a second GEMM with a tile of
+    their own (gemm_plan).  Every output against the oracle, bit-exact."""
+    M, N, K = 1024, 50257, 512
+    first, second, n1 = dg.plan(M, N, K, "bf16", 256, 0)
+    print(f"[two launches {M}x{N}x{K}: {first.name} x {n1} + {second and second.name}]", flush=True)
+    assert second is not None and n1 == 49152, "shape no longer splits"
+    A, B, ref = lmhead_smallint()
+    C, ok = run("bf16", A, B, ldc=N + col0 + ldc_extra, col0=col0)
+    assert ok, "wrote outside the M x N view"
+    check_exact(C, ref, f"two launches ldc+{ldc_extra} col0={col0}")
+
+
 def test_repeatable():
     M, N, K = 597, 11008, 512
     A, B = datagen.make_bf16_pair(M, N, K, "normal", "normal", config=77)
