@@ -116,3 +116,23 @@ def test_selected_with_workspace_sampled(dt, M, N, K, cfg):
     ms, ns, vals, absv = oracle_lines(dt, A, B, rows, cols, sa * sb)
     check_close(dt, C[ms, ns][None, :], vals[None, :], absv[None, :], K, scale=sa * sb,
                 what=f"{dt} {M}x{N}x{K} {t.name}")
+
+
+def test_two_launches_with_split_remainder():
+    """4096 x 12480 x 2048 with the bench's 64 MiB workspace: the chosen
+    256 x 256 tile would run 3 full rounds and 32 tiles more, so the first
+    12288 columns run with it and the other 192 as a split-K GEMM that uses
+    the workspace (gemm_plan).  Whole rows and whole columns on both sides of
+    the launch boundary and of tile boundaries, bit-exact on small integers."""
+    M, N, K = 4096, 12480, 2048
+    ws = nan_workspace(64 << 20)
+    first, second, n1 = dg.plan(M, N, K, "bf16", 256, ws.numel())
+    print(f"[two launches {M}x{N}x{K}: {first.name} x {n1} + {second and second.name}]", flush=True)
+    assert second is not None and second.k_split > 1 and n1 == 12288, "shape no longer splits"
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=213)
+    C, ok = run("bf16", A, B, workspace=ws)
+    assert ok
+    rows = sample_lines(M)
+    cols = np.unique(np.concatenate([sample_lines(N), np.arange(n1 - 3, n1 + 3), np.arange(N - 3, N)]))
+    ms, ns, vals, _ = oracle_lines("bf16", A, B, rows, cols)
+    check_exact(C[ms, ns][None, :], vals[None, :], "two launches, split-K remainder")
