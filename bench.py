@@ -642,6 +642,12 @@ def main(argv=None):
         peak, unit_r = PEAK_HBM_GBPS, "GB/s"
     value = flops(M, N, K) * args.steps / (r["total_ms"] * 1e-3) / 1e12
     tile = r["tile"]
+    second = None
+    if args.tile is None:      # the library's own plan: one launch, or two over column ranges
+        import dense_gemm_linear_amd as dg
+        _, t2, n1 = dg.plan(M, N, K, dt, CUS, workspace.numel() if workspace is not None else 0)
+        if t2 is not None:
+            second = {"tile": t2.name, "first_columns": n1, "second_columns": N - n1}
     out = {
         "metric": "GEMM TFLOP/s (2MNK/t) + % MFMA peak; HBM GB/s for M<=8 decode",
         "value": round(value, 2),
@@ -658,7 +664,8 @@ def main(argv=None):
         "config": {"workload": name, "M": M, "N": N, "K": K, "tile": tile.name,
                    "tile_eff": round(tile.tile_eff, 4), "wq_eff": round(tile.wq_eff, 4),
                    "operand_copies_rotated": r["copies"], "pct_of_mfma_peak": None,
-                   "workspace_mib": args.workspace_mib},
+                   "workspace_mib": args.workspace_mib,
+                   **({"second_launch": second} if second else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_r,
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "algorithmic_bytes": alg_bytes(M, N, K, dt),
