@@ -129,10 +129,6 @@ __device__ __forceinline__ float apply_epilogue(const Epilogue& ep, float v, int
 #ifndef DG_GROUP_M
 #define DG_GROUP_M 4
 #endif
-// A fragments read from LDS ahead of the MFMAs that consume them.
-#ifndef DG_LDS_AHEAD
-#define DG_LDS_AHEAD 2
-#endif
 #ifndef DG_XCD_REMAP
 #define DG_XCD_REMAP 1
 #endif
