@@ -1,4 +1,4 @@
-"""The C ABI from plain C: tests/c_client.c, compiled with gcc against
+"""The C ABI from plain C: tests/clients/c_client.c, compiled with gcc against
 include/densegemm.h alone and linked to libdensegemm.so, makes host-side
 queries (tile selection, the launch plan, sizes, argument errors); its
 answers must equal the Python binding's.  No device is needed."""
@@ -23,7 +23,7 @@ def fields(t):
 def test_c_client_matches_binding(tmp_path):
     exe = tmp_path / "c_client"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
-                    os.path.join(ROOT, "tests", "c_client.c"), "-L", LIBDIR, "-ldensegemm",
+                    os.path.join(ROOT, "tests", "clients", "c_client.c"), "-L", LIBDIR, "-ldensegemm",
                     f"-Wl,-rpath,{LIBDIR}", "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines()
     assert out[-1] == "ok"
