@@ -142,6 +142,8 @@ WORKLOADS = {
     "bf16_1x28672x8192": (1, 28672, 8192, "bf16", "normal", 1.0, "normal", 0.02, 76),
     "bf16_12x2048x8192": (12, 2048, 8192, "bf16", "normal", 1.0, "normal", 0.02, 77),
     "fp8_8x11008x4096": (8, 11008, 4096, "fp8", "normal", 1.0, "normal", 1.0, 78),
+    "bf16_16x11008x4096": (16, 11008, 4096, "bf16", "normal", 1.0, "normal", 0.02, 86),
+    "bf16_16x8192x8192": (16, 8192, 8192, "bf16", "normal", 1.0, "normal", 0.02, 87),
     "fp8_597x11008x4096": (597, 11008, 4096, "fp8", "normal", 1.0, "normal", 1.0, 79),
     "fp8_2048x8192x2048": (2048, 8192, 2048, "fp8", "normal", 1.0, "normal", 1.0, 80),
     "fp8_8192x4096x4096": (8192, 4096, 4096, "fp8", "normal", 1.0, "normal", 1.0, 85),
