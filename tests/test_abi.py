@@ -361,3 +361,35 @@ def test_gemm_plan_splits_a_stray_last_round():
         assert P(M, N, K, dt, cus, 0, ctypes.byref(t1), ctypes.byref(t2), ctypes.byref(n)) == \
             dg.GEMM_ERR_INVALID_VALUE
     assert P(16, 16, 16, 0, 256, 0, None, ctypes.byref(t2), ctypes.byref(n)) == dg.GEMM_ERR_INVALID_VALUE
+
+
+def test_select_tile_concurrent_callers_agree():
+    """Eight threads query the selector at once (ctypes drops the GIL during
+    the call), over more distinct shapes than its table keeps, so lookups,
+    inserts and clears interleave; every answer equals the single-threaded one."""
+    import threading
+    rng = np.random.default_rng(5)
+    shapes = [(int(m), int(n), int(k) * 16) for m, n, k in
+              zip(rng.integers(1, 5000, 600), rng.integers(16, 60000, 600), rng.integers(1, 512, 600))]
+    want = {s: dg.select_tile(*s, "bf16", 256).name for s in shapes}
+    errors = []
+
+    def worker(seed):
+        r = np.random.default_rng(seed)
+        try:
+            for j, i in enumerate(r.permutation(len(shapes)).tolist() * 2):
+                s = shapes[i]
+                got = dg.select_tile(*s, "bf16", 256).name
+                if got != want[s]:
+                    errors.append((s, got, want[s]))
+                # a shape of this thread's own each time: 9600 in all, past the table's 4096
+                dg.select_tile(1 + j, 100000 + seed, 64, "bf16", 256)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
