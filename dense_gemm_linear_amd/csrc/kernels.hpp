@@ -422,8 +422,9 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
     // chunks expanded at compile time: with a large epilogue the unroller
     // may keep this loop (it holds a barrier), and a run-time chunk index
     // would put the accumulators in scratch memory
-    auto chunks = [&](auto cls_c) __attribute__((always_inline)) {
+    auto chunks = [&](auto cls_c, auto scl_c) __attribute__((always_inline)) {
         constexpr int CLS = decltype(cls_c)::value;
+        constexpr bool SCL = decltype(scl_c)::value;   // row or column scales given
         static_for<MR / CH>([&](auto cc_c) __attribute__((always_inline)) {
             constexpr int cc = decltype(cc_c)::value;
             if constexpr (EPI) {
@@ -475,7 +476,7 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
 #pragma unroll
             for (int ml = 0; ml < CH; ++ml) {
                 float row_scale[AT::NACC];
-                if constexpr (EPI) {
+                if constexpr (EPI && SCL) {
 #pragma unroll
                     for (int e = 0; e < AT::NACC; ++e) {
                         const int grow =
@@ -495,8 +496,10 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
                         const int col = j * R + lc + ph;
                         uint16_t* sp = reinterpret_cast<uint16_t*>(stage + row * SROW + col * 2);
                         if constexpr (EPI) {
-                            v = v * row_scale[e];
-                            v = v * col_scale[j];
+                            if constexpr (SCL) {
+                                v = v * row_scale[e];
+                                v = v * col_scale[j];
+                            }
                             v = v + col_bias[j];
                             v = activate_c<CLS>(p.ep.act, v);
                             if (p.ep.mul)
@@ -553,16 +556,23 @@ __device__ __forceinline__ void store_c_tile(const GemmArgs& p,
             __syncthreads();
         });
     };
+    // The activation class is chosen once per launch; for the cheapest class
+    // (none or ReLU: a bias alone, say) also whether any scale is given, since
+    // there the two multiplies by 1 per element are most of the VALU work after
+    // the K loop (exact to drop).  The other classes keep one variant each:
+    // more copies of the staging loop raised register spills.
     if constexpr (EPI) {
         const int cls = act_class(p.ep.act);
         if (cls == 1)
-            chunks(std::integral_constant<int, 1>{});
+            chunks(std::integral_constant<int, 1>{}, std::true_type{});
         else if (cls == 2)
-            chunks(std::integral_constant<int, 2>{});
+            chunks(std::integral_constant<int, 2>{}, std::true_type{});
+        else if (p.ep.scale_m || p.ep.scale_n)
+            chunks(std::integral_constant<int, 0>{}, std::true_type{});
         else
-            chunks(std::integral_constant<int, 0>{});
+            chunks(std::integral_constant<int, 0>{}, std::false_type{});
     } else {
-        chunks(std::integral_constant<int, 0>{});
+        chunks(std::integral_constant<int, 0>{}, std::false_type{});
     }
 }
 
