@@ -479,20 +479,24 @@ def backward_prep(reps: int) -> int:
     import dense_gemm_linear_amd as dg
     T, D, F = 10240, 2048, 8192
     g = torch.Generator(device="cuda").manual_seed(3)
-    dY = torch.randn(T, F, device="cuda", generator=g).bfloat16()
-    W = torch.randn(F, D, device="cuda", generator=g).bfloat16()
-    X = torch.randn(T, D, device="cuda", generator=g).bfloat16()
-    dYt = torch.empty(F, T, dtype=torch.bfloat16, device="cuda")
-    Ws = torch.empty(dg.shuffle_b_bytes(D, F), dtype=torch.uint8, device="cuda")
-    Xs = torch.empty(dg.shuffle_b_bytes(D, T), dtype=torch.uint8, device="cuda")
+    # (source, destination) pairs rotated cold, as for the GEMM workloads
+    def pairs(shape, dst_of):
+        n = cold_copies(2 * shape[0] * shape[1] * 2)
+        src = torch.randn(*shape, device="cuda", generator=g).bfloat16()
+        return [(src if i == 0 else src.clone(), dst_of()) for i in range(n)]
+    dYs = pairs((T, F), lambda: torch.empty(F, T, dtype=torch.bfloat16, device="cuda"))
+    Wss = pairs((F, D), lambda: torch.empty(dg.shuffle_b_bytes(D, F), dtype=torch.uint8, device="cuda"))
+    Xss = pairs((T, D), lambda: torch.empty(dg.shuffle_b_bytes(D, T), dtype=torch.uint8, device="cuda"))
     out = {}
-    for label, call, nbytes in (
-            ("transpose_dY_10240x8192", lambda i: dg.transpose(dY, out=dYt), 2 * dY.numel() * 2),
-            ("shuffle_b_t_W_8192x2048", lambda i: dg.shuffle_b_t(W, out=Ws), W.numel() * 2 + Ws.numel()),
-            ("shuffle_b_t_X_10240x2048", lambda i: dg.shuffle_b_t(X, out=Xs), X.numel() * 2 + Xs.numel())):
-        us = time_graph(call, reps, trials=3)
+    for label, ps, fn in (
+            ("transpose_dY_10240x8192", dYs, lambda s, d: dg.transpose(s, out=d)),
+            ("shuffle_b_t_W_8192x2048", Wss, lambda s, d: dg.shuffle_b_t(s, out=d)),
+            ("shuffle_b_t_X_10240x2048", Xss, lambda s, d: dg.shuffle_b_t(s, out=d))):
+        nbytes = ps[0][0].numel() * 2 + ps[0][1].numel() * ps[0][1].element_size()
+        us = time_graph(lambda i, ps=ps, fn=fn: fn(*ps[i % len(ps)]), reps, trials=3)
         out[label] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
-    print(json.dumps({"backward_prep": out, "timing": f"hipGraph of {reps} calls, median of 3"}),
+    print(json.dumps({"backward_prep": out, "timing": f"hipGraph of {reps} calls, median of 3, "
+                                                   f"operands rotated cold"}),
           flush=True)
     return 0
 
