@@ -4,7 +4,8 @@
   bias, activation, multiplier on a 2 x 2 product.
 - Textbook activation values (logistic(1), the normal CDF at 1 and 2).
 - Library routines: SiLU = x * scipy.special.expit(x); the erf GELU = x *
-  scipy.stats.norm.cdf(x).
+  scipy.stats.norm.cdf(x); the tanh GELU = torch's float64
+  gelu(approximate="tanh"), with a planted coefficient slip shown to fail.
 - Identities: f(x) - f(-x) = x for SiLU and both GELU forms (logistic(x) +
   logistic(-x) = 1, Phi(x) + Phi(-x) = 1, tanh odd), which catches a sign or
   argument slip; the tanh form stays within 1e-3 of the erf form but is not
@@ -96,3 +97,29 @@ def test_parts_compose_and_identity():
     np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
     ones = bf16(np.ones((7, 9)))
     assert np.array_equal(oracle.epilogue(C, mul=ones), C)
+
+
+def test_gelu_tanh_against_torch():
+    """The tanh form against torch's own float64 gelu(approximate="tanh"), an
+    implementation written apart from this oracle: a slip in the cubic
+    coefficient (0.0447 for 0.044715 moves the output by up to 4.7e-4) or in
+    sqrt(2/pi) fails by orders of magnitude.  For large negative x both sides
+    compute 1 + tanh(.) by cancellation, so the absolute slack there is one
+    rounding of |x|."""
+    import torch
+    x = np.linspace(-12, 12, 48001)
+    got = oracle.activation(oracle.ACT_GELU_TANH, x)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.all(np.abs(got - ref) <= 1e-14 * np.abs(ref) + np.abs(x) * 2.0 ** -52)
+    pos = x > 0.5
+    np.testing.assert_allclose(got[pos], ref[pos], rtol=1e-14, atol=0)
+
+
+def test_gelu_tanh_planted_coefficient_slip_is_caught():
+    """The check above rejects the plausible slip: the same formula with the
+    cubic coefficient rounded to 0.0447 (computed here, not in the oracle)."""
+    import torch
+    x = np.linspace(-12, 12, 48001)
+    slipped = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.0447 * x ** 3)))
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert not np.all(np.abs(slipped - ref) <= 1e-14 * np.abs(ref) + np.abs(x) * 2.0 ** -52)

@@ -117,6 +117,28 @@ def test_points_match_full_product():
     np.testing.assert_array_equal(oracle.gemm_points(oracle.ORC_BF16, A, B, ms, ns), C[ms, ns])
 
 
+def test_points_e4m3_scaled_match_full_product():
+    """The per-point path on e4m3 codes with the product of the two dequant
+    scales, as the full-size parity checks call it, against the full product
+    (which applies the scales one after the other): equal to within one
+    rounding of the scale product; exactly equal with power-of-two scales."""
+    M, N, K = 23, 17, 192
+    A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=91)
+    C = oracle.gemm_e4m3(A, B, sa, sb)
+    ms = np.array([0, 22, 5, 11, 22, 0])
+    ns = np.array([0, 16, 3, 16, 0, 9])
+    pts = oracle.gemm_points(oracle.ORC_E4M3, A, B, ms, ns,
+                             float(np.float32(sa)) * float(np.float32(sb)))
+    np.testing.assert_allclose(pts, C[ms, ns], rtol=4 * 2.0 ** -53, atol=0)
+    C2 = oracle.gemm_e4m3(A, B, 2.0 ** -3, 2.0 ** 2)
+    pts2 = oracle.gemm_points(oracle.ORC_E4M3, A, B, ms, ns, 2.0 ** -3 * 2.0 ** 2)
+    np.testing.assert_array_equal(pts2, C2[ms, ns])
+    # and the scale really is applied: unscaled points differ by sa * sb
+    raw = oracle.gemm_points(oracle.ORC_E4M3, A, B, ms, ns, 1.0)
+    np.testing.assert_allclose(raw * float(np.float32(sa)) * float(np.float32(sb)), C[ms, ns],
+                               rtol=4 * 2.0 ** -53, atol=0)
+
+
 def test_threads_do_not_change_result():
     M, N, K = 37, 29, 96
     A = datagen.to_bf16_bits(datagen.normal(51, (M, K)))
