@@ -404,6 +404,41 @@ def _out(A, N, out):
     return out
 
 
+def _check_operands(code: int, A, Bs, N: int, scales=()):
+    """Everything the C ABI cannot see behind its plain pointers, checked
+    before any launch: A's element type matches the entry point (an e4m3 A
+    handed to the bf16 GEMM would have its byte pitch read as a bf16 pitch),
+    Bs is a device buffer at least shuffle_b_bytes(N, K) long (the kernels
+    size their B bounds from N and K, not from the buffer), and each scale is
+    a float32 device tensor with at least one element (a host tensor would
+    hand the kernel a host pointer).  Element types are checked first, so
+    the checks also run on a machine without a GPU."""
+    torch = _torch()
+    want = (torch.bfloat16, torch.int16, torch.uint16) if code == GEMM_BF16 else \
+        (torch.uint8, torch.int8, torch.float8_e4m3fn)
+    fn = "gemm_bf16" if code == GEMM_BF16 else "gemm_fp8_scaled"
+    if A.dtype not in want:
+        raise ValueError(f"{fn}: A has element type {A.dtype}, expected one of "
+                         f"{', '.join(str(d) for d in want)}")
+    for name, t in scales:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() < 1:
+            raise ValueError(f"{fn}: {name} must be a float32 device tensor with one element")
+    if not isinstance(Bs, torch.Tensor):
+        raise ValueError(f"{fn}: Bs must be the device tensor shuffle_b returned")
+    _check_rows("A", A)
+    if not Bs.is_cuda or Bs.device != A.device:
+        raise ValueError(f"{fn}: Bs must be a device tensor on A's device")
+    if not Bs.is_contiguous():
+        raise ValueError(f"{fn}: Bs must be contiguous (the preshuffled layout is dense)")
+    need = shuffle_b_bytes(N, A.shape[1], code)
+    if Bs.numel() * Bs.element_size() < need:
+        raise ValueError(f"{fn}: Bs holds {Bs.numel() * Bs.element_size()} bytes, the "
+                         f"preshuffled B of N={N}, K={A.shape[1]} needs {need}")
+    for name, t in scales:
+        if not t.is_cuda or t.device != A.device:
+            raise ValueError(f"{fn}: {name} must be on A's device, not {t.device}")
+
+
 def _tile_ptr(tile):
     if tile is None:
         return None
@@ -466,7 +501,7 @@ def gemm_bf16(A, Bs, N: int, out=None, tile: Tile | None = None, workspace=None,
     library weigh split-K tiles that fit in it).  Fused epilogue (all
     optional): C = act(acc * scale_m[m] * scale_n[n] + bias[n]) * mul[m, n],
     activation one of ACTIVATIONS; mul may be `out` itself."""
-    _check_rows("A", A)
+    _check_operands(GEMM_BF16, A, Bs, N)
     C = _out(A, N, out)
     M, K = A.shape
     ws, nbytes = _workspace(A, N, K, GEMM_BF16, tile, workspace)
@@ -493,7 +528,7 @@ def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None
     scale_a / scale_b are one-element float32 device tensors.  The fused
     epilogue parts are those of gemm_bf16 (scale_m / scale_n: per-token and
     per-channel fp32 multipliers)."""
-    _check_rows("A", A)
+    _check_operands(GEMM_FP8_E4M3, A, Bs, N, (("scale_a", scale_a), ("scale_b", scale_b)))
     C = _out(A, N, out)
     M, K = A.shape
     ws, nbytes = _workspace(A, N, K, GEMM_FP8_E4M3, tile, workspace)

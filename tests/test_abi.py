@@ -393,3 +393,28 @@ def test_select_tile_concurrent_callers_agree():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_binding_rejects_wrong_operand_types_before_any_launch():
+    """The binding checks what the C ABI cannot see behind its pointers:
+    element types first, so these run without a GPU.  Each mistake raises
+    ValueError before anything reaches the library."""
+    import torch
+    a_bf = torch.zeros((4, 64), dtype=torch.bfloat16)
+    a_f8 = torch.zeros((4, 64), dtype=torch.uint8)
+    bs = torch.zeros(dg.shuffle_b_bytes(16, 64), dtype=torch.uint8)
+    one = torch.ones(1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="element type"):
+        dg.gemm_bf16(a_f8, bs, 16)                      # e4m3 A to the bf16 GEMM
+    with pytest.raises(ValueError, match="element type"):
+        dg.gemm_bf16(a_bf.float(), bs, 16)              # fp32 A
+    with pytest.raises(ValueError, match="element type"):
+        dg.gemm_fp8_scaled(a_bf, bs, 16, one, one)      # bf16 A to the e4m3 GEMM
+    with pytest.raises(ValueError, match="scale_a"):
+        dg.gemm_fp8_scaled(a_f8, bs, 16, one.double(), one)
+    with pytest.raises(ValueError, match="scale_b"):
+        dg.gemm_fp8_scaled(a_f8, bs, 16, one, torch.ones(0, dtype=torch.float32))
+    with pytest.raises(ValueError, match="scale_a"):
+        dg.gemm_fp8_scaled(a_f8, bs, 16, 1.0, one)      # a number, not a tensor
+    with pytest.raises(ValueError, match="device"):
+        dg.gemm_bf16(a_bf, bs, 16)                      # host A
