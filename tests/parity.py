@@ -6,6 +6,9 @@ Comparison rules (fixed here, used by every GPU test):
     so every fp32 accumulation order gives it exactly and the bf16 output has
     one correct value: bits must equal the oracle's round-to-nearest-even of
     the fp64 sum (-0 and +0 identified);
+  * full-size workloads are compared on every element too (the oracle's
+    whole product on the host's threads), with the accumulation term of the
+    element bound taken from row norms (check_close_full);
   * general inputs: relative Frobenius error over the real M x N region
     against the unrounded fp64 oracle, at most 2e-3 (bf16) or 3e-2 (e4m3,
     after scales); and element by element
@@ -116,6 +119,24 @@ def check_close(dt: str, Cbits: np.ndarray, Cref: np.ndarray, absref: np.ndarray
     viol = np.argwhere(np.abs(err) > bound)
     assert viol.size == 0, f"{what}: {len(viol)} elements out of bound, first {viol[:5].tolist()}"
     return fro
+
+
+def row_norms(dt: str, X: np.ndarray) -> np.ndarray:
+    """Euclidean norm of every row of a bf16-bit or e4m3-code array."""
+    v = oracle.bf16_to_f64(X) if dt == "bf16" else oracle.e4m3_to_f64(X)
+    return np.sqrt(np.einsum("ij,ij->i", v, v))
+
+
+def check_close_full(dt: str, Cbits: np.ndarray, Cref: np.ndarray, A, B, K: int,
+                     scale: float = 1.0, what: str = ""):
+    """check_close over every element of a full-size product, with
+    sum_k |a_k b_k| replaced by its Cauchy-Schwarz bound |a_m| |b_n| (row
+    norms): an upper bound of the element bound that needs no second
+    full product of absolute values.  For the workloads' random inputs it is
+    about 1.6 times the exact sum, and the accumulation term stays far below
+    any indexing mistake (which is off by a fraction of the whole sum)."""
+    absref = np.multiply.outer(row_norms(dt, A), row_norms(dt, B))
+    return check_close(dt, Cbits, Cref, absref, K, scale, what)
 
 
 def sample_lines(extent: int, tiles=(256, 128, 64, 32, 16), n_random: int = 6, seed: int = 0):

@@ -12,8 +12,7 @@ import torch
 
 import datagen
 import dense_gemm_linear_amd as dg
-from parity import (abs_bits, check_close, check_exact, oracle_full, oracle_lines, run,
-                    sample_lines)
+from parity import abs_bits, check_close, check_close_full, check_exact, oracle_full, run
 
 pytestmark = pytest.mark.gpu
 
@@ -42,27 +41,29 @@ BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selecto
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("smallint", [False, True], ids=["general", "smallint"])
-@pytest.mark.parametrize("ws", [0, BENCH_WORKSPACE], ids=["no_ws", "bench_ws"])
-def test_workload_shapes_sampled(name, smallint, ws):
-    """ws as in the bf16 test: the bench's tile is run where it differs."""
+def test_workload_shapes_every_element(name, smallint):
+    """Every output element against the oracle's whole product, on the
+    library's plan without a workspace and, where it differs, on the tile
+    bench.py times with its 64 MiB workspace."""
     M, N, K, cfg = WORKLOADS[name]
-    tile = dg.select_tile(M, N, K, "fp8", workspace_bytes=ws)
-    if ws and tile.name == dg.select_tile(M, N, K, "fp8").name:
-        pytest.skip("the workspace does not change the tile: covered by no_ws")
     A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=cfg, smallint=smallint)
     if smallint:
         sa, sb = 2.0 ** -3, 2.0 ** 2
-    print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint} tile={tile.name}]", flush=True)
-    workspace = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda") if ws else None
-    C, ok = run("fp8", A, B, sa=sa, sb=sb, workspace=workspace)
-    assert ok
-    rows, cols = sample_lines(M), sample_lines(N)
-    ms, ns, vals, absv = oracle_lines("fp8", A, B, rows, cols, scale=sa * sb)
-    got = C[ms, ns]
-    if smallint:
-        check_exact(got[None, :], vals[None, :], name)
-    else:
-        check_close("fp8", got[None, :], vals[None, :], absv[None, :], K, scale=sa * sb, what=name)
+    print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint}: oracle product]", flush=True)
+    ref = oracle_full("fp8", A, B, sa, sb)
+    runs = [(0, dg.select_tile(M, N, K, "fp8"))]
+    t_ws = dg.select_tile(M, N, K, "fp8", workspace_bytes=BENCH_WORKSPACE)
+    if t_ws.name != runs[0][1].name:
+        runs.append((BENCH_WORKSPACE, t_ws))
+    for ws, tile in runs:
+        print(f"[gemm_fp8 {name} ws={ws >> 20} MiB tile={tile.name}]", flush=True)
+        workspace = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda") if ws else None
+        C, ok = run("fp8", A, B, sa=sa, sb=sb, workspace=workspace)
+        assert ok, "guard band written"
+        if smallint:
+            check_exact(C, ref, f"{name} {tile.name}")
+        else:
+            check_close_full("fp8", C, ref, A, B, K, scale=sa * sb, what=f"{name} {tile.name}")
 
 
 @pytest.mark.parametrize("tile", dg.ladder_tiles("fp8"), ids=lambda t: t.name)
