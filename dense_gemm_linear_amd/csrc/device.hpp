@@ -35,6 +35,21 @@ __device__ __forceinline__ i32x4 load16(rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+// The same with a scalar (wave-uniform) byte offset added to the per-lane
+// one, for loads whose k-tile offset is the same in every lane.
+__device__ __forceinline__ i32x4 load16_s(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+// A 16-byte LDS DMA (global -> LDS, no register round trip): lane l's 16
+// bytes land at lds_base + 16 l; m0 holds the wave-uniform lds_base.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+
 // The same with the non-temporal cache hint (bit 1 of the cache-policy
 // operand, `nt` on gfx950), for data read exactly once: a decode weight
 // streamed from HBM.  Measured on MI355X with cold operands, the skinny

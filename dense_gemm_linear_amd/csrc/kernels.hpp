@@ -646,30 +646,6 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x
         __builtin_amdgcn_sched_barrier(0);                       \
     } while (0)
 
-// Issue order inside one K step: its MFMAs with the LDS reads of the next
-// step (or of the next k-tile's first step) and this step's share of the
-// global loads spread between them, so that neither the LDS pipe nor the
-// texture-address FIFO sees all of a k-tile's requests in one burst ("GEMM
-// Optimization Guide" page, section 5: one VMEM per scheduler iteration, LDS
-// reads between MFMA groups).
-template <int MF, int RD, int VM>
-__device__ __forceinline__ void schedule_step()
-{
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < RD)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i < VM)
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    if (RD > MF)
-        __builtin_amdgcn_sched_group_barrier(0x100, RD > MF ? RD - MF : 1, 0);
-    if (VM > MF)
-        __builtin_amdgcn_sched_group_barrier(0x020, VM > MF ? VM - MF : 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // Fragment register sets: consecutive K steps alternate between sets, and a
 // trip of ST phases of STEPS steps must return to set 0, so the count
 // divides ST * STEPS: 2 when that is even, else its smallest odd divisor.
@@ -684,89 +660,125 @@ constexpr int frag_sets(int st, int steps)
     return n;
 }
 
-// Runs f(kt + i, integral_constant<i>, tail) for i in I...: one trip of the
-// steady-state loop (ST phases with compile-time stage indices), and the
-// tail variant only while kt + i < nkt.
-template <class F, int... I>
+// Groups a K step is cut into: two MFMAs per group where the step has enough
+// of them, at most eight groups.
+constexpr int step_groups(int mfmas)
+{
+    return mfmas >= 16 ? 8 : (mfmas >= 2 ? mfmas / 2 : 1);
+}
+
+// Runs f(kt + i, integral_constant<i>, tail, nomask) for i in I...: one trip
+// of the steady-state loop (ST phases with compile-time stage indices), and
+// the tail variant only while kt + i < nkt.  nomask: every load of the trip
+// lies inside K, so the loads need no K-tail masking.
+template <bool NOMASK, class F, int... I>
 __device__ __forceinline__ void run_phases(F& f, int kt, std::integer_sequence<int, I...>)
 {
-    (f(kt + I, std::integral_constant<int, I>{}, std::false_type{}), ...);
+    (f(kt + I, std::integral_constant<int, I>{}, std::false_type{},
+       std::integral_constant<bool, NOMASK>{}),
+     ...);
 }
 template <class F, int... I>
 __device__ __forceinline__ void run_tail(F& f, int kt, int nkt, std::integer_sequence<int, I...>)
 {
-    ((kt + I < nkt ? f(kt + I, std::integral_constant<int, I>{}, std::true_type{}) : void()), ...);
+    ((kt + I < nkt ? f(kt + I, std::integral_constant<int, I>{}, std::true_type{}, std::false_type{})
+                   : void()),
+     ...);
 }
 
 // The K loop shared by both tiled kernels.  Phase t multiplies k-tile t out
 // of stage t % ST while k-tile t + ST - 1 streams into the stage that phase
-// t - 1 finished with; its loads are issued in STEPS parts, one at the start
-// of each K step.  The workgroup barrier of phase t sits before the
+// t - 1 finished with.  The workgroup barrier of phase t sits before the
 // MFMAs of its last K step: after it, the first fragments of k-tile t + 1 are
-// read from LDS while those MFMAs run, so no LDS latency is exposed at the
-// k-tile boundary.  Fragment registers alternate between two sets along the
-// global sequence of K steps, NS = frag_sets(ST, STEPS) of them.
+// read from LDS while those MFMAs run.  Fragment registers alternate between
+// NS = frag_sets(ST, STEPS) sets along the global sequence of K steps.
+//
+// Issue order.  Every K step is cut into G groups, each a slice of the
+// step's MFMAs, of the LDS reads of the next fragments and of the k-tile's
+// loads, and the groups are fenced with sched_barrier(0), so that the
+// compiler keeps this order: one wave per SIMD (the 4-wave 256 x 256 tile)
+// has no second wave to hide a burst of loads or reads behind, and when the
+// scheduler was only asked to interleave (sched_group_barrier) it put all of
+// a k-tile's LDS DMA loads in one run.  Measured on MI355X (bf16 4096^3, K
+// loop cycles per k-tile): 1433 -> 1159 for the 4-wave 256 x 256 tile.
+//   - With two or more K steps per k-tile the loads go out during the steps
+//     before the last, so that none is issued between the last MFMAs before
+//     the barrier and the barrier (with one wave per SIMD the MFMA pipe ran
+//     dry there).
+//   - With one K step and three or more stages they go out after the barrier,
+//     into the stage one further from those being read; with one K step and
+//     two stages, before the barrier, which then waits for them.
 //
 // The last nkt % ST phases (the tail) would only load k-tiles past K: they
 // issue no loads and wait for every load in flight.  (Their register loads
 // would be dead code the compiler removes, and the steady-state wait counts
 // assume every phase issues exactly LOADS loads: with loads removed, a count
-// of in-flight loads no longer proves the next k-tile has landed.)
-//   load(kt, stage, part)      issue part `part` (of STEPS) of the loads of
-//                              k-tile kt (zeros past K)
-//   read(stage, step, set)     LDS -> fragment registers
-//   mma(stage, step, set)      the MFMAs of one K step
-template <int ST, int STEPS, int LOADS, int MF, int RD, class Load, class Read, class Mma>
-__device__ __forceinline__ void k_loop(int nkt, Load& load, Read& read, Mma& mma)
+// of in-flight loads no longer proves the next k-tile has landed.)  Trips
+// whose loads all lie before nomask_end (k-tiles of the whole K range) run
+// with loads that need no masking, which take their k-tile offset from a
+// scalar register.
+//   load(kt, stage, part, nparts, nomask)  issue the loads n of k-tile kt with
+//                                          n % nparts == part (zeros past K)
+//   read(stage, step, set, g, G)           LDS -> fragment registers, group g
+//   mma(stage, step, set, g, G)            the MFMAs of group g of one K step
+template <int ST, int STEPS, int LOADS, int G, class Load, class Read, class Mma>
+__device__ __forceinline__ void k_loop(int nkt, int nomask_end, Load& load, Read& read, Mma& mma)
 {
     constexpr int NS = frag_sets(ST, STEPS);
+    constexpr bool AFTER = STEPS == 1 && ST >= 3;   // one step: loads after the barrier
+    constexpr int NP = STEPS > 1 ? STEPS - 1 : 1;    // steps that issue loads
+    constexpr int LPARTS = NP * G;                   // load parts per k-tile
+    constexpr int VM = AFTER ? (ST - 3) * LOADS : (ST - 2) * LOADS;
     static_assert(ST >= 2 && (ST - 2) * LOADS <= 63, "pipeline depth vs vmcnt");
-    // Spreading the loads over the K steps keeps the texture-address FIFO from
-    // filling in a burst (measured: +10% on the register-B kernel); with a
-    // 2-stage ring the next k-tile's loads are needed one phase later, so
-    // they all go out at the start of the phase instead.
-    constexpr bool SPREAD = ST >= 3;
-    constexpr int VM = SPREAD ? (LOADS + STEPS - 1) / STEPS : 0;   // loads per K step
 #pragma unroll
     for (int t = 0; t < ST - 1; ++t)
-#pragma unroll
-        for (int part = 0; part < STEPS; ++part)
-            load(t, t, part);
+        load(t, t, 0, 1, std::false_type{});
     DG_STAGE_BARRIER((ST - 2) * LOADS);
-    read(0, 0, 0);
-    auto phase = [&](int t, auto sc, auto tail) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        read(0, 0, 0, g, G);
+    auto phase = [&](int t, auto sc, auto tail, auto nomask) __attribute__((always_inline)) {
         constexpr int si = decltype(sc)::value;
         constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const int cur = (si * STEPS + st) % NS;
             const int nxt = (si * STEPS + st + 1) % NS;
-            if constexpr (!TAIL) {
-                if (SPREAD) {
-                    load(t + ST - 1, (si + ST - 1) % ST, st);
-                } else if (st == 0) {
+            const bool last = st + 1 == STEPS;
+            if (last) {
+                if constexpr (!TAIL && STEPS == 1 && !AFTER) {
+                    // one step and two stages: the loads go out before the
+                    // barrier, which waits for them (VM = 0)
 #pragma unroll
-                    for (int part = 0; part < STEPS; ++part)
-                        load(t + ST - 1, (si + ST - 1) % ST, part);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int g = 0; g < G; ++g)
+                        load(t + ST - 1, (si + ST - 1) % ST, g, G, nomask);
                 }
-            }
-            if (st + 1 < STEPS) {
-                read(si, st + 1, nxt);
-            } else {
                 if constexpr (TAIL)
                     DG_STAGE_BARRIER(0);
                 else
-                    DG_STAGE_BARRIER((ST - 2) * LOADS);
-                read((si + 1) % ST, 0, nxt);
+                    DG_STAGE_BARRIER(VM);
             }
-            mma(si, st, cur);
-            schedule_step<MF, RD, VM>();
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (!last)
+                    read(si, st + 1, nxt, g, G);
+                else
+                    read((si + 1) % ST, 0, nxt, g, G);
+                mma(si, st, cur, g, G);
+                if constexpr (!TAIL) {
+                    if (!last || AFTER)
+                        load(t + ST - 1, (si + ST - 1) % ST, (AFTER ? 0 : st) * G + g, LPARTS,
+                             nomask);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
     int kt = 0;
+    for (; kt + ST <= nkt && kt + 2 * ST - 2 < nomask_end; kt += ST)
+        run_phases<true>(phase, kt, std::make_integer_sequence<int, ST>{});
     for (; kt + ST <= nkt; kt += ST)
-        run_phases(phase, kt, std::make_integer_sequence<int, ST>{});
+        run_phases<false>(phase, kt, std::make_integer_sequence<int, ST>{});
     run_tail(phase, kt, nkt, std::make_integer_sequence<int, ST - 1>{});
     // Loads past nkt (zeros) still target LDS: drain them everywhere before
     // the epilogue reuses it.
@@ -815,7 +827,8 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform: the LDS addresses of the DMA loads stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;     // wave row (M) and column (N)
     int wg, tm, tn;
     const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
@@ -857,19 +870,26 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     // A k-tile past the end of this workgroup's K range (past K, or past its
     // slice) loads through out-of-range offsets: zeros, and no memory
     // traffic.  Load op n (A DMAs first, then B fragments) belongs to part
-    // n % STEPS.
-    auto load = [&](int kt_local, int stage, int part) __attribute__((always_inline)) {
+    // n % nparts.  Without masking (every k-tile of the trip inside K) the
+    // k-tile's offset is a scalar operand of the load.
+    auto load = [&](int kt_local, int stage, int part, int nparts, auto nomask_c)
+                    __attribute__((always_inline)) {
+        constexpr bool NOMASK = decltype(nomask_c)::value;
         const int kt = kr.kt0 + kt_local;
         const bool mask = kt >= kr.last_full;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            if (i % STEPS != part)
+            if (i % nparts != part)
                 continue;
-            uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
-            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
-                off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void*)(lds + stage * A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+            uint8_t* dst = lds + stage * A_BUF + (wave + WAVES * i) * 1024;
+            if constexpr (NOMASK) {
+                dma16(ra, dst, ad[i].goff, (uint32_t)kt * KTB);
+            } else {
+                uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
+                if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
+                    off = kOOB;
+                dma16(ra, dst, off, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NR; ++j)
@@ -877,35 +897,44 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
             for (int s = 0; s < STEPS; ++s)
 #pragma unroll
                 for (int q = 0; q < P; ++q) {
-                    if ((A_DMA + (j * STEPS + s) * P + q) % STEPS != part)
+                    if ((A_DMA + (j * STEPS + s) * P + q) % nparts != part)
                         continue;
-                    const int kb = kt * KPK + AT::b_half(s, q);
-                    uint32_t off = b_lane + (uint32_t)(j * (R / 16) * p.KB + kb) * 1024u +
-                                   ((uint32_t)AT::b_group(s, lane, q) << 8);
-                    if (mask && kb >= kr.kb_end)
-                        off = kOOB;
-                    breg[stage][j][s][q] = load16(rb, off);
+                    const uint32_t voff = b_lane +
+                                          (uint32_t)(j * (R / 16) * p.KB + AT::b_half(s, q)) * 1024u +
+                                          ((uint32_t)AT::b_group(s, lane, q) << 8);
+                    if constexpr (NOMASK) {
+                        breg[stage][j][s][q] = load16_s(rb, voff, (uint32_t)kt * (KPK * 1024u));
+                    } else {
+                        const int kb = kt * KPK + AT::b_half(s, q);
+                        breg[stage][j][s][q] =
+                            load16(rb, mask && kb >= kr.kb_end ? kOOB : voff + (uint32_t)kt * (KPK * 1024u));
+                    }
                 }
     };
-    auto read = [&](int stage, int s, int set) __attribute__((always_inline)) {
+    // group g of a K step: A fragment reads and MFMAs (atom a = mi NR + j)
+    auto read = [&](int stage, int s, int set, int g, int G) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-            for (int q = 0; q < P; ++q) {
-                const uint32_t row = row0 + (uint32_t)(mi * R + lr);
-                const uint32_t off = (uint32_t)(stage * A_BUF) + row * KTB +
-                                     (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
-                af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
-            }
+        for (int f = 0; f < MR * P; ++f) {
+            if (f * G / (MR * P) != g)
+                continue;
+            const int mi = f / P, q = f % P;
+            const uint32_t row = row0 + (uint32_t)(mi * R + lr);
+            const uint32_t off = (uint32_t)(stage * A_BUF) + row * KTB +
+                                 (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+            af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
+        }
     };
-    auto mma = [&](int stage, int s, int set) __attribute__((always_inline)) {
+    auto mma = [&](int stage, int s, int set, int g, int G) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-            for (int j = 0; j < NR; ++j)
-                acc[mi][j] = AT::mma(af[set][mi], breg[stage][j][s], acc[mi][j]);
+        for (int a = 0; a < MR * NR; ++a) {
+            if (a * G / (MR * NR) != g)
+                continue;
+            const int mi = a / NR, j = a % NR;
+            acc[mi][j] = AT::mma(af[set][mi], breg[stage][j][s], acc[mi][j]);
+        }
     };
-    k_loop<ST, STEPS, S::LOADS, MR * NR, MR * P>(kr.n, load, read, mma);
+    k_loop<ST, STEPS, S::LOADS, step_groups(MR * NR)>(kr.n, min(kr.n, kr.last_full - kr.kt0), load,
+                                                      read, mma);
 
     if constexpr (MODE == MODE_SPLIT) {
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
@@ -973,7 +1002,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform: the LDS addresses of the DMA loads stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     int wg, tm, tn;
     const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
@@ -1018,61 +1048,79 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         for (int j = 0; j < NR; ++j)
             acc[mi][j] = zero_acc<AT>();
 
-    // Load op n (A DMAs first, then B DMAs) belongs to part n % STEPS.
-    auto load = [&](int kt_local, int stage, int part) __attribute__((always_inline)) {
+    // Load op n (A DMAs first, then B DMAs) belongs to part n % nparts.
+    // Without masking (every k-tile of the trip inside K) the k-tile's offset
+    // is a scalar operand of the load.
+    auto load = [&](int kt_local, int stage, int part, int nparts, auto nomask_c)
+                    __attribute__((always_inline)) {
+        constexpr bool NOMASK = decltype(nomask_c)::value;
         const int kt = kr.kt0 + kt_local;
         const bool mask = kt >= kr.last_full;
         uint8_t* base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            if (i % STEPS != part)
+            if (i % nparts != part)
                 continue;
-            uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
-            if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
-                off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void*)(base + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+            uint8_t* dst = base + (wave + WAVES * i) * 1024;
+            if constexpr (NOMASK) {
+                dma16(ra, dst, ad[i].goff, (uint32_t)kt * KTB);
+            } else {
+                uint32_t off = ad[i].goff + (uint32_t)kt * KTB;
+                if (mask && (int)((uint32_t)kt * KTB + ad[i].col) >= kr.ka_end)
+                    off = kOOB;
+                dma16(ra, dst, off, 0);
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) {
-            if ((A_DMA + i) % STEPS != part)
+            if ((A_DMA + i) % nparts != part)
                 continue;
-            uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
-            if (mask && kt * KPK + (int)b_half[i] >= kr.kb_end)
-                off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void*)(base + A_BUF + (wave + WAVES * i) * 1024), 16, off, 0, 0, 0);
+            uint8_t* dst = base + A_BUF + (wave + WAVES * i) * 1024;
+            if constexpr (NOMASK) {
+                dma16(rb, dst, b_goff[i], (uint32_t)kt * (KPK * 1024u));
+            } else {
+                uint32_t off = b_goff[i] + (uint32_t)kt * (KPK * 1024u);
+                if (mask && kt * KPK + (int)b_half[i] >= kr.kb_end)
+                    off = kOOB;
+                dma16(rb, dst, off, 0);
+            }
         }
     };
-    auto read = [&](int stage, int s, int set) __attribute__((always_inline)) {
+    // group g of a K step: fragment f (B fragments first, then A) and atom
+    // a = mi NR + j
+    auto read = [&](int stage, int s, int set, int g, int G) __attribute__((always_inline)) {
+        constexpr int NF = (MR + NR) * P;
 #pragma unroll
-        for (int j = 0; j < NR; ++j)
-#pragma unroll
-            for (int q = 0; q < P; ++q) {
+        for (int f = 0; f < NF; ++f) {
+            if (f * G / NF != g)
+                continue;
+            if (f < NR * P) {
+                const int j = f / P, q = f % P;
                 const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) + b_lds +
                                      (uint32_t)(j * (R / 16) * KPK * 1024) +
                                      ((uint32_t)AT::b_half(s, q) << 10) +
                                      ((uint32_t)AT::b_group(s, lane, q) << 8);
                 bf[set][j][q] = *reinterpret_cast<const i32x4*>(lds + off);
-            }
-#pragma unroll
-        for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-            for (int q = 0; q < P; ++q) {
+            } else {
+                const int mi = (f - NR * P) / P, q = (f - NR * P) % P;
                 const uint32_t row = row0 + (uint32_t)(mi * R + lr);
                 const uint32_t off = (uint32_t)(stage * STAGE) + row * KTB +
                                      (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
                 af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
+        }
     };
-    auto mma = [&](int, int, int set) __attribute__((always_inline)) {
+    auto mma = [&](int, int, int set, int g, int G) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mi = 0; mi < MR; ++mi)
-#pragma unroll
-            for (int j = 0; j < NR; ++j)
-                acc[mi][j] = AT::mma(af[set][mi], bf[set][j], acc[mi][j]);
+        for (int a = 0; a < MR * NR; ++a) {
+            if (a * G / (MR * NR) != g)
+                continue;
+            const int mi = a / NR, j = a % NR;
+            acc[mi][j] = AT::mma(af[set][mi], bf[set][j], acc[mi][j]);
+        }
     };
-    k_loop<ST, STEPS, S::LOADS, MR * NR, (MR + NR) * P>(kr.n, load, read, mma);
+    k_loop<ST, STEPS, S::LOADS, step_groups(MR * NR)>(kr.n, min(kr.n, kr.last_full - kr.kt0), load,
+                                                      read, mma);
 
     if constexpr (MODE == MODE_SPLIT) {
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
