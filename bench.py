@@ -13,8 +13,12 @@ Measurement:
     torch.cuda.synchronize() on both sides, timed with HIP events on the
     stream the kernels run on (torch's current stream); the calls run back
     to back, so total time / K is the average launch duration.  The K calls
-    are replayed from one HIP graph, behind a short spin kernel so that the
-    start event is reached after the graph has been submitted.
+    are replayed from one HIP graph, enqueued right behind the W warm-up
+    calls, so that the start event is reached with the device busy.
+  * `sustained`: the same graph replayed back to back for --soak seconds,
+    each replay timed by its own events, the shader clock and board power
+    sampled inside the timed half; `roofline.frac_at_sustained_clock` rates
+    that figure against the MFMA peak at the sampled clock.
   * The K calls rotate over enough copies of (A, Bs, C) to exceed twice the
     256 MB Infinity Cache, so every call reads its operands from HBM.
   * `roofline`: algorithmic flops (2MNK, "GEMM Optimization Guide" page,
@@ -283,10 +287,11 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
         else:
             dg.gemm_fp8_scaled(a, bs, N, s_a, s_b, out=c, tile=forced, workspace=workspace)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
     if graph:
+        # One call ahead of the capture (lazy initialisation of the code
+        # object), then the K timed calls captured in one HIP graph.
+        call(0)
+        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -297,17 +302,27 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        hold_stream()
+        # The W warm-up calls are enqueued right ahead of the timed replay,
+        # with no synchronisation between: the GPU runs them while the host
+        # submits the replay, so the start event is reached with the device
+        # busy, and the K timed calls follow back to back.  (A spin kernel
+        # in their place let the shader clock sink before the timed calls:
+        # an isolated launch after an idle gap ran at 1.2-1.4 GHz.)
         wall0 = time.perf_counter()
+        for i in range(warmup):
+            call(i)
         t0.record()
         g.replay()
         t1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
+        sustained = sustained_with_clock(g, steps, soak) if soak > 0 else None
         del g
-        clock = clock_under_load(call, soak) if soak > 0 else None
         return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "kernel_us": [], "tile": tile,
-                "shuffle_us": shuffle_us, "copies": copies, "clock": clock}
+                "shuffle_us": shuffle_us, "copies": copies, "sustained": sustained}
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)] if per_launch else []
@@ -326,11 +341,48 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
     kern_us = [s.elapsed_time(e) * 1e3 for s, e in ev] if per_launch else []
-    clock = clock_under_load(call, soak) if soak > 0 else None
     return {
         "total_ms": total_ms, "wall_s": wall, "kernel_us": kern_us, "tile": tile,
-        "shuffle_us": shuffle_us, "copies": copies, "clock": clock,
+        "shuffle_us": shuffle_us, "copies": copies, "sustained": None,
     }
+
+
+def sustained_with_clock(g, steps: int, seconds: float):
+    """sustained_replay with clock / power samples taken inside the timed
+    second half (replays stay queued while the samples are read)."""
+    import torch
+    out = {"samples": []}
+    t_start = time.perf_counter()
+    next_sample = 0.0
+    evs = []
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        evs.append((e0, e1))
+        now = time.perf_counter() - t_start
+        if len(evs) >= 3:
+            evs[-3][1].synchronize()
+        if now >= seconds / 2 and now >= next_sample and "error" not in out:
+            next_sample = now + 0.05      # every 50 ms: the queries take host time
+            try:
+                out["samples"].append((torch.cuda.clock_rate(), torch.cuda.power_draw()))
+            except Exception as e:  # noqa: BLE001 - any query failure means "unavailable"
+                out["error"] = f"{type(e).__name__}: {e}"
+        if now >= seconds:
+            break
+    torch.cuda.synchronize()
+    half = len(evs) // 2
+    per_call = sorted(a.elapsed_time(b) * 1e3 / steps for a, b in evs[half:])
+    mhz = [c for c, _ in out["samples"]]
+    watts = [p / 1000.0 if p > 20000 else float(p) for _, p in out["samples"]]
+    return {"per_call_us": round(per_call[len(per_call) // 2], 3), "replays": len(evs),
+            "timed_replays": len(evs) - half, "seconds": round(time.perf_counter() - t_start, 3),
+            "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1) if mhz else None,
+            "gfx_mhz_min_max": [min(mhz), max(mhz)] if mhz else None,
+            "power_w_mean": round(sum(watts) / len(watts), 1) if watts else None,
+            "clock_samples": len(mhz), **({"error": out["error"]} if "error" in out else {})}
 
 
 def hold_stream(stream=None):
@@ -508,41 +560,6 @@ def run_graph(name: str, reps: int, copies: int):
     return time_graph(gemm_call(name, sets, scales), reps), shuffle_us
 
 
-def clock_under_load(call, seconds: float = 1.5):
-    """Shader clock and board power while `call` runs back to back for about
-    `seconds`, read in-process (torch.cuda.clock_rate / power_draw, which
-    query amdsmi) at 2/3 and at the end of the soak, while kernels are still
-    queued.  The timed steps are too short for the board to reach its
-    power-limited steady state, so this is reported beside them, not used in
-    `value`.  Returns None when the queries are unavailable."""
-    import torch
-    t0 = time.perf_counter()
-    marks = (t0 + seconds * 2 / 3, t0 + seconds)
-    samples = []
-    i = 0
-    while len(samples) < len(marks):
-        call(i)
-        i += 1
-        if i % 16 == 0:
-            torch.cuda.synchronize()
-            call(i)          # keep the device busy while sampling
-            i += 1
-            if time.perf_counter() >= marks[len(samples)]:
-                try:
-                    samples.append((torch.cuda.clock_rate(), torch.cuda.power_draw()))
-                except Exception as e:  # noqa: BLE001 - any query failure means "unavailable"
-                    torch.cuda.synchronize()
-                    return {"error": f"{type(e).__name__}: {e}"}
-    torch.cuda.synchronize()
-    mhz = [c for c, _ in samples]
-    pw = [p for _, p in samples]
-    # power_draw reports milliwatts on some stacks and watts on others
-    watts = [p / 1000.0 if p > 20000 else float(p) for p in pw]
-    return {"gfx_mhz": mhz, "power_w": [round(w, 1) for w in watts], "calls": i,
-            "source": f"torch.cuda.clock_rate/power_draw at 2/3 and end of a {seconds:.1f} s "
-                      f"soak of the timed call"}
-
-
 # ------------------------------------------------------------ CPU oracle
 def cpu_baseline(name: str, budget_s: float = 20.0):
     """The oracle on whole rows of C of the same workload, scaled to TFLOP/s."""
@@ -563,7 +580,8 @@ def cpu_baseline(name: str, budget_s: float = 20.0):
             break
         rows = min(M, max(rows * 2, int(rows * budget_s / 2 / max(el, 1e-3))))
     val = flops(rows, N, K) / el / 1e12
-    return {"value": val, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": val, "unit": "TFLOP/s", "cores": threads, "host_cpu_count": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{rows} whole rows of C ({rows}x{N}x{K}, {rows * N * K / 1e9:.2f} G multiply-adds, "
                       f"fp64 triple loop on {threads} threads) in {el:.1f} s"}
 
@@ -580,8 +598,9 @@ def main(argv=None):
                     help="operand sets rotated through the timed calls (0 = enough to exceed twice "
                          "the Infinity Cache, so operands come from HBM; 1 = hot cache)")
     ap.add_argument("--soak", type=float, default=1.5,
-                    help="seconds of back-to-back calls after the timed steps, sampling the shader "
-                         "clock and board power (0 = skip)")
+                    help="seconds of back-to-back replays of the timed graph after the timed steps, "
+                         "timed by their own events, with the shader clock and board power sampled "
+                         "in the timed half (0 = skip)")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. tiled:256x256 or skinny:16x32")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
@@ -637,7 +656,7 @@ def main(argv=None):
     secondary = None
     if not args.no_secondary and name != DECODE:
         dM, dN, dK, ddt = WORKLOADS[DECODE][:4]
-        us_cold, _ = run_graph(DECODE, reps=60, copies=6)
+        us_cold, dshuf = run_graph(DECODE, reps=60, copies=6)
         us_hot, _ = run_graph(DECODE, reps=60, copies=1)
         gb = alg_bytes(dM, dN, dK, ddt)
         secondary = {
@@ -646,6 +665,8 @@ def main(argv=None):
             "us_cold": round(us_cold, 3), "GBps_cold": round(gb / (us_cold * 1e-6) / 1e9, 1),
             "frac_hbm_cold": round(gb / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "us_hot_mall": round(us_hot, 3), "GBps_hot_mall": round(gb / (us_hot * 1e-6) / 1e9, 1),
+            "shuffle_b_us": round(dshuf, 2),
+            "shuffle_b_amortized_below_1pct_after_calls": math.ceil(99.0 * dshuf / us_cold),
             "timing": "hipGraph of 60 launches, before the headline's steps; cold = 6 rotated "
                       "operand copies (541 MB)",
         }
@@ -697,6 +718,10 @@ def main(argv=None):
                      "timing": ("HIP events around the K back-to-back calls on the kernels' stream"
                                 + ("" if args.eager else ", replayed from one HIP graph"))},
         "shuffle_b_us": round(r["shuffle_us"], 2),
+        # the preshuffle runs once per weight: the number of GEMM calls on the
+        # same weight after which its cost is at most 1 % of the total
+        "shuffle_b_amortized_below_1pct_after_calls":
+            math.ceil(99.0 * r["shuffle_us"] / kern_avg) if kern_avg > 0 else None,
     }
     if bound == "mfma":
         out["config"]["pct_of_mfma_peak"] = round(100 * value / PEAK_TFLOPS[dt], 2)
@@ -706,12 +731,21 @@ def main(argv=None):
         out["roofline"]["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes",
                                                                  "fetch_factor", "write_factor",
                                                                  "source")}
-    clk = r["clock"]
-    out["clock_under_load"] = clk
-    if clk and clk.get("gfx_mhz") and bound == "mfma" and min(clk["gfx_mhz"]) > 0:
-        # the same kernel against the MFMA peak at the clock the chip sustains
-        mhz = sum(clk["gfx_mhz"]) / len(clk["gfx_mhz"])
-        out["roofline"]["frac_at_sustained_clock"] = round(achieved / (peak * mhz / 2400.0), 4)
+    sus = r["sustained"]
+    if sus:
+        # the same graph replayed back to back for about --soak seconds: the
+        # board at its loaded power state, timed by its own events, with the
+        # shader clock sampled inside the same interval
+        us = sus["per_call_us"]
+        sus["value"] = round(flops(M, N, K) / (us * 1e-6) / 1e12, 2) if bound == "mfma" else \
+            round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)
+        sus["unit"] = unit_r
+        sus["frac"] = round(sus["value"] / peak, 4)
+        out["sustained"] = sus
+        if bound == "mfma" and sus.get("gfx_mhz_mean"):
+            # against the MFMA peak at the clock sampled during that interval
+            out["roofline"]["frac_at_sustained_clock"] = round(
+                sus["value"] / (peak * sus["gfx_mhz_mean"] / 2400.0), 4)
     if secondary is not None:
         out["secondary"] = secondary
     if not args.no_cpu:
