@@ -31,6 +31,9 @@ GEMM_ERR_HIP = 3
 GEMM_BF16 = 0
 GEMM_FP8_E4M3 = 1
 
+# bytes of the library's own split-K scratch behind gemm_bf16_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 GEMM_KERNEL_TILED = 0
 GEMM_KERNEL_SKINNY = 1
 GEMM_KERNEL_TILED_AB = 2
@@ -39,7 +42,7 @@ GEMM_KERNEL_TILED_PP = 3
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
            "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex", "shuffle_b_t",
-           "transpose_2d", "gemm_plan")
+           "transpose_2d", "gemm_plan", "gemm_bf16_noalloc")
 
 # gemm_activation
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_SILU, GEMM_ACT_GELU_ERF, GEMM_ACT_GELU_TANH = 0, 1, 2, 3, 4
@@ -229,6 +232,8 @@ def _load_lib():
     lib.shuffle_b_t.restype = ctypes.c_int
     lib.transpose_2d.argtypes = [P, I64, P, I64, I64, I64, ctypes.c_int32, P]
     lib.transpose_2d.restype = ctypes.c_int
+    lib.gemm_bf16_noalloc.argtypes = [P, I64, P, P, I64, I64, I64, I64, ctypes.POINTER(GemmTile), P]
+    lib.gemm_bf16_noalloc.restype = ctypes.c_int
     lib.gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int32, ctypes.c_size_t,
                               ctypes.POINTER(GemmTile), ctypes.POINTER(GemmTile),
                               ctypes.POINTER(I64)]
@@ -548,4 +553,20 @@ def gemm_fp8_scaled(A, Bs, N: int, scale_a, scale_b, out=None, tile: Tile | None
                                     _tile_ptr(tile), ws, nbytes, _stream_ptr(A))
     if st != GEMM_OK:
         raise GemmError("gemm_fp8_scaled", st)
+    return C
+
+
+def gemm_bf16_noalloc(A, Bs, N: int, out, tile: Tile | None = None):
+    """gemm_bf16 for callers that cannot allocate: split-K partials go to the
+    library's fixed scratch array (NOALLOC_SCRATCH_BYTES per GPU), `out` must
+    be given, and nothing is allocated.  Calls on one GPU must not overlap."""
+    _check_operands(GEMM_BF16, A, Bs, N)
+    if out is None:
+        raise ValueError("gemm_bf16_noalloc: out must be given (the call allocates nothing)")
+    C = _out(A, N, out)
+    M, K = A.shape
+    st = lib.gemm_bf16_noalloc(A.data_ptr(), A.stride(0), Bs.data_ptr(), C.data_ptr(), C.stride(0),
+                               M, N, K, _tile_ptr(tile), _stream_ptr(A))
+    if st != GEMM_OK:
+        raise GemmError("gemm_bf16_noalloc", st)
     return C

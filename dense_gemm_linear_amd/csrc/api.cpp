@@ -308,10 +308,56 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
+// ---- scratch for callers that cannot allocate (gemm_bf16_noalloc)
+//
+// The split-K partials of gemm_bf16_noalloc live in this file-scope device
+// array: each GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  In host code `scratch` is a host-side
+// stand-in, not a device address; the device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// pointer is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`: its device address, looked up on
+// the first call on that device.  NULL if the lookup fails.
+void* device_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
 }  // namespace
 }  // namespace dg
 
 extern "C" {
+
+gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, const gemm_tile* tile,
+                              void* stream)
+{
+    // A forced split-K tile whose partials exceed the scratch array is
+    // refused before any device call.
+    if (tile && M > 0 && N > 0 && K > 0 &&
+        gemm_workspace_bytes(M, N, K, GEMM_BF16, tile) > (size_t)GEMM_NOALLOC_SCRATCH_BYTES)
+        return GEMM_ERR_INVALID_VALUE;
+    void* ws = dg::device_scratch();
+    if (!ws)
+        return GEMM_ERR_HIP;
+    return dg::run_gemm(dg::DT_BF16, A, lda, Bs, nullptr, nullptr, C, ldc, M, N, K, tile, nullptr,
+                        ws, (size_t)GEMM_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 gemm_status gemm_bf16(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C, int64_t ldc,
                       int64_t M, int64_t N, int64_t K, const gemm_tile* tile, void* stream)

@@ -362,6 +362,34 @@ gemm_status gemm_fp8_scaled_ex(const uint8_t* A, int64_t lda, const void* Bs,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gemm_bf16_noalloc -- gemm_bf16_ws for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The split-K workspace is a fixed array of
+ * GEMM_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, held
+ * until the process ends); the call allocates nothing and calls no
+ * allocating routine.
+ *
+ *   Arguments as for gemm_bf16; tile NULL = select_tile_ws(...,
+ *   GEMM_NOALLOC_SCRATCH_BYTES, ...) (or gemm_plan's two launches).
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (nothing in it needs to start at zero: every split-K
+ * slice writes its whole partial plane before the reduction reads it).
+ * Calls that overlap in time on one GPU -- concurrent streams, or several
+ * host threads -- race on it and must be serialised by the caller.  The
+ * first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress); make it outside graph capture.
+ *
+ * Errors as for gemm_bf16_ws, with INVALID_VALUE when a forced split-K tile
+ * needs more than GEMM_NOALLOC_SCRATCH_BYTES (gemm_workspace_bytes), and
+ * GEMM_ERR_HIP when the array's address cannot be obtained.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, uint16_t* C,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, const gemm_tile* tile,
+                              void* stream);
+
+/*
  * gemm_plan -- the launches gemm_bf16 / gemm_fp8_scaled (and their _ws / _ex
  * forms with `workspace_bytes`) make for an M x N x K GEMM when the caller
  * passes tile == NULL, on a device with num_cus compute units.  Pure host
