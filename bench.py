@@ -43,9 +43,10 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 CUS = 256
-# split-K: the workspace the bench hands the library (the selector weighs
-# split-K tiles whose fp32 partials fit), and the slice counts a sweep tries
-WORKSPACE_MIB = 64
+# split-K / stream-K: the workspace the bench hands the library (the selector
+# weighs split-K tiles whose fp32 partials fit, the launch plan stream-K), and
+# the slice counts a sweep tries
+WORKSPACE_MIB = 128
 SPLITS = (2, 3, 4, 6, 8, 12, 16)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
@@ -237,6 +238,9 @@ def parse_tile(spec: str | None):
     import dense_gemm_linear_amd as dg
     kind, dims = spec.split(":")
     atom, stages, tile_k = 16, 0, 0
+    stream_k = dims.endswith("streamk")
+    if stream_k:
+        dims = dims[:-len("streamk")]
     m = re.fullmatch(r"(\d+x\d+(?:w\d+)?)(?:a(\d+))?(?:s(\d+))?(?:k(\d+))?(?:sk(\d+))?", dims)
     if not m:
         raise ValueError(f"bad tile spec {spec!r}")
@@ -251,9 +255,11 @@ def parse_tile(spec: str | None):
         waves = int(w)
     tm, tn = (int(x) for x in dims.split("x"))
     if kind == "tiled":
-        return dg.tiled(tm, tn, waves, atom, stages, tile_k, k_split)
+        t = dg.tiled(tm, tn, waves, atom, stages, tile_k, k_split)
+        return dg.with_stream_k(t) if stream_k else t
     if kind == "ab":
-        return dg.tiled_ab(tm, tn, waves, atom, stages, tile_k, k_split)
+        t = dg.tiled_ab(tm, tn, waves, atom, stages, tile_k, k_split)
+        return dg.with_stream_k(t) if stream_k else t
     if kind == "pp":
         return dg.tiled_pp(tm, tn, atom, stages, tile_k, k_split)
     return dg.skinny(tm, tn, waves)
@@ -277,8 +283,8 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
     copies = len(sets)
     forced = tile
     ws_bytes = 0 if workspace is None else workspace.numel()
-    if tile is None:
-        tile = dg.select_tile(M, N, K, dt, workspace_bytes=ws_bytes)
+    if tile is None:   # the library's launch plan (its first launch)
+        tile = dg.plan(M, N, K, dt, CUS, ws_bytes)[0]
 
     def call(i):
         a, bs, c = sets[i % copies]
@@ -809,6 +815,16 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> in
             if 0 < need <= ws_bytes and need not in seen:
                 seen.add(need)
                 tiles.append(ts)
+    # stream-K forms of the rungs that have one, for shapes filling less than
+    # one round of the CUs
+    for t in list(tiles):
+        if t.kernel in (dg.GEMM_KERNEL_TILED, dg.GEMM_KERNEL_TILED_AB) and t.k_split <= 1 and \
+                128 * 128 <= t.tile_m * t.tile_n <= 128 * 256 and \
+                -(-M // t.tile_m) * -(-N // t.tile_n) < CUS:
+            ts = dg.with_stream_k(t)
+            need = dg.workspace_bytes(M, N, K, dt, ts)
+            if 0 < need <= ws_bytes:
+                tiles.append(ts)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     sets, scales, _ = setup
     res = {}
@@ -818,7 +834,7 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> in
         print(json.dumps({"sweep": name, "tile": t.name, "kernel_us_median": round(us, 3),
                           "tflops": round(flops(M, N, K) / (us * 1e-6) / 1e12, 1),
                           "gbps": round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)}), flush=True)
-    pick = dg.select_tile(M, N, K, dt, workspace_bytes=ws_bytes)
+    pick = dg.plan(M, N, K, dt, CUS, ws_bytes)[0]
     best = min(res, key=res.get)
     print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
                       "best": best, "best_us": round(res[best], 3),

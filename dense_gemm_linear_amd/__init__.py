@@ -62,7 +62,7 @@ class GemmTile(ctypes.Structure):
                 ("tile_k", ctypes.c_int32), ("atom", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("k_split", ctypes.c_int32), ("lds_stages", ctypes.c_int32),
                 ("tile_eff", ctypes.c_float), ("wq_eff", ctypes.c_float),
-                ("predicted_us", ctypes.c_float)]
+                ("predicted_us", ctypes.c_float), ("stream_k", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -78,6 +78,7 @@ class Tile:
     tile_eff: float = 0.0
     wq_eff: float = 0.0
     predicted_us: float = 0.0
+    stream_k: int = 0
 
     @property
     def name(self) -> str:
@@ -88,6 +89,8 @@ class Tile:
         pipe = (f"s{self.lds_stages}" if self.lds_stages else "") + (f"k{self.tile_k}" if self.tile_k else "")
         if self.kernel != GEMM_KERNEL_SKINNY and self.k_split > 1:
             pipe += f"sk{self.k_split}"
+        if self.stream_k:
+            pipe += "streamk"
         if self.kernel == GEMM_KERNEL_TILED:
             return f"tiled{self.tile_m}x{self.tile_n}" + ("" if self.waves == 4 else f"w{self.waves}") + \
                 atom + pipe
@@ -99,12 +102,13 @@ class Tile:
 
     def to_c(self) -> GemmTile:
         return GemmTile(self.kernel, self.tile_m, self.tile_n, self.tile_k, self.atom, self.waves,
-                        self.k_split, self.lds_stages, self.tile_eff, self.wq_eff, self.predicted_us)
+                        self.k_split, self.lds_stages, self.tile_eff, self.wq_eff, self.predicted_us,
+                        self.stream_k)
 
     @staticmethod
     def from_c(t: GemmTile) -> "Tile":
         return Tile(t.kernel, t.tile_m, t.tile_n, t.tile_k, t.atom, t.waves, t.k_split,
-                    t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us)
+                    t.lds_stages, t.tile_eff, t.wq_eff, t.predicted_us, t.stream_k)
 
 
 def tiled(tm: int, tn: int, waves: int = 4, atom: int = 16, stages: int = 0, tile_k: int = 0,
@@ -127,6 +131,14 @@ def tiled_pp(tm: int, tn: int, atom: int = 32, stages: int = 0, tile_k: int = 0,
     """A rung of the ping-pong A+B ladder (8 waves); stages / tile_k 0 = any."""
     return Tile(GEMM_KERNEL_TILED_PP, tm, tn, tile_k=tile_k, atom=atom, waves=8, k_split=k_split,
                 lds_stages=stages)
+
+
+def with_stream_k(tile: Tile) -> Tile:
+    """The same one-pass tiled / A+B rung as a stream-K launch (needs a
+    workspace of workspace_bytes(...) bytes)."""
+    if tile.kernel not in (GEMM_KERNEL_TILED, GEMM_KERNEL_TILED_AB):
+        raise ValueError("stream-K runs on tiled and A+B rungs")
+    return replace(tile, stream_k=1, k_split=1)
 
 
 def with_split(tile: Tile, k_split: int) -> Tile:
@@ -457,7 +469,7 @@ def _workspace(A, N: int, K: int, code: int, tile, workspace):
         if not workspace.is_cuda:
             raise ValueError("workspace must be a device tensor")
         return workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    if tile is None or tile.kernel == GEMM_KERNEL_SKINNY or tile.k_split <= 1:
+    if tile is None or tile.kernel == GEMM_KERNEL_SKINNY or (tile.k_split <= 1 and not tile.stream_k):
         return None, 0
     nbytes = workspace_bytes(A.shape[0], N, K, code, tile)
     if nbytes == 0:

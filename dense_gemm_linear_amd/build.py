@@ -25,7 +25,7 @@ SOURCES = [("api.cpp", "api", []), ("select_tile.cpp", "select_tile", []), ("mis
            ("skinny.hip", "skinny", [])] + \
     [("tiled_inst.hip", f"tiled_d{d}_m{m}_f{f}",
       [f"-DDG_INST_DT={d}", f"-DDG_INST_MODE={m}", f"-DDG_INST_FAMILY={f}"])
-     for d in (0, 1) for m in (0, 1, 2) for f in (0, 1)]
+     for d in (0, 1) for m in (0, 1, 2, 3) for f in (0, 1)]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",

@@ -9,15 +9,48 @@ namespace dg {
 
 hipError_t launch_tiled_rung(int kernel, int dt, int idx, const GemmArgs& a, hipStream_t s)
 {
-    const int mode = a.splits > 1 ? MODE_SPLIT : (a.ep.on ? MODE_EPI : MODE_PLAIN);
+    const int mode = a.sk_count ? MODE_SK : a.splits > 1 ? MODE_SPLIT : (a.ep.on ? MODE_EPI : MODE_PLAIN);
     const int fam = kernel == GEMM_KERNEL_TILED ? 0 : 1;
 #define DG_PICK(D, M, F) \
     if (dt == D && mode == M && fam == F) return launch_inst_##D##_##M##_##F(kernel, idx, a, s);
     DG_PICK(0, 0, 0) DG_PICK(0, 0, 1) DG_PICK(0, 1, 0) DG_PICK(0, 1, 1) DG_PICK(0, 2, 0)
     DG_PICK(0, 2, 1) DG_PICK(1, 0, 0) DG_PICK(1, 0, 1) DG_PICK(1, 1, 0) DG_PICK(1, 1, 1)
-    DG_PICK(1, 2, 0) DG_PICK(1, 2, 1)
+    DG_PICK(1, 2, 0) DG_PICK(1, 2, 1) DG_PICK(0, 3, 0) DG_PICK(0, 3, 1) DG_PICK(1, 3, 0)
+    DG_PICK(1, 3, 1)
 #undef DG_PICK
     return hipErrorInvalidValue;
+}
+
+SkPlan sk_plan(int kernel, int idx, int tm, int tn, int64_t M, int64_t N, int64_t K, int e, int grid)
+{
+    SkPlan pl;
+    memset(&pl, 0, sizeof pl);
+    if ((kernel != GEMM_KERNEL_TILED && kernel != GEMM_KERNEL_TILED_AB) || !sk_rung(tm, tn) ||
+        M <= 0 || N <= 0 || K <= 0 || grid <= 0 || grid > GEMM_STREAM_K_MAX_GRID)
+        return pl;
+    const int kpk = rung_ktb(kernel, idx) / 64;   // 64-byte blocks per k-tile
+    if (kpk <= 0)
+        return pl;
+    const int64_t kblocks = (K * e + 63) / 64;
+    const int nkt = (int)((kblocks + kpk - 1) / kpk);
+    const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+    // whole tiles: every full round but the last when there is a stray one
+    const int64_t dp = tiles >= grid ? (tiles / grid - (tiles % grid ? 1 : 0)) * grid : 0;
+    const int64_t units = (tiles - dp) * nkt;
+    if (units != 0 && units < grid)
+        return pl;                 // a workgroup would get no unit
+    if (tiles > INT32_MAX || units > (INT64_C(1) << 40))
+        return pl;
+    pl.ok = true;
+    pl.grid = grid;
+    pl.dp_tiles = (int)dp;
+    pl.nkt = nkt;
+    pl.tiles = tiles;
+    // partial slots for the largest grid, so the size does not depend on the
+    // device; counters for every tile (an upper bound of the stream-K ones)
+    pl.slot_bytes = (int64_t)GEMM_STREAM_K_MAX_GRID * 2 * tm * tn * 4;
+    pl.ws_bytes = pl.slot_bytes + (tiles * 4 + 255) / 256 * 256;
+    return pl;
 }
 
 namespace {
@@ -75,6 +108,11 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
     if (t.tile_k < 0 || t.tile_k > 4096 || t.lds_stages < 0 || t.k_split < 0 ||
         (t.kernel != GEMM_KERNEL_SKINNY && t.k_split > kMaxKSplit))
         return false;
+    // stream-K: one-pass tiled / A+B rungs with a stream-K instance
+    if (t.stream_k != 0 &&
+        (t.stream_k != 1 || (t.kernel != GEMM_KERNEL_TILED && t.kernel != GEMM_KERNEL_TILED_AB) ||
+         !sk_rung(t.tile_m, t.tile_n) || t.k_split > 1))
+        return false;
     const int atom = t.atom == 0 ? 16 : t.atom;
     const int ktb = t.tile_k * e;
     *idx = -1;
@@ -119,7 +157,7 @@ bool make_epilogue(const gemm_epilogue* e, int64_t N, Epilogue* out)
 hipError_t launch_gemm(int dt, const gemm_tile& t, int idx, const SplitPlan& pl, const void* A,
                        int64_t lda, const void* Bs, const float* sa, const float* sb, uint16_t* C,
                        int64_t ldc, int64_t M, int64_t N, int64_t K, const Epilogue& ep, void* ws,
-                       hipStream_t s)
+                       hipStream_t s, const SkPlan* sk = nullptr)
 {
     const int e = dt == DT_BF16 ? 2 : 1;
     GemmArgs a;
@@ -148,6 +186,17 @@ hipError_t launch_gemm(int dt, const gemm_tile& t, int idx, const SplitPlan& pl,
         return launch_skinny(dt, t.tile_m, t.tile_n, t.k_split == 0 ? 4 : t.k_split, a, s);
     a.tiles_m = (int)((M + t.tile_m - 1) / t.tile_m);
     a.tiles_n = (int)((N + t.tile_n - 1) / t.tile_n);
+    if (t.stream_k && sk && sk->ok) {
+        a.splits = sk->grid;             // the persistent grid
+        a.sk_dp_tiles = sk->dp_tiles;
+        a.sk_nkt = sk->nkt;
+        a.ws = static_cast<float*>(ws);
+        a.sk_count = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + sk->slot_bytes);
+        hipError_t err = launch_zero_u32(a.sk_count, (int)(sk->tiles - sk->dp_tiles), s);
+        if (err == hipSuccess)
+            err = launch_tiled_rung(t.kernel, dt, idx, a, s);
+        return err;
+    }
     hipError_t err = launch_tiled_rung(t.kernel, dt, idx, a, s);
     if (err == hipSuccess && pl.S > 1)
         err = launch_splitk_reduce(a.ws, pl.S, a.M, a.N, pl.ldw, C, ldc, sa, sb, ep, s);
@@ -187,10 +236,24 @@ struct AutoPlan {
     gemm_tile t1, t2;
     int idx1, idx2;
     SplitPlan pl1, pl2;
+    SkPlan sk1;    // the first launch's stream-K plan when t1.stream_k
     int64_t n1;    // columns of the first launch; N: a single launch
 };
 
-bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, AutoPlan* ap)
+// Stream-K in place of a one-pass tile that fills less than one round of
+// the CUs, priced from measurements on MI355X (LLaMA prefill 597 x 11008 x
+// 4096 on 128 x 256 tiles, per-phase timestamps): a k-tile unit takes about
+// 1.45 times as long as in the one-pass launch (every CU streams, and
+// neighbouring workgroups read different K ranges of the same tiles, so the
+// L2 serves fewer re-reads), and a cut tile's fix-up (partials written
+// through to memory, read back past the caches) costs about 20 us at the
+// end of the launch.  Taken when that is below 95 % of the one-pass time:
+// shapes whose tiles leave most CUs idle.
+constexpr double kSkUnitSlowdown = 1.45;
+constexpr double kSkFixupUs = 20.0;
+
+bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, AutoPlan* ap,
+               bool allow_sk = true)
 {
     const int e = dt == DT_BF16 ? 2 : 1;
     memset(ap, 0, sizeof *ap);
@@ -201,6 +264,21 @@ bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes
     ap->pl1 = tile_split(ap->t1, ap->idx1, M, N, K, e);
     if (ap->pl1.ws_bytes > (int64_t)ws_bytes)
         return false;
+    if (allow_sk && ap->pl1.S == 1 && ap->t1.kernel != GEMM_KERNEL_SKINNY) {
+        const int grid = std::min(cus, (int)GEMM_STREAM_K_MAX_GRID);
+        const SkPlan sk = sk_plan(ap->t1.kernel, ap->idx1, ap->t1.tile_m, ap->t1.tile_n, M, N, K,
+                                  e, grid);
+        if (sk.ok && sk.tiles < grid && sk.ws_bytes <= (int64_t)ws_bytes) {
+            const double t_sk =
+                ap->t1.predicted_us * kSkUnitSlowdown * (double)sk.tiles / grid + kSkFixupUs;
+            if (t_sk < 0.95 * ap->t1.predicted_us) {
+                ap->t1.stream_k = 1;
+                ap->t1.predicted_us = (float)t_sk;
+                ap->sk1 = sk;
+                return true;
+            }
+        }
+    }
     const int64_t n1 = tail_split_columns(ap->t1, ap->pl1, M, N, cus);
     if (n1 == 0)
         return true;
@@ -258,10 +336,24 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     gemm_tile t;
     int idx = -1;
     SplitPlan pl{1, 0, 0, 0};
+    SkPlan sk;
+    memset(&sk, 0, sizeof sk);
     if (tile) {
         t = *tile;
         if (!resolve_tile(t, M, e, &idx))
             return GEMM_ERR_UNSUPPORTED;
+        if (t.stream_k) {
+            // no fused epilogue with stream-K; the workspace is checked with
+            // the largest grid, the launch uses the device's
+            if (ep.on || t.k_split > 1)
+                return GEMM_ERR_UNSUPPORTED;
+            const SkPlan chk = sk_plan(t.kernel, idx, t.tile_m, t.tile_n, M, N, K, e,
+                                       GEMM_STREAM_K_MAX_GRID);
+            if (!chk.ok)
+                return GEMM_ERR_UNSUPPORTED;
+            if (chk.ws_bytes > (int64_t)ws_bytes)
+                return ws_bytes == 0 ? GEMM_ERR_UNSUPPORTED : GEMM_ERR_INVALID_VALUE;
+        }
         pl = tile_split(t, idx, M, N, K, e);
         if (pl.S > 1 && !partial_plane_fits(M, pl.ldw))
             return GEMM_ERR_UNSUPPORTED;
@@ -276,13 +368,20 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (K == 0)
         return launch_zero_c(C, ldc, M, N, ep, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    if (tile && t.stream_k) {
+        sk = sk_plan(t.kernel, idx, t.tile_m, t.tile_n, M, N, K, e,
+                     std::min(cus, (int)GEMM_STREAM_K_MAX_GRID));
+        if (!sk.ok)
+            return GEMM_ERR_UNSUPPORTED;
+    }
     if (!tile) {
         AutoPlan ap;
-        if (!plan_auto(M, N, K, dt, cus, ws_bytes, &ap))
+        if (!plan_auto(M, N, K, dt, cus, ws_bytes, &ap, !ep.on))
             return GEMM_ERR_UNSUPPORTED;   // the selector names only rungs that exist
         t = ap.t1;
         idx = ap.idx1;
         pl = ap.pl1;
+        sk = ap.sk1;
         if (ap.n1 < N) {
             const int64_t n1 = ap.n1;
             const int64_t be = 64 * ((K * e + 63) / 64) * 16;   // Bs bytes per 16 columns
@@ -304,7 +403,8 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
             return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
         }
     }
-    const hipError_t err = launch_gemm(dt, t, idx, pl, A, lda, Bs, sa, sb, C, ldc, M, N, K, ep, ws, s);
+    const hipError_t err =
+        launch_gemm(dt, t, idx, pl, A, lda, Bs, sa, sb, C, ldc, M, N, K, ep, ws, s, &sk);
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -420,6 +520,13 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
     int idx = -1;
     if (!dg::resolve_tile(*tile, M, e, &idx))
         return 0;
+    if (tile->stream_k) {
+        if (tile->k_split > 1)
+            return 0;
+        const dg::SkPlan sk = dg::sk_plan(tile->kernel, idx, tile->tile_m, tile->tile_n, M, N, K, e,
+                                          GEMM_STREAM_K_MAX_GRID);
+        return sk.ok ? (size_t)sk.ws_bytes : 0;
+    }
     return (size_t)dg::tile_split(*tile, idx, M, N, K, e).ws_bytes;
 }
 

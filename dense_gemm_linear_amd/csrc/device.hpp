@@ -42,6 +42,23 @@ __device__ __forceinline__ i32x4 load16_s(rsrc_t r, uint32_t voff, uint32_t soff
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
+// Cache policy of a buffer access that must be coherent across XCDs
+// without whole-cache maintenance: sc0 | sc1 (gfx940-family bits 0 and 4),
+// i.e. system scope -- stores write through the L2 to memory, loads miss in
+// the L1 and L2.  For data handed between workgroups on different XCDs
+// inside one kernel (the stream-K partials).
+constexpr int kCpolCoherent = 0x11;
+
+__device__ __forceinline__ void store16_coherent(rsrc_t r, uint32_t off, i32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCpolCoherent);
+}
+
+__device__ __forceinline__ i32x4 load16_coherent(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolCoherent);
+}
+
 // A 16-byte LDS DMA (global -> LDS, no register round trip): lane l's 16
 // bytes land at lds_base + 16 l; m0 holds the wave-uniform lds_base.
 __device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff)

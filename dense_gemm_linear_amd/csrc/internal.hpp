@@ -103,6 +103,7 @@ bool skinny_supported(int tm, int tn, int waves);
 DG_DECL_INST(0, 0, 0) DG_DECL_INST(0, 0, 1) DG_DECL_INST(0, 1, 0) DG_DECL_INST(0, 1, 1)
 DG_DECL_INST(0, 2, 0) DG_DECL_INST(0, 2, 1) DG_DECL_INST(1, 0, 0) DG_DECL_INST(1, 0, 1)
 DG_DECL_INST(1, 1, 0) DG_DECL_INST(1, 1, 1) DG_DECL_INST(1, 2, 0) DG_DECL_INST(1, 2, 1)
+DG_DECL_INST(0, 3, 0) DG_DECL_INST(0, 3, 1) DG_DECL_INST(1, 3, 0) DG_DECL_INST(1, 3, 1)
 #undef DG_DECL_INST
 // rung idx of `kernel` (tiled, A+B or ping-pong) for element type dt, in the
 // variant the arguments ask for (split-K, fused epilogue, or plain)
@@ -146,6 +147,19 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int e, int ktb, int k_spli
 int rung_ktb(int kernel, int idx);
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
                  gemm_tile* out);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+// Stream-K plan of a resolved tiled / A+B rung (see gemm_workspace_bytes):
+// grid G, whole tiles [0, dp_tiles), k-tiles per tile nkt (the rung's k-tile
+// size), the partial slots' bytes and the whole workspace.  ok = false when
+// the rung has no stream-K instance or the shape has fewer units than G.
+struct SkPlan {
+    bool ok;
+    int grid, dp_tiles, nkt;
+    int64_t tiles, slot_bytes, ws_bytes;
+};
+// stream-K instances: outputs of 128 x 128 to 128 x 256
+constexpr bool sk_rung(int tm, int tn) { return tm * tn >= 128 * 128 && tm * tn <= 128 * 256; }
+SkPlan sk_plan(int kernel, int idx, int tm, int tn, int64_t M, int64_t N, int64_t K, int e, int grid);
 hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,
                                 int64_t ldc, const float* sa, const float* sb, Epilogue ep,
                                 hipStream_t s);

@@ -38,7 +38,7 @@ enum { DT_BF16 = 0, DT_FP8 = 1 };
 // partials, the epilogue runs in the reduction), one-pass with the fused
 // epilogue.  Separate instances, so that no variant pays for another's code
 // in registers.
-enum { MODE_PLAIN = 0, MODE_SPLIT = 1, MODE_EPI = 2 };
+enum { MODE_PLAIN = 0, MODE_SPLIT = 1, MODE_EPI = 2, MODE_SK = 3 };
 // activation codes (the values of gemm_activation)
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2, ACT_GELU_ERF = 3, ACT_GELU_TANH = 4 };
 
@@ -158,6 +158,15 @@ struct GemmArgs {
     int ldw;
     float* ws;
     Epilogue ep;
+    // Stream-K (MODE_SK): a persistent grid of G workgroups.  Tiles
+    // [0, sk_dp_tiles) run whole, logical workgroup g taking tiles g, g + G,
+    // ...; the (tile, k-tile) units of the other tiles are cut into G equal
+    // contiguous ranges, one per workgroup.  A tile cut between workgroups
+    // is finished by the last of them to arrive (sk_count), from fp32
+    // partials in ws: two slots of TM x TN floats per workgroup.
+    int sk_dp_tiles;
+    int sk_nkt;           // k-tiles per tile, in the kernel's own k-tile size
+    uint32_t* sk_count;   // per stream-K tile; zero on entry, left zero on exit
 };
 
 // The K range of one workgroup: k-tiles [kt0, kt0 + n) of KTB bytes, and the
@@ -211,16 +220,32 @@ __device__ __forceinline__ int split_slice(const GemmArgs& p, int& wg)
 // contiguous run of logical tiles, then walk the logical tiles in groups of
 // GROUP_M tile rows, column by column, so tiles that share A rows or B columns
 // run at the same time on the same L2.
+__device__ __forceinline__ int xcd_remap(int wg, int G)
+{
+    if (!DG_XCD_REMAP)
+        return wg;
+    const int x = wg & 7, j = wg >> 3;
+    const int q = G >> 3, r = G & 7;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
+// Logical tile t -> (tile row, tile column), GROUP_M tile rows at a time.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_raster(int t, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int per_group = GROUP_M * tiles_n;
+    const int grp = t / per_group;
+    const int first = grp * GROUP_M;
+    const int gm = min(tiles_m - first, GROUP_M);
+    const int in = t - grp * per_group;
+    tm = first + in % gm;
+    tn = in / gm;
+}
+
 template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn)
 {
-    const int G = tiles_m * tiles_n;
-    int t = wg;
-    if (DG_XCD_REMAP) {
-        const int x = wg & 7, j = wg >> 3;
-        const int q = G >> 3, r = G & 7;
-        t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
-    }
+    const int t = xcd_remap(wg, tiles_m * tiles_n);
     const int per_group = GROUP_M * tiles_n;
     const int grp = t / per_group;
     const int first = grp * GROUP_M;
@@ -618,6 +643,173 @@ __device__ __forceinline__ void store_partial(const GemmArgs& p,
         }
 }
 
+// s_waitcnt (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vector-memory counter at most n, every LDS access of this
+// wave complete (lgkmcnt 0; expcnt left at its maximum).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// ---------------------------------------------------------------------------
+// Stream-K (the TraceLens GEMM analysis page, "Important considerations",
+// names Stream-K among what its tile/wave model leaves out).  The U = tiles x
+// k-tiles units of the stream-K tiles, in tile order, are cut into G
+// contiguous ranges, [sk_start(g), sk_start(g + 1)) for logical workgroup g.
+
+__device__ __forceinline__ int64_t sk_start(int64_t U, int G, int g)
+{
+    return U * g / G;
+}
+
+// The logical workgroup whose range holds unit u.
+__device__ __forceinline__ int sk_owner(int64_t U, int G, int64_t u)
+{
+    int g = (int)(u * G / U);
+    while (g + 1 < G && sk_start(U, G, g + 1) <= u)
+        ++g;
+    while (g > 0 && sk_start(U, G, g) > u)
+        --g;
+    return g;
+}
+
+// A workgroup's fp32 partial tile, in the order its lanes hold it: for
+// wave w and atom (mi, j), piece q (accumulator elements 4q .. 4q + 3) of
+// all 64 lanes is one contiguous 1 KiB run, lane l at 16 l, so every store
+// and load instruction moves whole cache lines (the stores write through
+// to memory).  Slot s of logical workgroup g starts at ws + (2 g + s) TM TN
+// floats.  sk_lane_off is the byte offset of piece 0 of lane l.
+template <class AT, int MR, int NR>
+__device__ __forceinline__ uint32_t sk_lane_off(int wave, int mi, int j, int lane)
+{
+    return (uint32_t)(((wave * MR + mi) * NR + j) * AT::NACC * 256 + lane * 16);
+}
+
+template <class AT, int MR, int NR>
+__device__ __forceinline__ void sk_store_partial(rsrc_t rs, const typename AT::acc_t (&acc)[MR][NR],
+                                                 int wave, int lane)
+{
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const uint32_t o = sk_lane_off<AT, MR, NR>(wave, mi, j, lane);
+#pragma unroll
+            for (int e = 0; e < AT::NACC; e += 4) {
+                i32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = acc[mi][j][e + i];   // through a scalar (see store_partial)
+                    v[i] = __float_as_int(x);
+                }
+                store16_coherent(rs, o + 256u * e, v);   // piece e / 4: 1 KiB further
+            }
+        }
+}
+
+// The fix-up of stream-K tile ts after this workgroup (logical g) wrote its
+// partial to slot `slot` (`flag`: one int of the kernel's LDS, free between
+// the K loop and the epilogue; a separate LDS variable made the compiler
+// guard every LDS read of the K loop with a wait for all LDS DMA loads).
+// Fix-up steps:
+// partial to slot `slot`: count the segment in; the last segment to arrive
+// sums every segment's partial in k order, ((0 + p0) + p1) + ..., into acc
+// and returns true (the caller then stores C).  Nothing waits on another
+// workgroup, so no grid-wide residency is assumed.  The partials cross XCDs,
+// each with its own L2: they are written through to memory and read past
+// the caches (kCpolCoherent), every wave waits for its stores to complete
+// before the workgroup barrier, and the counter is a system-scope atomic
+// (performed past the L2s), so the last arriver reads every partial as
+// written.  (Device-scope fences
+// instead wrote back and invalidated the whole L2 at every cut tile: the
+// LLaMA prefill took 251 us against 61 us without stream-K.)
+template <class AT, int MR, int NR, int TM, int TN>
+__device__ __forceinline__ bool sk_fixup(const GemmArgs& p, typename AT::acc_t (&acc)[MR][NR],
+                                         int* flag, int g, int G, int64_t U, int ts, int slot,
+                                         int wave, int lane)
+{
+    constexpr uint32_t SLOT_BYTES = (uint32_t)TM * TN * 4u;
+    const rsrc_t mine = make_rsrc(p.ws + ((size_t)g * 2 + slot) * TM * TN, SLOT_BYTES);
+    sk_store_partial<AT, MR, NR>(mine, acc, wave, lane);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));   // this wave's partial stored
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = (int)__hip_atomic_fetch_add(p.sk_count + ts, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    const int arrived = *flag;
+    // the flag lives in the LDS the epilogue stages C through: every wave
+    // has read it before any wave goes on
+    __syncthreads();
+    const int64_t u0 = (int64_t)ts * p.sk_nkt;
+    const int g_first = sk_owner(U, G, u0);
+    const int nseg = sk_owner(U, G, u0 + p.sk_nkt - 1) - g_first + 1;
+    if (arrived != nseg - 1)
+        return false;
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[mi][j] = zero_acc<AT>();
+    for (int k = 0; k < nseg; ++k) {
+        const int gk = g_first + k;
+        // slot 0: the tile is the first item of gk's range
+        const int sk = sk_start(U, G, gk) >= u0 ? 0 : 1;
+        const rsrc_t rk = make_rsrc(p.ws + ((size_t)gk * 2 + sk) * TM * TN, SLOT_BYTES);
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                const uint32_t o = sk_lane_off<AT, MR, NR>(wave, mi, j, lane);
+#pragma unroll
+                for (int e = 0; e < AT::NACC; e += 4) {
+                    const i32x4 v = load16_coherent(rk, o + 256u * e);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[mi][j][e + i] += __int_as_float(v[i]);
+                    }
+                }
+            }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(p.sk_count + ts, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return true;
+}
+
+// Runs item(tile, kb, ke, slot) for this workgroup's work: its whole tiles,
+// then its stream-K range cut at tile boundaries (k-tiles [kb, ke) of the
+// tile; slot = which of its two partial slots a cut tile uses).
+template <class Item>
+__device__ __forceinline__ void sk_for_each(const GemmArgs& p, Item& item)
+{
+    const int G = (int)gridDim.x;
+    const int g = xcd_remap((int)blockIdx.x, G);
+    const int tiles = p.tiles_m * p.tiles_n;
+    for (int t = g; t < p.sk_dp_tiles; t += G)
+        item(t, 0, p.sk_nkt, 0);
+    const int nkt = p.sk_nkt;
+    const int64_t U = (int64_t)(tiles - p.sk_dp_tiles) * nkt;
+    const int64_t u0 = sk_start(U, G, g), u1 = sk_start(U, G, g + 1);
+    for (int64_t u = u0; u < u1;) {
+        const int ts = (int)(u / nkt);
+        const int kb = (int)(u - (int64_t)ts * nkt);
+        const int ke = (int)min((int64_t)nkt, kb + (u1 - u));
+        item(p.sk_dp_tiles + ts, kb, ke, u == u0 ? 0 : 1);
+        u += ke - kb;
+    }
+}
+
+// The K range of k-tiles [kb, ke) of the whole K.
+template <int KTB>
+__device__ __forceinline__ KRange k_range_of(const GemmArgs& p, int kb, int ke)
+{
+    constexpr int KPK = KTB / 64;
+    KRange r;
+    r.kt0 = kb;
+    r.n = ke - kb;
+    r.ka_end = min(p.KA_b, ke * KTB);
+    r.kb_end = min(p.KB, ke * KPK);
+    r.last_full = r.ka_end / KTB;
+    return r;
+}
+
 constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
 {
     int ch = MR;
@@ -626,10 +818,6 @@ constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
     return ch;
 }
 
-// s_waitcnt (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): vector-memory counter at most n, every LDS access of this
-// wave complete (lgkmcnt 0; expcnt left at its maximum).
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 
 // End of a k-tile: this wave's LDS reads of the stage are done and its share
 // of the next k-tile has landed (at most `vm` newer loads in flight); the
@@ -830,22 +1018,6 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     // wave-uniform: the LDS addresses of the DMA loads stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;     // wave row (M) and column (N)
-    int wg, tm, tn;
-    const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
-    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * TM;
-    const int n0 = tn * TN;
-    const int rows = min(TM, p.M - m0);
-    const KRange kr = k_range<KTB, MODE == MODE_SPLIT>(p, slice);
-
-    // Descriptors rebased at this tile: rows past M and 16-column blocks past
-    // ceil(N/16) fall outside and read as zero.
-    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
-                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
-    const int nb0 = n0 >> 4;
-    const int nbv = min(TN / 16, p.nblk - nb0);
-    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
-                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 
     ADma ad[A_DMA];
 #pragma unroll
@@ -861,6 +1033,23 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     i32x4 breg[ST][NR][STEPS][P];
     i32x4 af[frag_sets(ST, STEPS)][MR][P];
     acc_t acc[MR][NR];
+
+    // One work item: output tile (tm, tn) over the K range kr (split-K: its
+    // slice; stream-K: k-tiles [kb, ke) of stream-K tile sk_tile, whose
+    // partial goes to slot sk_slot unless the item covers the whole K).
+    auto run = [&](int tm, int tn, const KRange& kr, int slice, int sk_tile, int sk_slot,
+                   bool whole) __attribute__((always_inline)) {
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+    // Descriptors rebased at this tile: rows past M and 16-column blocks past
+    // ceil(N/16) fall outside and read as zero.
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
@@ -940,6 +1129,14 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
         return;
     }
+    if constexpr (MODE == MODE_SK) {
+        if (!whole &&
+            !sk_fixup<AT, MR, NR, TM, TN>(p, acc, reinterpret_cast<int*>(lds), xcd_remap((int)blockIdx.x, (int)gridDim.x),
+                                          (int)gridDim.x,
+                                          (int64_t)(p.tiles_m * p.tiles_n - p.sk_dp_tiles) * p.sk_nkt,
+                                          sk_tile, sk_slot, wave, lane))
+            return;
+    }
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
         scale_a = *p.sa;
@@ -948,6 +1145,22 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS, MODE == MODE_EPI>(
         p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
         scale_a, scale_b);
+    };
+
+    if constexpr (MODE == MODE_SK) {
+        auto item = [&](int t, int kb, int ke, int slot) __attribute__((always_inline)) {
+            int tm, tn;
+            tile_raster<DG_GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
+            run(tm, tn, k_range_of<KTB>(p, kb, ke), 0, t - p.sk_dp_tiles, slot,
+                kb == 0 && ke == p.sk_nkt);
+        };
+        sk_for_each(p, item);
+    } else {
+        int wg, tm, tn;
+        const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
+        tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
+        run(tm, tn, k_range<KTB, MODE == MODE_SPLIT>(p, slice), slice, 0, 0, true);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1005,19 +1218,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     // wave-uniform: the LDS addresses of the DMA loads stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    int wg, tm, tn;
-    const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
-    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * TM;
-    const int n0 = tn * TN;
-    const int rows = min(TM, p.M - m0);
-    const KRange kr = k_range<KTB, MODE == MODE_SPLIT>(p, slice);
-    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
-                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
-    const int nb0 = n0 >> 4;
-    const int nbv = min(TN / 16, p.nblk - nb0);
-    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
-                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 
     // A chunk w + WAVES*i: rows (1024/KTB) c ...  B chunk b = w + WAVES*i:
     // 16-column block b / KPK, 64-byte block b % KPK of the k-tile.
@@ -1042,6 +1242,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 
     i32x4 af[frag_sets(ST, STEPS)][MR][P], bf[frag_sets(ST, STEPS)][NR][P];
     acc_t acc[MR][NR];
+
+    // One work item: output tile (tm, tn) over the K range kr (split-K: its
+    // slice; stream-K: k-tiles [kb, ke) of stream-K tile sk_tile, whose
+    // partial goes to slot sk_slot unless the item covers the whole K).
+    auto run = [&](int tm, int tn, const KRange& kr, int slice, int sk_tile, int sk_slot,
+                   bool whole) __attribute__((always_inline)) {
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll
@@ -1126,6 +1341,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
         store_partial<AT, MR, NR>(p, acc, slice, m0 + (int)row0, n0 + wn * S::WCOLS, lane);
         return;
     }
+    if constexpr (MODE == MODE_SK) {
+        if (!whole &&
+            !sk_fixup<AT, MR, NR, TM, TN>(p, acc, reinterpret_cast<int*>(lds), xcd_remap((int)blockIdx.x, (int)gridDim.x),
+                                          (int)gridDim.x,
+                                          (int64_t)(p.tiles_m * p.tiles_n - p.sk_dp_tiles) * p.sk_nkt,
+                                          sk_tile, sk_slot, wave, lane))
+            return;
+    }
     float scale_a = 1.f, scale_b = 1.f;
     if constexpr (DT == DT_FP8) {
         scale_a = *p.sa;
@@ -1134,6 +1357,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     store_c_tile<DT, AT, MR, NR, S::CH, S::SROW, S::WCOLS, MODE == MODE_EPI>(
         p, acc, lds + wave * (S::CH * R * S::SROW), m0, rows, n0 + wn * S::WCOLS, (int)row0, lane,
         scale_a, scale_b);
+    };
+
+    if constexpr (MODE == MODE_SK) {
+        auto item = [&](int t, int kb, int ke, int slot) __attribute__((always_inline)) {
+            int tm, tn;
+            tile_raster<DG_GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
+            run(tm, tn, k_range_of<KTB>(p, kb, ke), 0, t - p.sk_dp_tiles, slot,
+                kb == 0 && ke == p.sk_nkt);
+        };
+        sk_for_each(p, item);
+    } else {
+        int wg, tm, tn;
+        const int slice = split_slice<MODE == MODE_SPLIT>(p, wg);
+        tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
+        run(tm, tn, k_range<KTB, MODE == MODE_SPLIT>(p, slice), slice, 0, 0, true);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -225,6 +225,25 @@ hipError_t launch_zero_c(uint16_t* C, int64_t ldc, int64_t M, int64_t N, Epilogu
                            dim3(256), args, 0, s);
 }
 
+// Zeroes n 32-bit words (the stream-K tile counters) with vector stores; a
+// kernel rather than hipMemsetAsync, so that a graph capturing the launch
+// holds no memset node.
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n)
+{
+    const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (i < n)
+        p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    void* args[] = {&p, &n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&zero_u32_kernel),
+                           dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, s);
+}
+
 // Split-K reduction.  ws holds `splits` fp32 partial planes [M][ldw]; the
 // output is C[m][n] = bf16_rne(sum over s of ws[s][m][n]) with the planes
 // added in increasing s, a fixed order, so the result does not depend on

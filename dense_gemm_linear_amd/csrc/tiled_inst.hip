@@ -1,6 +1,6 @@
 // Instantiations of the tiled kernels for one (element type, variant,
 // family), chosen by the build: DG_INST_DT (DT_BF16 / DT_FP8), DG_INST_MODE
-// (MODE_PLAIN / MODE_SPLIT / MODE_EPI) and DG_INST_FAMILY (0: the tiled
+// (MODE_PLAIN / MODE_SPLIT / MODE_EPI / MODE_SK) and DG_INST_FAMILY (0: the tiled
 // ladder, 1: the A+B and ping-pong ladders).  The build compiles this file
 // once per combination, in parallel; each defines launch_inst_<dt>_<mode>_<family>,
 // which launches rung idx of its ladders.
@@ -19,30 +19,49 @@ namespace {
 constexpr int DT = DG_INST_DT;
 constexpr int MODE = DG_INST_MODE;
 
-// split-K: tiles x slices workgroups
+// split-K: tiles x slices workgroups; stream-K: a persistent grid, one
+// workgroup per CU (a.splits carries the grid size)
 dim3 grid_of(const GemmArgs& a)
 {
+    if (MODE == MODE_SK)
+        return dim3((unsigned)a.splits);
     return dim3((unsigned)(a.tiles_m * a.tiles_n * (MODE == MODE_SPLIT ? a.splits : 1)));
 }
+
+// Stream-K instances exist for outputs of 128 x 128 to 128 x 256 only
+// (sk_rung); other rungs answer hipErrorInvalidValue.
 
 #if DG_INST_FAMILY == 0
 template <int TM, int TN, int WM, int ST, int R, int KTB>
 hipError_t go(const GemmArgs& a, hipStream_t s)
 {
-    return launch_args(&gemm_tiled_kernel<DT, TM, TN, WM, ST, R, KTB, MODE>, grid_of(a),
-                       dim3(TiledShape<TM, TN, WM, ST, R, KTB>::THREADS), a, s);
+    if constexpr (MODE == MODE_SK && !sk_rung(TM, TN)) {
+        return hipErrorInvalidValue;
+    } else {
+        return launch_args(&gemm_tiled_kernel<DT, TM, TN, WM, ST, R, KTB, MODE>, grid_of(a),
+                           dim3(TiledShape<TM, TN, WM, ST, R, KTB>::THREADS), a, s);
+    }
 }
 #else
 template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
 hipError_t go_ab(const GemmArgs& a, hipStream_t s)
 {
-    return launch_args(&gemm_ab_kernel<DT, TM, TN, WM, WN, ST, R, KTB, MODE>, grid_of(a),
-                       dim3(ABShape<TM, TN, WM, WN, ST, R, KTB>::THREADS), a, s);
+    if constexpr (MODE == MODE_SK && !sk_rung(TM, TN)) {
+        return hipErrorInvalidValue;
+    } else {
+        return launch_args(&gemm_ab_kernel<DT, TM, TN, WM, WN, ST, R, KTB, MODE>, grid_of(a),
+                           dim3(ABShape<TM, TN, WM, WN, ST, R, KTB>::THREADS), a, s);
+    }
 }
 template <int TM, int TN, int ST, int R, int KTB>
 hipError_t go_pp(const GemmArgs& a, hipStream_t s)
 {
-    return launch_args(&gemm_pp_kernel<DT, TM, TN, ST, R, KTB, MODE>, grid_of(a), dim3(512), a, s);
+    if constexpr (MODE == MODE_SK) {
+        return hipErrorInvalidValue;
+    } else {
+        return launch_args(&gemm_pp_kernel<DT, TM, TN, ST, R, KTB, MODE>, grid_of(a), dim3(512), a,
+                           s);
+    }
 }
 #endif
 }  // namespace

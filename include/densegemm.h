@@ -156,6 +156,8 @@ typedef struct {
     float tile_eff;      /* M*N / (M_pad*N_pad) for the chosen tile */
     float wq_eff;        /* tiles / (ceil(tiles / CUs) * CUs) */
     float predicted_us;  /* cost model estimate (informational) */
+    int32_t stream_k;    /* tiled / A+B rungs of 128 x 128 to 128 x 256 outputs, k_split <= 1:
+                            1 = stream-K launch (see gemm_workspace_bytes); 0 = none */
 } gemm_tile;
 
 /*
@@ -195,9 +197,25 @@ gemm_status select_tile_ws(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, in
 /*
  * gemm_workspace_bytes -- device workspace the *_ws entry points need to run
  * `tile` on M x N x K: S * M * ldw * 4 bytes for a split-K tile (S slices
- * after lowering, ldw = N rounded up to 4), 0 for any other tile.  Returns 0
- * for tile == NULL, sizes <= 0, or a tile that names no rung.  Host only.
+ * after lowering, ldw = N rounded up to 4); for a stream-K tile
+ * (tile->stream_k = 1) two fp32 partial tiles per workgroup of a grid of at
+ * most GEMM_STREAM_K_MAX_GRID workgroups plus one 32-bit counter per
+ * stream-K tile (rounded up to 256 bytes); 0 for any other tile.  Returns 0
+ * for tile == NULL, sizes <= 0, a tile that names no rung, or a stream-K
+ * tile the shape cannot use (fewer k-tile units than workgroups).  Host only.
+ *
+ * Stream-K (the TraceLens GEMM analysis page lists Stream-K among what its
+ * tile/wave-quantization model leaves out): a persistent grid of one
+ * workgroup per CU (at most GEMM_STREAM_K_MAX_GRID).  When the tiles fill
+ * two or more rounds, all but the last full round and the stray one run as
+ * whole tiles, workgroup g taking every G-th; the (tile, k-tile) units of the
+ * remaining tiles are cut into G equal contiguous ranges.  A tile cut
+ * between workgroups is finished by the last of them to arrive, which adds
+ * the fp32 partials in k order -- results are bitwise repeatable -- and
+ * applies the epilogue.  No workgroup waits on another.  The fused epilogue
+ * (gemm_epilogue) is not offered with stream-K.
  */
+#define GEMM_STREAM_K_MAX_GRID 256
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
                             const gemm_tile* tile);
 
@@ -404,6 +422,14 @@ gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, ui
  * its cost, at least about 6 us, is below 40 % of one round's, what such a
  * stray round measured on MI355X.  Both launches are enqueued on the caller's
  * stream, in that order; the outputs they write are disjoint.
+ *
+ * When the chosen one-pass tile (a stream-K rung) fills less than one round
+ * of the CUs and the workspace holds its stream-K partials, *first is its
+ * stream-K form (stream_k = 1) if the model prices that below 95 % of the
+ * one-pass launch: the one-pass time scaled by tiles / CUs and by 1.45 (a
+ * stream-K unit measured that much slower than a one-pass one), plus about
+ * 20 us for the fix-up of the cut tiles.  The launch with a fused epilogue
+ * (gemm_*_ex with any part set) keeps the one-pass form.
  *
  * GEMM_ERR_INVALID_VALUE for a NULL output, M, N or K <= 0, num_cus <= 0 or
  * an unknown dtype.

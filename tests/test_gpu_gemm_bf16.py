@@ -70,7 +70,7 @@ def test_small_shapes_full(shape):
     check_exact(C, oracle_full("bf16", A, B), f"{shape} smallint")
 
 
-BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selector
+BENCH_WORKSPACE = 128 << 20   # the split-K / stream-K workspace bench.py hands the library
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -78,14 +78,15 @@ BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selecto
 def test_workload_shapes_every_element(name, smallint):
     """Every output element of the full workload against the oracle's whole
     product (computed once per case on the host's threads): on the library's
-    plan without a workspace, and, where it differs, on the tile bench.py
-    times with its 64 MiB workspace (the workspace NaN-poisoned first)."""
+    plan without a workspace, and, where it differs, on the plan bench.py
+    times with its 128 MiB workspace (split-K or stream-K; the workspace
+    NaN-poisoned first)."""
     M, N, K, da, sa, db, sb, cfg = WORKLOADS[name]
     A, B = inputs(M, N, K, da, sa, db, sb, cfg, smallint)
     print(f"[gemm_bf16 {name} {M}x{N}x{K} smallint={smallint}: oracle product]", flush=True)
     ref = oracle_full("bf16", A, B)
-    runs = [(0, dg.select_tile(M, N, K, "bf16"))]
-    t_ws = dg.select_tile(M, N, K, "bf16", workspace_bytes=BENCH_WORKSPACE)
+    runs = [(0, dg.plan(M, N, K, "bf16", 256, 0)[0])]
+    t_ws = dg.plan(M, N, K, "bf16", 256, BENCH_WORKSPACE)[0]
     if t_ws.name != runs[0][1].name:
         runs.append((BENCH_WORKSPACE, t_ws))
     for ws, tile in runs:

@@ -36,23 +36,23 @@ def test_small_shapes_full(shape):
         check_exact(C, oracle_full("fp8", A, B, s1, s2), f"{shape} smallint scales {s1},{s2}")
 
 
-BENCH_WORKSPACE = 64 << 20    # the split-K workspace bench.py hands the selector
+BENCH_WORKSPACE = 128 << 20   # the split-K / stream-K workspace bench.py hands the library
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("smallint", [False, True], ids=["general", "smallint"])
 def test_workload_shapes_every_element(name, smallint):
     """Every output element against the oracle's whole product, on the
-    library's plan without a workspace and, where it differs, on the tile
-    bench.py times with its 64 MiB workspace."""
+    library's plan without a workspace and, where it differs, on the plan
+    bench.py times with its 128 MiB workspace."""
     M, N, K, cfg = WORKLOADS[name]
     A, B, sa, sb = datagen.make_e4m3_pair(M, N, K, config=cfg, smallint=smallint)
     if smallint:
         sa, sb = 2.0 ** -3, 2.0 ** 2
     print(f"[gemm_fp8 {name} {M}x{N}x{K} smallint={smallint}: oracle product]", flush=True)
     ref = oracle_full("fp8", A, B, sa, sb)
-    runs = [(0, dg.select_tile(M, N, K, "fp8"))]
-    t_ws = dg.select_tile(M, N, K, "fp8", workspace_bytes=BENCH_WORKSPACE)
+    runs = [(0, dg.plan(M, N, K, "fp8", 256, 0)[0])]
+    t_ws = dg.plan(M, N, K, "fp8", 256, BENCH_WORKSPACE)[0]
     if t_ws.name != runs[0][1].name:
         runs.append((BENCH_WORKSPACE, t_ws))
     for ws, tile in runs:
