@@ -18,7 +18,11 @@ Measurement:
   * `sustained`: the same graph replayed back to back for --soak seconds,
     each replay timed by its own events, the shader clock and board power
     sampled inside the timed half; `roofline.frac_at_sustained_clock` rates
-    that figure against the MFMA peak at the sampled clock.
+    that figure against the MFMA peak at the sampled clock.  With --soak > 0
+    the W warm-ups and the K timed calls run once from idle (reported as
+    `sustained.from_idle_ms_per_step`: the clock is still ramping up) and
+    again right after the sustained replay; `value` is that second run, the
+    board's loaded power state.
   * The K calls rotate over enough copies of (A, Bs, C) to exceed twice the
     256 MB Infinity Cache, so every call reads its operands from HBM.
   * `roofline`: algorithmic flops (2MNK, "GEMM Optimization Guide" page,
@@ -314,17 +318,30 @@ def run_timed(name: str, steps: int, warmup: int, copies: int | None = None, per
         # busy, and the K timed calls follow back to back.  (A spin kernel
         # in their place let the shader clock sink before the timed calls:
         # an isolated launch after an idle gap ran at 1.2-1.4 GHz.)
-        wall0 = time.perf_counter()
-        for i in range(warmup):
-            call(i)
-        t0.record()
-        g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        sustained = sustained_with_clock(g, steps, soak) if soak > 0 else None
+        def timed_replay():
+            wall0 = time.perf_counter()
+            for i in range(warmup):
+                call(i)
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1), time.perf_counter() - wall0
+
+        total_ms, wall = timed_replay()
+        sustained = None
+        if soak > 0:
+            # The board starts from idle: its shader clock ramps up over the
+            # first milliseconds, so K steps timed right away mix the ramp
+            # with the loaded state.  After the sustained replay (about
+            # `soak` seconds, timed by its own events) the W warm-ups and the
+            # K timed steps are run once more: the reported K-step time is
+            # the loaded power state's, and the first one is kept as context.
+            sustained = sustained_with_clock(g, steps, soak)
+            sustained["from_idle_ms_per_step"] = round(total_ms / steps, 5)
+            total_ms, wall = timed_replay()
         del g
-        return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "kernel_us": [], "tile": tile,
+        return {"total_ms": total_ms, "wall_s": wall, "kernel_us": [], "tile": tile,
                 "shuffle_us": shuffle_us, "copies": copies, "sustained": sustained}
     for i in range(warmup):
         call(i)
@@ -722,7 +739,9 @@ def main(argv=None):
                      "algorithmic_bytes": alg_bytes(M, N, K, dt),
                      "kernel_us_avg": round(kern_avg, 3),
                      "timing": ("HIP events around the K back-to-back calls on the kernels' stream"
-                                + ("" if args.eager else ", replayed from one HIP graph"))},
+                                + ("" if args.eager else ", replayed from one HIP graph")
+                                + (", right after the sustained replay (board at its loaded "
+                                   "power state)" if r["sustained"] else ""))},
         "shuffle_b_us": round(r["shuffle_us"], 2),
         # the preshuffle runs once per weight: the number of GEMM calls on the
         # same weight after which its cost is at most 1 % of the total
