@@ -583,6 +583,95 @@ def run_graph(name: str, reps: int, copies: int):
     return time_graph(gemm_call(name, sets, scales), reps), shuffle_us
 
 
+def read_floor_us(nbytes: int, reps: int = 60) -> float:
+    """Per-launch time of the library's streaming-read probe over nbytes of
+    device memory, timed as the decode kernels are (a HIP graph of R launches
+    over enough buffer copies to exceed twice the Infinity Cache): the floor
+    under any kernel that reads those bytes once from HBM."""
+    import torch
+    import dense_gemm_linear_amd as dg
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = cold_copies(nbytes)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i & 0xFF) for i in range(copies)]
+    out = torch.empty(dg.READ_PROBE_SLOTS, dtype=torch.int32, device="cuda")
+    us = time_graph(lambda i: dg.read_probe(bufs[i % copies], out=out), reps, trials=3)
+    del bufs
+    return us
+
+
+def read_floor_report(names) -> int:
+    """One JSON line per workload: the bytes it must read from HBM (its
+    algorithmic bytes less C) and the streaming-read probe's time for them."""
+    for name in names:
+        M, N, K, dt = WORKLOADS[name][:4]
+        e = 2 if dt == "bf16" else 1
+        nbytes = (M + N) * K * e
+        us = read_floor_us(nbytes)
+        print(json.dumps({"read_floor": name, "bytes": nbytes, "probe_us": round(us, 3),
+                          "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
+    return 0
+
+
+def hipblaslt_same_box(name: str, steps: int, warmup: int, soak: float):
+    """The same workload through torch's matmul (hipBLASLt on ROCm; fp8 via
+    torch._scaled_mm with unit scales), timed exactly as the library's call:
+    W warm-ups ahead of a graph replay of K calls over the same number of
+    cold operand copies, then a sustained replay.  Context for the library's
+    figure on the same box and in the same power state, not a baseline from
+    the pages."""
+    import torch
+    M, N, K, dt = WORKLOADS[name][:4]
+    e = 2 if dt == "bf16" else 1
+    copies = cold_copies(alg_bytes(M, N, K, dt))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    sets = []
+    for _ in range(copies):
+        a = torch.randn(M, K, device="cuda", generator=g)
+        b = torch.randn(N, K, device="cuda", generator=g) * 0.02
+        if dt == "bf16":
+            sets.append((a.bfloat16(), b.bfloat16(), torch.empty(M, N, dtype=torch.bfloat16, device="cuda")))
+        else:
+            sets.append((a.to(torch.float8_e4m3fn), (b * 50).to(torch.float8_e4m3fn),
+                         torch.empty(M, N, dtype=torch.bfloat16, device="cuda")))
+    one = torch.ones((), device="cuda")
+
+    def call(i):
+        a, b, c = sets[i % copies]
+        if dt == "bf16":
+            torch.mm(a, b.t(), out=c)
+        else:
+            torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16, out=c)
+
+    call(0)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gr, stream=side):
+            for i in range(steps):
+                call(warmup + i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    sus = sustained_with_clock(gr, steps, soak) if soak > 0 else None
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        call(i)
+    t0.record()
+    gr.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    del gr
+    out = {"us_per_call": round(us, 3), "TFLOPs": round(flops(M, N, K) / (us * 1e-6) / 1e12, 2)}
+    if sus:
+        out["sustained_us_per_call"] = sus["per_call_us"]
+        out["sustained_gfx_mhz_mean"] = sus["gfx_mhz_mean"]
+    out["timing"] = ("torch.mm / torch._scaled_mm (hipBLASLt), K calls replayed from one HIP graph "
+                     "after the sustained replay, same operand rotation as the library's")
+    return out
+
+
 # ------------------------------------------------------------ CPU oracle
 def cpu_baseline(name: str, budget_s: float = 20.0):
     """The oracle on whole rows of C of the same workload, scaled to TFLOP/s."""
@@ -642,6 +731,11 @@ def main(argv=None):
                     help="time transpose_2d and shuffle_b_t on the GPT-3-XL backward operands")
     ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
                     help="split-K workspace handed to the library (0: no split-K)")
+    ap.add_argument("--read-floor", nargs="*", default=None, metavar="WORKLOAD",
+                    help="time the streaming-read probe over each workload's A and B bytes "
+                         "(default: the HBM-bound workloads), one JSON line each, and exit")
+    ap.add_argument("--no-hipblaslt", action="store_true",
+                    help="skip the same-box hipBLASLt (torch.mm) comparison")
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
@@ -667,6 +761,9 @@ def main(argv=None):
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
         return sweep(name, args.steps, args.warmup, args.workspace_mib)
+    if args.read_floor is not None:
+        return read_floor_report(args.read_floor or
+                                 [n for n in WORKLOADS if bound_of(*WORKLOADS[n][:4]) == "hbm"])
     if args.backward_prep:
         return backward_prep(args.steps)
     if args.epilogue is not None:
@@ -690,6 +787,9 @@ def main(argv=None):
             "us_hot_mall": round(us_hot, 3), "GBps_hot_mall": round(gb / (us_hot * 1e-6) / 1e9, 1),
             "shuffle_b_us": round(dshuf, 2),
             "shuffle_b_amortized_below_1pct_after_calls": math.ceil(99.0 * dshuf / us_cold),
+            # the library's streaming-read probe over the same bytes, timed
+            # the same way: what any kernel reading them once would need
+            "read_floor_us": round(read_floor_us((dM + dN) * dK * 2), 3),
             "timing": "hipGraph of 60 launches, before the headline's steps; cold = 6 rotated "
                       "operand copies (541 MB)",
         }
@@ -771,6 +871,8 @@ def main(argv=None):
             # against the MFMA peak at the clock sampled during that interval
             out["roofline"]["frac_at_sustained_clock"] = round(
                 sus["value"] / (peak * sus["gfx_mhz_mean"] / 2400.0), 4)
+    if not args.no_hipblaslt and args.tile is None:
+        out["hipblaslt_same_box"] = hipblaslt_same_box(name, args.steps, args.warmup, args.soak)
     if secondary is not None:
         out["secondary"] = secondary
     if not args.no_cpu:

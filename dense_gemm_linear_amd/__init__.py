@@ -33,6 +33,7 @@ GEMM_FP8_E4M3 = 1
 
 # bytes of the library's own split-K scratch behind gemm_bf16_noalloc
 NOALLOC_SCRATCH_BYTES = 32 << 20
+READ_PROBE_SLOTS = 32768
 
 GEMM_KERNEL_TILED = 0
 GEMM_KERNEL_SKINNY = 1
@@ -42,7 +43,7 @@ GEMM_KERNEL_TILED_PP = 3
 EXPORTS = ("select_tile", "shuffle_b_bytes", "shuffle_b", "gemm_bf16", "gemm_fp8_scaled",
            "gemm_tile_check", "gemm_status_string", "select_tile_ws", "gemm_workspace_bytes",
            "gemm_bf16_ws", "gemm_fp8_scaled_ws", "gemm_bf16_ex", "gemm_fp8_scaled_ex", "shuffle_b_t",
-           "transpose_2d", "gemm_plan", "gemm_bf16_noalloc")
+           "transpose_2d", "gemm_plan", "gemm_bf16_noalloc", "gemm_read_probe")
 
 # gemm_activation
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_SILU, GEMM_ACT_GELU_ERF, GEMM_ACT_GELU_TANH = 0, 1, 2, 3, 4
@@ -252,6 +253,8 @@ def _load_lib():
     lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
+    lib.gemm_read_probe.argtypes = [P, ctypes.c_uint64, P, P]
+    lib.gemm_read_probe.restype = ctypes.c_int
     lib.gemm_status_string.argtypes = [ctypes.c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
     return lib
@@ -353,6 +356,28 @@ def shuffle_b(B, dtype=None, out=None):
     st = lib.shuffle_b(B.data_ptr(), B.stride(0), out.data_ptr(), N, K, code, _stream_ptr(B))
     if st != GEMM_OK:
         raise GemmError("shuffle_b", st)
+    return out
+
+
+def read_probe(buf, out=None):
+    """Read every byte of the contiguous device tensor `buf` once with the
+    library's streaming-read probe (a measurement aid: the time floor of a
+    kernel that reads the same bytes).  Returns `out`, READ_PROBE_SLOTS
+    uint32 values (as int32) whose XOR is the XOR of all 32-bit words of
+    buf."""
+    torch = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(READ_PROBE_SLOTS, dtype=torch.int32, device=buf.device)
+    elif (not out.is_cuda or out.dtype != torch.int32 or out.numel() < READ_PROBE_SLOTS
+          or out.device != buf.device):
+        raise ValueError(f"out must be an int32 device tensor of {READ_PROBE_SLOTS} elements "
+                         "on buf's device")
+    st = lib.gemm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), _stream_ptr(buf))
+    if st != GEMM_OK:
+        raise GemmError("gemm_read_probe", st)
     return out
 
 

@@ -562,6 +562,19 @@ gemm_status shuffle_b(const void* B, int64_t ldb, void* Bs, int64_t N, int64_t K
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
+gemm_status gemm_read_probe(const void* buf, uint64_t bytes, uint32_t* out, void* stream)
+{
+    if (!buf || !out || bytes == 0 || bytes % 16 != 0 || bytes > (1ull << 40) || !dg::aligned16(buf))
+        return GEMM_ERR_INVALID_VALUE;
+    int cus = 0;
+    gemm_status st = dg::device_info(&cus);
+    if (st != GEMM_OK)
+        return st;
+    const hipError_t err = dg::launch_read_probe(buf, (int64_t)bytes, out, GEMM_READ_PROBE_SLOTS / 16,
+                                                 reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 gemm_status shuffle_b_t(const void* Bt, int64_t ldbt, void* Bs, int64_t N, int64_t K,
                         gemm_dtype dtype, void* stream)
 {

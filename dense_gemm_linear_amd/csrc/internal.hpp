@@ -148,6 +148,7 @@ int rung_ktb(int kernel, int idx);
 void choose_tile(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
                  gemm_tile* out);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, int grid, hipStream_t s);
 // Stream-K plan of a resolved tiled / A+B rung (see gemm_workspace_bytes):
 // grid G, whole tiles [0, dp_tiles), k-tiles per tile nkt (the rung's k-tile
 // size), the partial slots' bytes and the whole workspace.  ok = false when

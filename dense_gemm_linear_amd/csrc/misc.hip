@@ -235,6 +235,68 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n)
         p[i] = 0u;
 }
 
+// Streaming-read probe (a measurement aid, not part of any GEMM): workgroup
+// g XORs the 32-bit words of its contiguous share of the buffer, every lane
+// keeping D 16-byte non-temporal loads in flight (the access pattern of the
+// skinny kernel's weight stream, without its arithmetic), and each wave
+// writes its XOR to its own slot.  No workgroup barrier and no LDS: a wave
+// that is done leaves at once and frees its slot for the next workgroup's
+// waves (measured on MI355X, 90 MB: a barrier before one store per
+// workgroup cost 2.7 us, a shuffle reduction through LDS 2.3 us).  Its time is the floor under a kernel that must read the same
+// bytes once.
+template <int D>
+__global__ __launch_bounds__(1024) void read_probe_kernel(const i32x4* buf, int64_t n16,
+                                                         int64_t per16, uint32_t* out)
+{
+    const int64_t base = (int64_t)blockIdx.x * per16;
+    const int64_t end = base + per16 < n16 ? base + per16 : n16;
+    const int nt = (int)blockDim.x;
+    i32x4 acc = {0, 0, 0, 0};
+    for (int64_t i = base + threadIdx.x; i < end; i += (int64_t)nt * D) {
+        i32x4 v[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t j = i + (int64_t)d * nt;
+            v[d] = j < end ? __builtin_nontemporal_load(buf + j) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            acc ^= v[d];
+    }
+    // XOR over the wave: DPP moves within each row of 16 lanes (quad
+    // permutations, then the half-row and row mirrors), then the four row
+    // results read into scalars -- no LDS round trips on the way out
+    int x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    x ^= __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x ^= __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    x ^= __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    x ^= __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);   // row_mirror
+    x = __builtin_amdgcn_readlane(x, 0) ^ __builtin_amdgcn_readlane(x, 16) ^
+        __builtin_amdgcn_readlane(x, 32) ^ __builtin_amdgcn_readlane(x, 48);
+    // 16 slots per workgroup whatever its size: wave w owns 16 / waves of
+    // them, its XOR in the first and zeros in the others
+    const int per = 16 / (nt / 64);
+    const int lane = (int)threadIdx.x & 63;
+    if (lane < per)
+        out[(int64_t)blockIdx.x * 16 + (threadIdx.x >> 6) * per + lane] = lane == 0 ? (uint32_t)x : 0u;
+}
+
+// grid workgroups; out holds grid * 16 slots, all of them written.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, int grid, hipStream_t s)
+{
+    int64_t n16 = bytes / 16;
+    int64_t per16 = (n16 + grid - 1) / grid;
+    const i32x4* b = static_cast<const i32x4*>(buf);
+    void* args[] = {&b, &n16, &per16, &out};
+    // measured on MI355X: 256 threads with 4 loads each in flight up to a
+    // few tens of MB, 1024 threads with 8 each beyond
+    if (bytes >= (64ll << 20))
+        return hipLaunchKernel(reinterpret_cast<const void*>(&read_probe_kernel<8>), dim3((unsigned)grid),
+                               dim3(1024), args, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&read_probe_kernel<4>), dim3((unsigned)grid),
+                           dim3(256), args, 0, s);
+}
+
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s)
 {
     if (n <= 0)

@@ -446,6 +446,26 @@ gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t
  */
 gemm_status gemm_tile_check(const gemm_tile* tile, int64_t M, gemm_dtype dtype);
 
+/*
+ * gemm_read_probe -- a measurement aid, not a step of the GEMM: reads the
+ * `bytes` bytes of device memory at `buf` once, the way the skinny kernel
+ * streams a decode weight (16-byte non-temporal loads, several in flight per
+ * lane, no arithmetic but an XOR), so that its duration is the floor under
+ * any kernel that reads those bytes on this device (the HBM-bound rows of
+ * the "TraceLens GEMM analysis" page, "Prefill versus decode": a decode GEMM
+ * is a weight read).  Every wave writes the XOR of the 32-bit words it read
+ * to a slot of its own and zeros to the slots no wave owns, so the XOR of
+ * all GEMM_READ_PROBE_SLOTS values of out is the XOR of every word of the
+ * buffer.
+ *   buf    device memory, 16-byte aligned; not written
+ *   bytes  a positive multiple of 16, at most 2^40
+ *   out    device memory for GEMM_READ_PROBE_SLOTS uint32 values (written)
+ * GEMM_ERR_INVALID_VALUE for a null pointer, a misaligned buf or a bad size;
+ * GEMM_ERR_HIP if the launch fails.  Asynchronous on `stream`.
+ */
+#define GEMM_READ_PROBE_SLOTS 32768
+gemm_status gemm_read_probe(const void* buf, uint64_t bytes, uint32_t* out, void* stream);
+
 /* Static, human-readable name of a status code ("GEMM_OK", ...). */
 const char* gemm_status_string(gemm_status status);
 

@@ -418,3 +418,18 @@ def test_binding_rejects_wrong_operand_types_before_any_launch():
         dg.gemm_fp8_scaled(a_f8, bs, 16, 1.0, one)      # a number, not a tensor
     with pytest.raises(ValueError, match="device"):
         dg.gemm_bf16(a_bf, bs, 16)                      # host A
+
+
+def test_read_probe_rejects_bad_arguments_before_any_launch():
+    """Null pointers, a misaligned buffer and sizes that are zero or not a
+    multiple of 16 bytes are refused on the host (the device is never
+    reached: this runs without one)."""
+    E = dg.GEMM_ERR_INVALID_VALUE
+    f = dg.lib.gemm_read_probe
+    P = 1 << 20
+    assert f(None, 64, P, None) == E
+    assert f(P, 64, None, None) == E
+    assert f(P + 8, 64, P, None) == E
+    assert f(P, 0, P, None) == E
+    assert f(P, 72, P, None) == E
+    assert f(P, (1 << 40) + 16, P, None) == E
