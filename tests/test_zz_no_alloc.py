@@ -4,6 +4,7 @@ ABI: two calls in a row, the second on a smaller input, each bitwise equal
 to the workspace entry point and, on small-integer inputs, to the oracle.
 A forced split-K tile whose partials exceed the scratch is refused before
 any launch."""
+import gc
 import numpy as np
 import pytest
 import torch
@@ -26,10 +27,18 @@ def _both(M, N, K, cfg, tile=None):
     ws = torch.full((SCRATCH,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN-poisoned
     dg.gemm_bf16(Ad, Bs, N, out=c_ws, tile=tile, workspace=ws)
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
-    dg.gemm_bf16_noalloc(Ad, Bs, N, out=c_na, tile=tile)
-    torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    # torch's allocator count must not change across the call; the garbage
+    # collector is kept from freeing earlier tests' tensors meanwhile
+    gc.collect()
+    gc.disable()
+    try:
+        before = torch.cuda.memory_allocated()
+        dg.gemm_bf16_noalloc(Ad, Bs, N, out=c_na, tile=tile)
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
+    assert after == before
     return A, B, host_bits(c_ws), host_bits(c_na)
 
 
