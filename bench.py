@@ -612,6 +612,15 @@ def read_floor_report(names) -> int:
     return 0
 
 
+def _safe(f):
+    """f(), or the error's text: for context figures that must not cost the
+    bench line if they fail."""
+    try:
+        return f()
+    except Exception as e:  # noqa: BLE001
+        return f"error: {type(e).__name__}: {e}"[:200]
+
+
 def hipblaslt_same_box(name: str, steps: int, warmup: int, soak: float):
     """The same workload through torch's matmul (hipBLASLt on ROCm; fp8 via
     torch._scaled_mm with unit scales), timed exactly as the library's call:
@@ -789,7 +798,7 @@ def main(argv=None):
             "shuffle_b_amortized_below_1pct_after_calls": math.ceil(99.0 * dshuf / us_cold),
             # the library's streaming-read probe over the same bytes, timed
             # the same way: what any kernel reading them once would need
-            "read_floor_us": round(read_floor_us((dM + dN) * dK * 2), 3),
+            "read_floor_us": _safe(lambda: round(read_floor_us((dM + dN) * dK * 2), 3)),
             "timing": "hipGraph of 60 launches, before the headline's steps; cold = 6 rotated "
                       "operand copies (541 MB)",
         }
@@ -872,7 +881,10 @@ def main(argv=None):
             out["roofline"]["frac_at_sustained_clock"] = round(
                 sus["value"] / (peak * sus["gfx_mhz_mean"] / 2400.0), 4)
     if not args.no_hipblaslt and args.tile is None:
-        out["hipblaslt_same_box"] = hipblaslt_same_box(name, args.steps, args.warmup, args.soak)
+        try:
+            out["hipblaslt_same_box"] = hipblaslt_same_box(name, args.steps, args.warmup, args.soak)
+        except Exception as e:  # noqa: BLE001 - context only: never lose the bench line for it
+            out["hipblaslt_same_box"] = {"error": f"{type(e).__name__}: {e}"[:200]}
     if secondary is not None:
         out["secondary"] = secondary
     if not args.no_cpu:
