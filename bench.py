@@ -740,6 +740,9 @@ def main(argv=None):
                     help="time transpose_2d and shuffle_b_t on the GPT-3-XL backward operands")
     ap.add_argument("--workspace-mib", type=int, default=WORKSPACE_MIB,
                     help="split-K workspace handed to the library (0: no split-K)")
+    ap.add_argument("--sweep-soak", type=float, default=0.0, metavar="SECONDS",
+                    help="with --sweep: time every tile in the loaded power state, its graph "
+                         "replayed for SECONDS")
     ap.add_argument("--read-floor", nargs="*", default=None, metavar="WORKLOAD",
                     help="time the streaming-read probe over each workload's A and B bytes "
                          "(default: the HBM-bound workloads), one JSON line each, and exit")
@@ -769,7 +772,7 @@ def main(argv=None):
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
-        return sweep(name, args.steps, args.warmup, args.workspace_mib)
+        return sweep(name, args.steps, args.warmup, args.workspace_mib, args.sweep_soak)
     if args.read_floor is not None:
         return read_floor_report(args.read_floor or
                                  [n for n in WORKLOADS if bound_of(*WORKLOADS[n][:4]) == "hbm"])
@@ -926,10 +929,35 @@ def regret_report(path: str, ws_mib: int = WORKSPACE_MIB) -> int:
     return 0
 
 
-def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> int:
+def sustained_graph_us(call, steps: int, seconds: float) -> float:
+    """Per-call time of `call` in the loaded power state: `steps` calls
+    captured in one HIP graph, replayed back to back for `seconds`, the
+    median of the second half (sustained_with_clock)."""
+    import torch
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                call(3 + i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    us = sustained_with_clock(g, steps, seconds)["per_call_us"]
+    del g
+    return us
+
+
+def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak: float = 0.0) -> int:
     """Every feasible tile on one workload, graph-timed (`steps` launches per
     graph, median of 3 replays); prints a line per tile and a summary with
-    the selector's regret (its pick's time over the best time)."""
+    the selector's regret (its pick's time over the best time).  soak > 0:
+    each tile is timed instead in the loaded power state, its graph replayed
+    for `soak` seconds (for long compute-bound workloads, whose ranking
+    under the board's power limit can differ from a short burst's)."""
     import torch
     import dense_gemm_linear_amd as dg
     M, N, K, dt = WORKLOADS[name][:4]
@@ -962,9 +990,11 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB) -> in
     sets, scales, _ = setup
     res = {}
     for t in tiles:
-        us = time_graph(gemm_call(name, sets, scales, t, workspace), reps=steps, trials=3)
+        call = gemm_call(name, sets, scales, t, workspace)
+        us = sustained_graph_us(call, steps, soak) if soak > 0 else time_graph(call, reps=steps, trials=3)
         res[t.name] = us
         print(json.dumps({"sweep": name, "tile": t.name, "kernel_us_median": round(us, 3),
+                          **({"timing": f"sustained {soak} s"} if soak > 0 else {}),
                           "tflops": round(flops(M, N, K) / (us * 1e-6) / 1e12, 1),
                           "gbps": round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)}), flush=True)
     pick = dg.plan(M, N, K, dt, CUS, ws_bytes)[0]

@@ -167,7 +167,7 @@ AB_LADDER = [(256, 128, 4, 3, 16, 128), (128, 256, 4, 3, 16, 128), (128, 128, 4,
              (256, 256, 8, 2, 32, 128), (256, 256, 4, 2, 32, 128), (256, 128, 8, 3, 32, 128),
              (256, 128, 4, 3, 32, 128), (128, 256, 4, 3, 32, 128), (128, 128, 4, 3, 32, 128),
              (256, 256, 8, 4, 32, 64), (256, 256, 4, 4, 32, 64),
-             (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64)]
+             (256, 128, 8, 6, 32, 64), (128, 256, 4, 6, 32, 64), (256, 256, 8, 4, 16, 64)]
 # (tile_m, tile_n, waves splitting K)
 # (tile_m, tile_n, stages, atom, k-tile bytes)
 PP_LADDER = [(256, 256, 4, 32, 64)]
@@ -178,8 +178,10 @@ SKINNY_LADDER = [(m, n, 4) for m in (16, 32, 48, 64) for n in (16, 32, 64)] + \
 def ladder_tiles(dtype="bf16"):
     """Every tiled and A+B rung, fully specified for an element type."""
     e = 2 if _dtype_code(dtype) == GEMM_BF16 else 1
-    return [tiled(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in TILED_LADDER] + \
-        [tiled_ab(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in AB_LADDER] + \
+    # e4m3 16 x 16 atoms take 128 K bytes per MFMA: 128-byte k-tiles only
+    fits = lambda a, kb: not (e == 1 and a == 16 and kb != 128)  # noqa: E731
+    return [tiled(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in TILED_LADDER if fits(a, kb)] + \
+        [tiled_ab(m, n, w, a, st, kb // e) for m, n, w, st, a, kb in AB_LADDER if fits(a, kb)] + \
         [tiled_pp(m, n, a, st, kb // e) for m, n, st, a, kb in PP_LADDER]
 
 

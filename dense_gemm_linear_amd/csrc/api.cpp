@@ -120,6 +120,9 @@ bool resolve_tile(const gemm_tile& t, int64_t M, int e, int* idx)
         *idx = tiled_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
     else if (t.kernel == GEMM_KERNEL_TILED_AB)
         *idx = ab_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
+    if ((t.kernel == GEMM_KERNEL_TILED || t.kernel == GEMM_KERNEL_TILED_AB) && *idx >= 0 &&
+        !atom_fits_rt(e == 2 ? DT_BF16 : DT_FP8, atom, rung_ktb(t.kernel, *idx)))
+        *idx = -1;
     else if (t.kernel == GEMM_KERNEL_TILED_PP)
         *idx = pp_rung(t.tile_m, t.tile_n, t.waves, atom, t.lds_stages, ktb);
     else if (t.kernel == GEMM_KERNEL_SKINNY)

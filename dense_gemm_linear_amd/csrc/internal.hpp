@@ -34,7 +34,8 @@ namespace dg {
     X(256, 128, 2, 4, 3, 32, 128) X(256, 128, 2, 2, 3, 32, 128)                            \
     X(128, 256, 2, 2, 3, 32, 128) X(128, 128, 2, 2, 3, 32, 128)                            \
     X(256, 256, 2, 4, 4, 32, 64) X(256, 256, 2, 2, 4, 32, 64)                            \
-    X(256, 128, 2, 4, 6, 32, 64) X(128, 256, 2, 2, 6, 32, 64)
+    X(256, 128, 2, 4, 6, 32, 64) X(128, 256, 2, 2, 6, 32, 64)                            \
+    X(256, 256, 2, 4, 4, 16, 64)
 
 // Ping-pong A+B ladder (8 waves, 2 groups x 4): (tile_m, tile_n, stages, atom,
 // k-tile bytes).  Narrower tiles halve each wave's MFMAs per k-tile while its
@@ -159,6 +160,18 @@ struct SkPlan {
     int64_t tiles, slot_bytes, ws_bytes;
 };
 // stream-K instances: outputs of 128 x 128 to 128 x 256
+// An atom whose MFMA takes more K bytes than a k-tile holds has no instance
+// (the e4m3 16 x 16 x 128 MFMA needs 128-byte k-tiles).
+template <int DT, int R, int KTB>
+constexpr bool atom_fits()
+{
+    return !(DT == DT_FP8 && R == 16 && KTB != 128);
+}
+constexpr bool atom_fits_rt(int dt, int atom, int ktb)
+{
+    return !(dt == DT_FP8 && atom == 16 && ktb != 128);
+}
+
 constexpr bool sk_rung(int tm, int tn) { return tm * tn >= 128 * 128 && tm * tn <= 128 * 256; }
 SkPlan sk_plan(int kernel, int idx, int tm, int tn, int64_t M, int64_t N, int64_t K, int e, int grid);
 hipError_t launch_splitk_reduce(const float* ws, int splits, int M, int N, int ldw, uint16_t* C,

@@ -185,6 +185,8 @@ bool price_ab(int64_t M, int64_t N, int64_t K, int dt, int cus, int idx, const A
               const Chip& c, Cand& out)
 {
     const int waves = r.wm * r.wn;
+    if (dt == GEMM_FP8_E4M3 && r.atom == 16 && r.ktb != 128)
+        return false;
     const int lds = ab_lds_bytes(idx);
     if (lds < 0 || lds > c.lds_per_cu)
         return false;

@@ -29,13 +29,14 @@ dim3 grid_of(const GemmArgs& a)
 }
 
 // Stream-K instances exist for outputs of 128 x 128 to 128 x 256 only
-// (sk_rung); other rungs answer hipErrorInvalidValue.
+// (sk_rung), and e4m3 16 x 16 atoms (128 K bytes per MFMA) only with
+// 128-byte k-tiles (atom_fits); other rungs answer hipErrorInvalidValue.
 
 #if DG_INST_FAMILY == 0
 template <int TM, int TN, int WM, int ST, int R, int KTB>
 hipError_t go(const GemmArgs& a, hipStream_t s)
 {
-    if constexpr (MODE == MODE_SK && !sk_rung(TM, TN)) {
+    if constexpr ((MODE == MODE_SK && !sk_rung(TM, TN)) || !atom_fits<DT, R, KTB>()) {
         return hipErrorInvalidValue;
     } else {
         return launch_args(&gemm_tiled_kernel<DT, TM, TN, WM, ST, R, KTB, MODE>, grid_of(a),
@@ -46,7 +47,7 @@ hipError_t go(const GemmArgs& a, hipStream_t s)
 template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
 hipError_t go_ab(const GemmArgs& a, hipStream_t s)
 {
-    if constexpr (MODE == MODE_SK && !sk_rung(TM, TN)) {
+    if constexpr ((MODE == MODE_SK && !sk_rung(TM, TN)) || !atom_fits<DT, R, KTB>()) {
         return hipErrorInvalidValue;
     } else {
         return launch_args(&gemm_ab_kernel<DT, TM, TN, WM, WN, ST, R, KTB, MODE>, grid_of(a),

@@ -82,7 +82,8 @@ typedef enum {
  *     32 x 32, 128-byte k-tiles: 256x256 (8 or 4 waves, 2 stages), 256x128
  *       (8 or 4 waves, 3 stages), 128x256 and 128x128 (4 waves, 3 stages);
  *     32 x 32, 64-byte k-tiles: 256x256 with 8 or 4 waves and 4 stages, 256x128 with 8 waves and 6 stages, 128x256 with
- *       4 waves and 6 stages.
+ *       4 waves and 6 stages;
+ *     16 x 16, 64-byte k-tiles (bf16 only): 256x256 with 8 waves and 4 stages.
  *   tiled_pp (8 waves; group g owns tile rows [g tile_m/2, (g+1) tile_m/2)):
  *     32 x 32: 256x256 with 4 stages of 64-byte k-tiles.
  *   16 x 16 e4m3 atoms need 128-byte k-tiles.

@@ -96,7 +96,11 @@ def test_every_python_rung_is_a_library_rung(dt):
     assert dg.tile_check(dg.tiled(96, 128), 100, dt) == U
     assert dg.tile_check(dg.tiled(128, 128, 4, 32, stages=7), 100, dt) == U
     assert dg.tile_check(dg.tiled(128, 128, 4, 32, tile_k=48), 100, dt) == U
-    assert dg.tile_check(dg.tiled_ab(256, 256, 8, 16), 100, dt) == U
+    assert dg.tile_check(dg.tiled_ab(256, 256, 8, 16, stages=3), 100, dt) == U
+    # the 16 x 16-atom 256 x 256 rung has 64-byte k-tiles: bf16 only (an e4m3
+    # 16 x 16 x 128 MFMA needs 128 K bytes per k-tile)
+    a16 = dg.tiled_ab(256, 256, 8, 16, stages=4, tile_k=32 if dt == "bf16" else 64)
+    assert dg.tile_check(a16, 100, dt) == (dg.GEMM_OK if dt == "bf16" else U)
     assert dg.tile_check(dg.Tile(7, 128, 128), 100, dt) == U
     assert dg.lib.gemm_tile_check(None, 1, 0) == dg.GEMM_ERR_INVALID_VALUE
 
