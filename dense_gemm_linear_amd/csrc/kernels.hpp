@@ -346,10 +346,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // ---------------------------------------------------------------------------
 // The k-tile: KTB bytes of K (64 or 128) per pipeline stage.  A stage of the
 // A tile holds TM rows of KTB bytes; 16-byte chunk c of row r is stored at
-// slot c ^ key(r), key(r) = (r / (256 / KTB)) % (KTB / 16): an XOR swizzle at
-// 16-byte granularity ("GEMM Optimization Guide" page, section 3) chosen so
-// that 16 lanes reading the same chunk of 16 consecutive rows touch all 64
-// LDS banks once.  The global -> LDS copy is a 16-byte LDS DMA per lane (page
+// slot c ^ key(r), an XOR swizzle at 16-byte granularity ("GEMM Optimization
+// Guide" page, section 3).  key depends on bits 1-3 of r only, so rows 16
+// apart share it (a fragment read takes it from lane % 16).  Measured on
+// MI355X (SQ_LDS_BANK_CONFLICT of the fragment reads alone): for 128-byte
+// rows key = (r / 2) % 8 serves the 16 x 16 and 32 x 32 fragments without a
+// conflict; for 64-byte rows (r / 4) % 4 doubled every 16 x 16 fragment read
+// (lanes 16 i .. 16 i + 15 reading chunk i of 16 rows), while
+// ((r / 4) ^ (r / 2)) % 4 is conflict-free for both atoms.  The global -> LDS copy is a 16-byte LDS DMA per lane (page
 // section 11: 16 bytes per op on gfx950): one wave load fills 1 KiB = 1024 /
 // KTB rows, lane l landing in row l / (KTB / 16), slot l % (KTB / 16), so the
 // swizzle is applied to the global address.  B arrives as whole 1 KiB blocks
@@ -363,7 +367,7 @@ struct KTile {
     static constexpr int KPK = KTB / 64;           // Bs blocks per 16 columns per k-tile
     static __host__ __device__ constexpr uint32_t key(uint32_t row)
     {
-        return (row / (256 / KTB)) % CHUNKS;
+        return KTB == 64 ? ((row >> 2) ^ (row >> 1)) & 3u : (row >> 1) & 7u;
     }
 };
 
