@@ -823,6 +823,29 @@ constexpr int fit_stage_rows(int MR, int WAVES, int R, int SROW, int avail)
 }
 
 
+// Per-lane base addresses for LDS reads at compile-time offsets below LDS
+// bytes.  ds_read's immediate offset holds 16 bits, so a read at offset c
+// takes base c >> 16 and immediate c & 0xFFFF.  The bases past the first are
+// passed through an empty asm statement, so that the compiler cannot see them
+// as the first plus a constant: when it could, it gave every read past 64 KiB
+// an address register of its own (16 more VGPRs on the 8-wave 256 x 256
+// tile with 16x16 atoms, which then spilled to scratch).
+template <int LDS>
+struct LdsBases {
+    static constexpr int W = (LDS + 65535) / 65536;
+    uint32_t b[W];
+    __device__ __forceinline__ void init(uint32_t lane_off)
+    {
+        b[0] = lane_off;
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+            b[w] = lane_off + (uint32_t)w * 65536u;
+            asm volatile("" : "+v"(b[w]));
+        }
+    }
+    __device__ __forceinline__ uint32_t at(uint32_t c) const { return b[c >> 16] + (c & 0xFFFFu); }
+};
+
 // End of a k-tile: this wave's LDS reads of the stage are done and its share
 // of the next k-tile has landed (at most `vm` newer loads in flight); the
 // barrier then makes both true for the whole workgroup.  No workgroup memory
@@ -1033,6 +1056,14 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
     // 16-column block of this lane's column in atom 0 of this wave
     const uint32_t bblk = (uint32_t)(wn * NR * (R / 16) + (lr >> 4));
     const uint32_t b_lane = bblk * (uint32_t)p.KB * 1024u + (uint32_t)(lane & 15) * 16;
+    // A fragment reads: a per-lane part for each (K step, fragment part)
+    // plus a compile-time offset (stage, atom row).
+    LdsBases<S::LDS> a_at[STEPS][P];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            a_at[s][q].init((row0 + (uint32_t)lr) * KTB + (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4));
 
     i32x4 breg[ST][NR][STEPS][P];
     i32x4 af[frag_sets(ST, STEPS)][MR][P];
@@ -1111,9 +1142,7 @@ __global__ __launch_bounds__(64 * 4 * WM, 1) void gemm_tiled_kernel(GemmArgs p)
             if (f * G / (MR * P) != g)
                 continue;
             const int mi = f / P, q = f % P;
-            const uint32_t row = row0 + (uint32_t)(mi * R + lr);
-            const uint32_t off = (uint32_t)(stage * A_BUF) + row * KTB +
-                                 (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+            const uint32_t off = a_at[s][q].at((uint32_t)(stage * A_BUF + mi * R * KTB));
             af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
         }
     };
@@ -1243,6 +1272,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
     // atom 0 of this wave, group 0, 64-byte block 0.
     const uint32_t b_lds =
         (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * KPK * 1024 + (lane & 15) * 16);
+    // Fragment reads: a per-lane part for each (K step, fragment part) plus
+    // a compile-time offset (stage, atom row or column block, 1 KiB block).
+    LdsBases<S::LDS> a_at[STEPS][P], b_at[STEPS][P];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            a_at[s][q].init((row0 + (uint32_t)lr) * KTB +
+                            (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4));
+            b_at[s][q].init(b_lds + ((uint32_t)AT::b_group(s, lane, q) << 8));
+        }
 
     i32x4 af[frag_sets(ST, STEPS)][MR][P], bf[frag_sets(ST, STEPS)][NR][P];
     acc_t acc[MR][NR];
@@ -1315,16 +1355,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
                 continue;
             if (f < NR * P) {
                 const int j = f / P, q = f % P;
-                const uint32_t off = (uint32_t)(stage * STAGE + A_BUF) + b_lds +
-                                     (uint32_t)(j * (R / 16) * KPK * 1024) +
-                                     ((uint32_t)AT::b_half(s, q) << 10) +
-                                     ((uint32_t)AT::b_group(s, lane, q) << 8);
+                const uint32_t off = b_at[s][q].at((uint32_t)(stage * STAGE + A_BUF +
+                                                              j * (R / 16) * KPK * 1024 +
+                                                              (AT::b_half(s, q) << 10)));
                 bf[set][j][q] = *reinterpret_cast<const i32x4*>(lds + off);
             } else {
                 const int mi = (f - NR * P) / P, q = (f - NR * P) % P;
-                const uint32_t row = row0 + (uint32_t)(mi * R + lr);
-                const uint32_t off = (uint32_t)(stage * STAGE) + row * KTB +
-                                     (((uint32_t)AT::a_chunk(s, lane, q) ^ swz) << 4);
+                const uint32_t off = a_at[s][q].at((uint32_t)(stage * STAGE + mi * R * KTB));
                 af[set][mi][q] = *reinterpret_cast<const i32x4*>(lds + off);
             }
         }

@@ -5,7 +5,7 @@ select_tile is priced for 256 CUs, no device is touched).
   table the pick is the fastest swept tile, regret 1.0.
 - Held-out shapes (calibration/mi355x_holdout.jsonl, never fitted): the pick
   is one of the swept tiles and within 15 % of the fastest (measured:
-  geometric mean 1.032, worst 1.147).
+  geometric mean 1.017, worst 1.047).
 """
 import json
 import os
