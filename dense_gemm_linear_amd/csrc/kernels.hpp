@@ -270,8 +270,11 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // The 16 x 16 atoms are the pages' choice ("GEMM Optimization Guide" page,
 // section 6.1).  On MI355X the 32 x 32 bf16 MFMA sustains the full dense
 // rate with its accumulators in ordinary VGPRs, while back-to-back 16 x 16 x
-// 32 bf16 MFMAs accumulating in VGPRs issue at roughly half of it (measured),
-// so the large tiles use 32 x 32 atoms.
+// 32 bf16 MFMAs from one wave accumulating in VGPRs issue at roughly half of
+// it (measured).  With two waves per SIMD taking turns, the 16 x 16 atom
+// keeps the pipe as busy as the 32 x 32 one in the 8-wave 256 x 256 tile,
+// and the board holds a higher clock with it under its power limit, so the
+// ladder has both.
 template <int DT, int R>
 struct Atom;
 
@@ -353,10 +356,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // rows key = (r / 2) % 8 serves the 16 x 16 and 32 x 32 fragments without a
 // conflict; for 64-byte rows (r / 4) % 4 doubled every 16 x 16 fragment read
 // (lanes 16 i .. 16 i + 15 reading chunk i of 16 rows), while
-// ((r / 4) ^ (r / 2)) % 4 is conflict-free for both atoms.  The global -> LDS copy is a 16-byte LDS DMA per lane (page
-// section 11: 16 bytes per op on gfx950): one wave load fills 1 KiB = 1024 /
-// KTB rows, lane l landing in row l / (KTB / 16), slot l % (KTB / 16), so the
-// swizzle is applied to the global address.  B arrives as whole 1 KiB blocks
+// ((r / 4) ^ (r / 2)) % 4 is conflict-free for both atoms.  The global -> LDS
+// copy is a 16-byte LDS DMA per lane (page section 11: 16 bytes per op on
+// gfx950): one wave load fills 1 KiB = 1024 / KTB rows, lane l landing in row
+// l / (KTB / 16), slot l % (KTB / 16), so the swizzle is applied to the global
+// address.  B arrives as whole 1 KiB blocks
 // of the preshuffled layout (16 columns x 64 K bytes), KTB / 64 per 16-column
 // block per k-tile.
 template <int KTB>
