@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n)
 // writes its XOR to its own slot.  No workgroup barrier and no LDS: a wave
 // that is done leaves at once and frees its slot for the next workgroup's
 // waves (measured on MI355X, 90 MB: a barrier before one store per
-// workgroup cost 2.7 us, a shuffle reduction through LDS 2.3 us).  Its time is the floor under a kernel that must read the same
-// bytes once.
+// workgroup cost 2.7 us, a shuffle reduction through LDS 2.3 us).  Its time
+// is the floor under a kernel that must read the same bytes once.
 template <int D>
 __global__ __launch_bounds__(1024) void read_probe_kernel(const i32x4* buf, int64_t n16,
                                                          int64_t per16, uint32_t* out)
