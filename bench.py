@@ -823,11 +823,13 @@ def main(argv=None):
     value = flops(M, N, K) * args.steps / (r["total_ms"] * 1e-3) / 1e12
     tile = r["tile"]
     second = None
-    if args.tile is None:      # the library's own plan: one launch, or two over column ranges
+    if args.tile is None:      # the library's own plan: one launch, or two over column or row ranges
         import dense_gemm_linear_amd as dg
-        _, t2, n1 = dg.plan(M, N, K, dt, CUS, workspace.numel() if workspace is not None else 0)
-        if t2 is not None:
+        _, t2, n1, m1 = dg.plan(M, N, K, dt, CUS, workspace.numel() if workspace is not None else 0)
+        if t2 is not None and n1 < N:
             second = {"tile": t2.name, "first_columns": n1, "second_columns": N - n1}
+        elif t2 is not None:
+            second = {"tile": t2.name, "first_rows": m1, "second_rows": M - m1}
     out = {
         "metric": "GEMM TFLOP/s (2MNK/t) + % MFMA peak; HBM GB/s for M<=8 decode",
         "value": round(value, 2),

@@ -251,7 +251,7 @@ def _load_lib():
     lib.gemm_bf16_noalloc.restype = ctypes.c_int
     lib.gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int32, ctypes.c_size_t,
                               ctypes.POINTER(GemmTile), ctypes.POINTER(GemmTile),
-                              ctypes.POINTER(I64)]
+                              ctypes.POINTER(I64), ctypes.POINTER(I64)]
     lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_tile_check.argtypes = [ctypes.POINTER(GemmTile), I64, ctypes.c_int]
     lib.gemm_tile_check.restype = ctypes.c_int
@@ -298,13 +298,16 @@ def workspace_bytes(M: int, N: int, K: int, dtype, tile: Tile) -> int:
 
 def plan(M: int, N: int, K: int, dtype="bf16", num_cus: int = 256, workspace_bytes: int = 0):
     """The launches a GEMM with tile=None makes: (first tile, second tile or
-    None, columns of the first launch)."""
-    a, b, n = GemmTile(), GemmTile(), ctypes.c_int64(0)
+    None, columns of the first launch, rows of the first launch).  A second
+    launch takes the remaining columns (first columns < N) or the remaining
+    rows (first rows < M)."""
+    a, b, n, m = GemmTile(), GemmTile(), ctypes.c_int64(0), ctypes.c_int64(0)
     st = lib.gemm_plan(M, N, K, _dtype_code(dtype), num_cus, workspace_bytes, ctypes.byref(a),
-                       ctypes.byref(b), ctypes.byref(n))
+                       ctypes.byref(b), ctypes.byref(n), ctypes.byref(m))
     if st != GEMM_OK:
         raise GemmError("gemm_plan", st)
-    return Tile.from_c(a), (Tile.from_c(b) if n.value < N else None), n.value
+    two = n.value < N or m.value < M
+    return Tile.from_c(a), (Tile.from_c(b) if two else None), n.value, m.value
 
 
 def tile_check(tile: Tile, M: int, dtype="bf16") -> int:

@@ -233,15 +233,85 @@ int64_t tail_split_columns(const gemm_tile& t, const SplitPlan& pl, int64_t M, i
 // the stray round.  Measured on MI355X: the stray round costs about 40 % of a
 // round (its tiles start while the last full round drains), and a small GEMM
 // at least about 6 us (launch, cold prologue, epilogue), more than the model
-// gives it.  False if a chosen tile names no rung (never, for the selector's
-// own choices).
+// gives it.  Or, when no column split applies, the rows whose tiles of a
+// large rung fill whole rounds and the rest as a second GEMM (row_split).
+// False if a chosen tile names no rung (never, for the selector's own
+// choices).
 struct AutoPlan {
     gemm_tile t1, t2;
     int idx1, idx2;
     SplitPlan pl1, pl2;
     SkPlan sk1;    // the first launch's stream-K plan when t1.stream_k
-    int64_t n1;    // columns of the first launch; N: a single launch
+    int64_t n1;    // columns of the first launch; N: all of them
+    int64_t m1;    // rows of the first launch; M: all of them (at most one of
+                   // n1, m1 splits)
 };
+
+// Row split.  A shape whose tiles make one or more whole rounds plus a
+// stray part (GPT-3-XL dX, 10240 x 2048 x 8192: 320 tiles of 256 x 256 on
+// 256 CUs) runs the rows [0, m1) that fill whole rounds with a large tile
+// and the remaining rows as a second GEMM with a tile of their own, when the
+// model prices the pair, plus 3 us for the second launch starting only once
+// the first has drained, below 95 % of the single launch.  Candidates are the
+// 256 x 256, 256 x 128 and 128 x 256 tiles whose column count divides the
+// CUs, so that m1 rows make whole rounds; the first launch must choose that
+// tile for its rows.  The column split takes precedence.  Measured on
+// MI355X (graph replay, single launch -> two): 10240 x 2048 x 8192
+// 301.6 -> 269.2-270.4 us, 10240 x 2048 x 2048 88.0 -> 80.8, 8704 x 2048 x
+// 1024 44.9 -> 42.7, 8448 x 1024 x 2048 50.2 -> 47.3, 9216 x 2048 x 1024
+// 45.9 -> 44.0; without the 3 us, 8704 x 2048 x 512 was also split and
+// went 27.6 -> 29.3 (its launches are short), and 9216 x 1024 x 2048 gained
+// 1 %, which the rule now leaves as one launch.
+bool row_split(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes, AutoPlan* ap)
+{
+    const int e = dt == DT_BF16 ? 2 : 1;
+    constexpr double kMinGemmUs = 6.0, kSecondLaunchUs = 3.0;
+    constexpr int kShapes[3][2] = {{256, 256}, {256, 128}, {128, 256}};
+    double best = 0.95 * (double)ap->t1.predicted_us;
+    bool found = false;
+    AutoPlan cand = *ap;
+    for (const auto& sh : kShapes) {
+        const int tm = sh[0], tn = sh[1];
+        const int64_t tiles_n = (N + tn - 1) / tn;
+        if (tiles_n > cus || cus % tiles_n != 0)
+            continue;
+        const int64_t rows_round = (int64_t)(cus / tiles_n) * tm;
+        const int64_t m1 = M / rows_round * rows_round;
+        if (m1 == 0 || m1 >= M)
+            continue;
+        gemm_tile ta, tb;
+        int ia = -1, ib = -1;
+        choose_tile(m1, N, K, dt, cus, ws_bytes, &ta);
+        if (ta.kernel == GEMM_KERNEL_SKINNY || ta.tile_m != tm || ta.tile_n != tn ||
+            ta.k_split > 1 || !resolve_tile(ta, m1, e, &ia))
+            continue;
+        choose_tile(M - m1, N, K, dt, cus, ws_bytes, &tb);
+        if (!resolve_tile(tb, M - m1, e, &ib))
+            continue;
+        const SplitPlan pa = tile_split(ta, ia, m1, N, K, e);
+        const SplitPlan pb = tile_split(tb, ib, M - m1, N, K, e);
+        if (pa.ws_bytes > (int64_t)ws_bytes || pb.ws_bytes > (int64_t)ws_bytes)
+            continue;
+        const double price =
+            (double)ta.predicted_us + std::max((double)tb.predicted_us, kMinGemmUs) + kSecondLaunchUs;
+        if (price < best) {
+            best = price;
+            found = true;
+            cand.t1 = ta;
+            cand.idx1 = ia;
+            cand.pl1 = pa;
+            cand.t2 = tb;
+            cand.idx2 = ib;
+            cand.pl2 = pb;
+            cand.m1 = m1;
+        }
+    }
+    if (found) {
+        memset(&cand.sk1, 0, sizeof cand.sk1);
+        *ap = cand;
+    }
+    return found;
+}
 
 // Stream-K in place of a one-pass tile that fills less than one round of
 // the CUs, priced from measurements on MI355X (LLaMA prefill 597 x 11008 x
@@ -261,6 +331,7 @@ bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes
     const int e = dt == DT_BF16 ? 2 : 1;
     memset(ap, 0, sizeof *ap);
     ap->n1 = N;
+    ap->m1 = M;
     choose_tile(M, N, K, dt, cus, ws_bytes, &ap->t1);
     if (!resolve_tile(ap->t1, M, e, &ap->idx1))
         return false;
@@ -283,25 +354,28 @@ bool plan_auto(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes
         }
     }
     const int64_t n1 = tail_split_columns(ap->t1, ap->pl1, M, N, cus);
-    if (n1 == 0)
-        return true;
-    gemm_tile t2;
-    int idx2 = -1;
-    choose_tile(M, N - n1, K, dt, cus, ws_bytes, &t2);
-    const int64_t tiles = ((M + ap->t1.tile_m - 1) / ap->t1.tile_m) *
-                          ((N + ap->t1.tile_n - 1) / ap->t1.tile_n);
-    const double round_us = ap->t1.predicted_us / (double)((tiles + cus - 1) / cus);
-    constexpr double kMinGemmUs = 6.0;
-    if (!resolve_tile(t2, M, e, &idx2) ||
-        std::max((double)t2.predicted_us, kMinGemmUs) >= 0.4 * round_us)
-        return true;
-    const SplitPlan pl2 = tile_split(t2, idx2, M, N - n1, K, e);
-    if (pl2.ws_bytes > (int64_t)ws_bytes)
-        return true;
-    ap->t2 = t2;
-    ap->idx2 = idx2;
-    ap->pl2 = pl2;
-    ap->n1 = n1;
+    if (n1 != 0) {
+        gemm_tile t2;
+        int idx2 = -1;
+        choose_tile(M, N - n1, K, dt, cus, ws_bytes, &t2);
+        const int64_t tiles = ((M + ap->t1.tile_m - 1) / ap->t1.tile_m) *
+                              ((N + ap->t1.tile_n - 1) / ap->t1.tile_n);
+        const double round_us = ap->t1.predicted_us / (double)((tiles + cus - 1) / cus);
+        constexpr double kMinGemmUs = 6.0;
+        if (resolve_tile(t2, M, e, &idx2) &&
+            std::max((double)t2.predicted_us, kMinGemmUs) < 0.4 * round_us) {
+            const SplitPlan pl2 = tile_split(t2, idx2, M, N - n1, K, e);
+            if (pl2.ws_bytes <= (int64_t)ws_bytes) {
+                ap->t2 = t2;
+                ap->idx2 = idx2;
+                ap->pl2 = pl2;
+                ap->n1 = n1;
+                return true;
+            }
+        }
+    }
+    if (ap->t1.kernel != GEMM_KERNEL_SKINNY)
+        row_split(M, N, K, dt, cus, ws_bytes, ap);
     return true;
 }
 
@@ -403,6 +477,23 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
                 err = launch_gemm(dt, ap.t2, ap.idx2, ap.pl2, A, lda,
                                   static_cast<const uint8_t*>(Bs) + n1 / 16 * be, sa, sb, C + n1,
                                   ldc, M, N - n1, K, ep2, ws, s);
+            return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+        }
+        if (ap.m1 < M) {
+            const int64_t m1 = ap.m1;
+            Epilogue ep2 = ep;
+            if (ep2.scale_m)
+                ep2.scale_m += m1;
+            if (ep2.mul) {
+                ep2.mul += m1 * ep2.ldmul;
+                ep2.mul_vec = ((uintptr_t)ep2.mul & 15u) == 0 && ep2.ldmul % 8 == 0;
+            }
+            hipError_t err =
+                launch_gemm(dt, t, idx, pl, A, lda, Bs, sa, sb, C, ldc, m1, N, K, ep, ws, s);
+            if (err == hipSuccess)
+                err = launch_gemm(dt, ap.t2, ap.idx2, ap.pl2,
+                                  static_cast<const uint8_t*>(A) + m1 * lda * e, lda, Bs, sa, sb,
+                                  C + m1 * ldc, ldc, M - m1, N, K, ep2, ws, s);
             return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
         }
     }
@@ -624,9 +715,10 @@ gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_
 
 gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
                       size_t workspace_bytes, gemm_tile* first, gemm_tile* second,
-                      int64_t* first_columns)
+                      int64_t* first_columns, int64_t* first_rows)
 {
-    if (!first || !second || !first_columns || M <= 0 || N <= 0 || K <= 0 || num_cus <= 0 ||
+    if (!first || !second || !first_columns || !first_rows || M <= 0 || N <= 0 || K <= 0 ||
+        num_cus <= 0 ||
         (dtype != GEMM_BF16 && dtype != GEMM_FP8_E4M3))
         return GEMM_ERR_INVALID_VALUE;
     dg::AutoPlan ap;
@@ -635,6 +727,7 @@ gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t
     *first = ap.t1;
     *second = ap.t2;
     *first_columns = ap.n1;
+    *first_rows = ap.m1;
     return GEMM_OK;
 }
 

@@ -289,7 +289,7 @@ gemm_status transpose_2d(const void* src, int64_t ld_src, void* dst, int64_t ld_
  *   C   device, bf16 bits, row-major [M, ldc], ldc >= N, 2-byte aligned; only
  *       the M x N region is written (columns N..ldc-1 are untouched).
  *   tile  NULL = select_tile(M, N, K, GEMM_BF16, <device CUs>), or the two
- *         launches over column ranges gemm_plan describes when that tile
+ *         launches over column or row ranges gemm_plan describes when that tile
  *         would leave a nearly empty last round; otherwise a forced
  *         configuration, validated against the shape (always one launch).
  *
@@ -414,8 +414,9 @@ gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, ui
  * passes tile == NULL, on a device with num_cus compute units.  Pure host
  * function, no device access.
  *
- * Usually one launch: *first = select_tile_ws(...), *first_columns = N and
- * *second zeroed.  When the chosen one-pass tiled tile would run two or more
+ * Usually one launch: *first = select_tile_ws(...), *first_columns = N,
+ * *first_rows = M and *second zeroed.  When the chosen one-pass tiled tile
+ * would run two or more
  * full rounds of tiles over the CUs and then a last round that fills at most
  * a quarter of them (wave quantization, TraceLens GEMM analysis page), the
  * columns [0, *first_columns) that fill whole rounds run with *first and the
@@ -423,6 +424,15 @@ gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, ui
  * its cost, at least about 6 us, is below 40 % of one round's, what such a
  * stray round measured on MI355X.  Both launches are enqueued on the caller's
  * stream, in that order; the outputs they write are disjoint.
+ *
+ * Otherwise, when a 256 x 256, 256 x 128 or 128 x 256 tile's column count
+ * divides the CUs and the rows [0, *first_rows) make whole rounds of such
+ * tiles, those rows may run with *first (that tile, chosen for them) and the
+ * rows [*first_rows, M) as a second GEMM with *second, if the model prices
+ * the pair, plus 3 us for the second launch's start, below 95 % of the single
+ * launch.  Measured on MI355X for the GPT-3-XL input gradient 10240 x 2048 x
+ * 8192: 302 us as one launch, 270 us as 8192 + 2048 rows.  At most one of
+ * *first_columns < N and *first_rows < M.
  *
  * When the chosen one-pass tile (a stream-K rung) fills less than one round
  * of the CUs and the workspace holds its stream-K partials, *first is its
@@ -437,7 +447,7 @@ gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, ui
  */
 gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, int32_t num_cus,
                       size_t workspace_bytes, gemm_tile* first, gemm_tile* second,
-                      int64_t* first_columns);
+                      int64_t* first_columns, int64_t* first_rows);
 
 /*
  * gemm_tile_check -- would `tile`, forced on gemm_bf16 (dtype GEMM_BF16) or

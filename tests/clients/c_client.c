@@ -16,7 +16,7 @@ static void show(const char* what, const gemm_tile* t)
 int main(void)
 {
     gemm_tile t, t2;
-    int64_t n1 = 0;
+    int64_t n1 = 0, m1 = 0;
     if (select_tile(4096, 4096, 4096, GEMM_BF16, 256, &t) != GEMM_OK)
         return 1;
     show("select_4096", &t);
@@ -27,11 +27,12 @@ int main(void)
         return 1;
     show("select_ws_48", &t);
     printf("workspace_48 %zu\n", gemm_workspace_bytes(48, 4096, 4096, GEMM_BF16, &t));
-    if (gemm_plan(1024, 50257, 512, GEMM_BF16, 256, 0, &t, &t2, &n1) != GEMM_OK)
+    if (gemm_plan(1024, 50257, 512, GEMM_BF16, 256, 0, &t, &t2, &n1, &m1) != GEMM_OK)
         return 1;
     show("plan_first", &t);
     show("plan_second", &t2);
     printf("plan_columns %lld\n", (long long)n1);
+    printf("plan_rows %lld\n", (long long)m1);
     printf("shuffle_bytes %zu %zu\n", shuffle_b_bytes(11008, 4096, GEMM_BF16),
            shuffle_b_bytes(4096, 4096, GEMM_FP8_E4M3));
     printf("tile_check %d %d\n", (int)gemm_tile_check(&t, 1024, GEMM_BF16),

@@ -350,21 +350,43 @@ def test_gemm_plan_splits_a_stray_last_round():
     as 49152 columns with that tile and 1105 with their own; shapes whose
     rounds are full, or whose rounds are too short to pay a second launch,
     run as one."""
-    first, second, n1 = dg.plan(1024, 50257, 512, "bf16", 256, 0)
-    assert (first.tile_m, first.tile_n, n1) == (256, 256, 49152)
+    first, second, n1, m1 = dg.plan(1024, 50257, 512, "bf16", 256, 0)
+    assert (first.tile_m, first.tile_n, n1, m1) == (256, 256, 49152, 1024)
     assert second is not None and dg.tile_check(second, 1024, "bf16") == dg.GEMM_OK
     assert first.name == dg.select_tile(1024, 50257, 512, "bf16", 256).name
     for shape in ((4096, 4096, 4096), (512, 50257, 256), (1, 11008, 4096), (597, 11008, 4096)):
-        f, s, n = dg.plan(*shape, "bf16", 256, 0)
-        assert s is None and n == shape[1], shape
+        f, s, n, m = dg.plan(*shape, "bf16", 256, 0)
+        assert s is None and n == shape[1] and m == shape[0], shape
         assert f.name == dg.select_tile(*shape, "bf16", 256).name
     P = dg.lib.gemm_plan
-    t1, t2, n = dg.GemmTile(), dg.GemmTile(), ctypes.c_int64()
+    t1, t2, n, m = dg.GemmTile(), dg.GemmTile(), ctypes.c_int64(), ctypes.c_int64()
     for bad in ((0, 16, 16, 0, 256), (16, 16, 16, 0, 0), (16, 16, 16, 7, 256)):
         M, N, K, dt, cus = bad
-        assert P(M, N, K, dt, cus, 0, ctypes.byref(t1), ctypes.byref(t2), ctypes.byref(n)) == \
-            dg.GEMM_ERR_INVALID_VALUE
-    assert P(16, 16, 16, 0, 256, 0, None, ctypes.byref(t2), ctypes.byref(n)) == dg.GEMM_ERR_INVALID_VALUE
+        assert P(M, N, K, dt, cus, 0, ctypes.byref(t1), ctypes.byref(t2), ctypes.byref(n),
+                 ctypes.byref(m)) == dg.GEMM_ERR_INVALID_VALUE
+    assert P(16, 16, 16, 0, 256, 0, None, ctypes.byref(t2), ctypes.byref(n),
+             ctypes.byref(m)) == dg.GEMM_ERR_INVALID_VALUE
+    assert P(16, 16, 16, 0, 256, 0, ctypes.byref(t1), ctypes.byref(t2), ctypes.byref(n),
+             None) == dg.GEMM_ERR_INVALID_VALUE
+
+
+def test_gemm_plan_splits_rows_of_a_stray_round():
+    """gemm_plan, row split: 10240 x 2048 x 8192 (the GPT-3-XL input gradient)
+    has 320 tiles of 256 x 256, one round and a quarter, and no column split
+    applies; the rows [0, 8192) make one whole round with the 256 x 256 tile
+    and the other 2048 rows run as a second GEMM.  A short K (512) leaves
+    8704 x 2048 as one launch, and neither the 4096^3 product nor lm_head
+    (a column split) is split by rows."""
+    first, second, n1, m1 = dg.plan(10240, 2048, 8192, "bf16", 256, 128 << 20)
+    assert (first.tile_m, first.tile_n, n1, m1) == (256, 256, 2048, 8192)
+    assert second is not None and dg.tile_check(second, 2048, "bf16") == dg.GEMM_OK
+    assert first.name == dg.select_tile(8192, 2048, 8192, "bf16", 256, workspace_bytes=128 << 20).name
+    assert second.name == dg.select_tile(2048, 2048, 8192, "bf16", 256, workspace_bytes=128 << 20).name
+    for shape, ws in (((8704, 2048, 512), 0), ((4096, 4096, 4096), 0), ((8192, 2048, 10240), 0)):
+        f, s, n, m = dg.plan(*shape, "bf16", 256, ws)
+        assert s is None and (n, m) == (shape[1], shape[0]), shape
+    f, s, n, m = dg.plan(1024, 50257, 512, "bf16", 256, 0)
+    assert m == 1024 and n < 50257
 
 
 def test_select_tile_concurrent_callers_agree():

@@ -33,9 +33,9 @@ def test_c_client_matches_binding(tmp_path):
     t48 = dg.select_tile(48, 4096, 4096, "bf16", 256, workspace_bytes=64 << 20)
     assert got["select_ws_48"] == fields(t48)
     assert int(got["workspace_48"]) == dg.workspace_bytes(48, 4096, 4096, "bf16", t48)
-    first, second, n1 = dg.plan(1024, 50257, 512, "bf16", 256, 0)
+    first, second, n1, m1 = dg.plan(1024, 50257, 512, "bf16", 256, 0)
     assert got["plan_first"] == fields(first) and got["plan_second"] == fields(second)
-    assert int(got["plan_columns"]) == n1
+    assert int(got["plan_columns"]) == n1 and int(got["plan_rows"]) == m1 == 1024
     assert got["shuffle_bytes"] == f"{dg.shuffle_b_bytes(11008, 4096)} {dg.shuffle_b_bytes(4096, 4096, 'fp8')}"
     assert got["tile_check"] == f"{dg.GEMM_OK} {dg.GEMM_ERR_INVALID_VALUE}"
     assert got["errors"] == "GEMM_ERR_INVALID_VALUE GEMM_ERR_INVALID_VALUE GEMM_ERR_INVALID_VALUE"

@@ -250,6 +250,21 @@ def test_epilogue_across_two_launches(inplace):
     check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], "epilogue across two launches")
 
 
+@pytest.mark.parametrize("inplace", [False, True], ids=["mul", "mul_in_place"])
+def test_epilogue_across_two_launches_over_rows(inplace):
+    """8704 x 2048 x 1024 runs as two GEMMs over row ranges (gemm_plan's row
+    split, rows [0, 8192) and the rest): the second one's row scales and
+    multiplier start at the first's last row."""
+    M, N, K = 8704, 2048, 1024
+    plan = dg.plan(M, N, K, "bf16", 256, 0)
+    assert plan[1] is not None and plan[3] == 8192, "shape no longer splits by rows"
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=216)
+    parts = make_parts(M, N, True, 14)
+    C, ok = run_epi("bf16", A, B, parts, "relu", None, inplace=inplace)
+    assert ok
+    check_exact(C, oracle_epi("bf16", A, B, parts, "relu")[1], "epilogue across two launches over rows")
+
+
 @pytest.mark.parametrize("tile", [dg.tiled(128, 256, 4, 32), dg.tiled_ab(256, 256, 8, 32),
                                   dg.tiled_pp(256, 256), dg.tiled(64, 64)],
                          ids=lambda t: t.name)

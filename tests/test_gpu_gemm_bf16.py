@@ -206,7 +206,7 @@ def test_ragged_last_round_two_launches(ldc_extra, col0):
     49152 columns with it and the other 1105 as a second GEMM with a tile of
     their own (gemm_plan).  Every output against the oracle, bit-exact."""
     M, N, K = 1024, 50257, 512
-    first, second, n1 = dg.plan(M, N, K, "bf16", 256, 0)
+    first, second, n1, _ = dg.plan(M, N, K, "bf16", 256, 0)
     print(f"[two launches {M}x{N}x{K}: {first.name} x {n1} + {second and second.name}]", flush=True)
     assert second is not None and n1 == 49152, "shape no longer splits"
     A, B, ref = lmhead_smallint()

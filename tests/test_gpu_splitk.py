@@ -126,7 +126,7 @@ def test_two_launches_with_split_remainder():
     the launch boundary and of tile boundaries, bit-exact on small integers."""
     M, N, K = 4096, 12480, 2048
     ws = nan_workspace(64 << 20)
-    first, second, n1 = dg.plan(M, N, K, "bf16", 256, ws.numel())
+    first, second, n1, _ = dg.plan(M, N, K, "bf16", 256, ws.numel())
     print(f"[two launches {M}x{N}x{K}: {first.name} x {n1} + {second and second.name}]", flush=True)
     assert second is not None and second.k_split > 1 and n1 == 12288, "shape no longer splits"
     A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=213)
@@ -136,3 +136,43 @@ def test_two_launches_with_split_remainder():
     cols = np.unique(np.concatenate([sample_lines(N), np.arange(n1 - 3, n1 + 3), np.arange(N - 3, N)]))
     ms, ns, vals, _ = oracle_lines("bf16", A, B, rows, cols)
     check_exact(C[ms, ns][None, :], vals[None, :], "two launches, split-K remainder")
+
+
+@pytest.mark.parametrize("ws_mib", [0, 128])
+def test_two_launches_over_rows(ws_mib):
+    """8704 x 2048 x 1024: 272 tiles of 256 x 256, one round and 16 tiles
+    more; the rows [0, 8192) run with that tile and the other 512 rows as a
+    second GEMM (gemm_plan's row split).  Whole rows on both sides of the
+    launch boundary, whole columns, bit-exact on small integers."""
+    M, N, K = 8704, 2048, 1024
+    ws = nan_workspace(ws_mib << 20) if ws_mib else None
+    first, second, n1, m1 = dg.plan(M, N, K, "bf16", 256, ws.numel() if ws is not None else 0)
+    print(f"[row split {M}x{N}x{K} ws {ws_mib} MiB: {first.name} x {m1} rows + "
+          f"{second and second.name}]", flush=True)
+    assert second is not None and m1 == 8192 and n1 == N, "shape no longer splits by rows"
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=214)
+    C, ok = run("bf16", A, B, workspace=ws)
+    assert ok
+    rows = np.unique(np.concatenate([sample_lines(M), np.arange(m1 - 3, m1 + 3), np.arange(M - 3, M)]))
+    cols = sample_lines(N)
+    ms, ns, vals, _ = oracle_lines("bf16", A, B, rows, cols)
+    check_exact(C[ms, ns][None, :], vals[None, :], "two launches over rows")
+
+
+def test_two_launches_over_rows_split_remainder():
+    """10240 x 2048 x 8192 (the GPT-3-XL input gradient) with a 128 MiB
+    workspace: 8192 rows on the 256 x 256 tile, the other 2048 as a split-K
+    GEMM that uses the workspace.  Sampled rows and columns on both sides of
+    the boundary against the oracle: bit-exact on small integers."""
+    M, N, K = 10240, 2048, 8192
+    ws = nan_workspace(128 << 20)
+    first, second, n1, m1 = dg.plan(M, N, K, "bf16", 256, ws.numel())
+    print(f"[row split {M}x{N}x{K}: {first.name} x {m1} rows + {second and second.name}]", flush=True)
+    assert second is not None and second.k_split > 1 and m1 == 8192, "shape no longer splits by rows"
+    A, B = datagen.make_bf16_pair(M, N, K, "smallint", "smallint", config=215)
+    C, ok = run("bf16", A, B, workspace=ws)
+    assert ok
+    rows = np.unique(np.concatenate([sample_lines(M, n_random=3), np.arange(m1 - 2, m1 + 2)]))
+    cols = sample_lines(N, n_random=3)
+    ms, ns, vals, _ = oracle_lines("bf16", A, B, rows, cols)
+    check_exact(C[ms, ns][None, :], vals[None, :], "two launches over rows, split-K remainder")
