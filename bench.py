@@ -999,7 +999,9 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak:
                           **({"timing": f"sustained {soak} s"} if soak > 0 else {}),
                           "tflops": round(flops(M, N, K) / (us * 1e-6) / 1e12, 1),
                           "gbps": round(alg_bytes(M, N, K, dt) / (us * 1e-6) / 1e9, 1)}), flush=True)
-    pick = dg.plan(M, N, K, dt, CUS, ws_bytes)[0]
+    # the selector's single-launch pick (the sweep times single launches; a
+    # two-launch plan's first tile is chosen for part of the shape only)
+    pick = dg.select_tile(M, N, K, dt, CUS, workspace_bytes=ws_bytes)
     best = min(res, key=res.get)
     print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
                       "best": best, "best_us": round(res[best], 3),
