@@ -311,7 +311,9 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s)
 // added in increasing s, a fixed order, so the result does not depend on
 // which workgroup of the GEMM finished first; e4m3 products are then scaled
 // as (x * sa) * sb, as in the one-pass epilogue.  One thread per 4
-// consecutive columns of one row; planes are read with 16-byte loads.
+// consecutive columns of one row; planes are read with 16-byte loads, eight
+// at a time in flight before any is added (48 x 4096 x 4096 in six slices,
+// measured on MI355X: 14.0-14.2 -> 13.6 us for the whole GEMM).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int splits, int M,
                                                             int N, int ldw, uint16_t* C,
                                                             int64_t ldc, const float* sa,
@@ -325,18 +327,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int
     const int c0 = (int)(t - (int64_t)row * q) * 4;
     const int64_t plane = (int64_t)M * ldw;
     const float* src = ws + (int64_t)row * ldw + c0;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-    for (int s = 1; s < splits; ++s) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + s * plane);
-        acc[0] += v[0];
-        acc[1] += v[1];
-        acc[2] += v[2];
-        acc[3] += v[3];
-    }
     float scale_a = 1.f, scale_b = 1.f;
     if (sa) {
         scale_a = *sa;
         scale_b = *sb;
+    }
+    constexpr int B = 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += B) {
+        f32x4 v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (s0 + j < splits)
+                v[j] = *reinterpret_cast<const f32x4*>(src + (int64_t)(s0 + j) * plane);
+        // plane 0 starts the sum (so a -0 partial stays -0), the others are
+        // added in increasing order
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (s0 + j >= splits)
+                break;
+            if (s0 + j == 0) {
+                acc = v[0];
+            } else {
+                acc[0] += v[j][0];
+                acc[1] += v[j][1];
+                acc[2] += v[j][2];
+                acc[3] += v[j][3];
+            }
+        }
     }
     uint16_t h[4];
 #pragma unroll
