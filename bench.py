@@ -751,6 +751,8 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile of the ladder on the workload (one JSON line each) and the "
                          "selector's pick; reports the selector's regret")
+    ap.add_argument("--sweep-only", default=None, metavar="REGEX",
+                    help="with --sweep: time only the tiles whose name matches REGEX (a full match)")
     ap.add_argument("--regret", default=None, metavar="SWEEP_JSONL",
                     help="host only: the selector's pick against the fastest tile of every workload "
                          "in a --sweep output file")
@@ -772,7 +774,7 @@ def main(argv=None):
     name = args.workload
     M, N, K, dt = WORKLOADS[name][:4]
     if args.sweep:
-        return sweep(name, args.steps, args.warmup, args.workspace_mib, args.sweep_soak)
+        return sweep(name, args.steps, args.warmup, args.workspace_mib, args.sweep_soak, args.sweep_only)
     if args.read_floor is not None:
         return read_floor_report(args.read_floor or
                                  [n for n in WORKLOADS if bound_of(*WORKLOADS[n][:4]) == "hbm"])
@@ -953,7 +955,8 @@ def sustained_graph_us(call, steps: int, seconds: float) -> float:
     return us
 
 
-def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak: float = 0.0) -> int:
+def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak: float = 0.0,
+          only: str | None = None) -> int:
     """Every feasible tile on one workload, graph-timed (`steps` launches per
     graph, median of 3 replays); prints a line per tile and a summary with
     the selector's regret (its pick's time over the best time).  soak > 0:
@@ -988,6 +991,9 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak:
             need = dg.workspace_bytes(M, N, K, dt, ts)
             if 0 < need <= ws_bytes:
                 tiles.append(ts)
+    if only:
+        import re
+        tiles = [t for t in tiles if re.fullmatch(only, t.name)]
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     sets, scales, _ = setup
     res = {}
@@ -1002,6 +1008,12 @@ def sweep(name: str, steps: int, warmup: int, ws_mib: int = WORKSPACE_MIB, soak:
     # the selector's single-launch pick (the sweep times single launches; a
     # two-launch plan's first tile is chosen for part of the shape only)
     pick = dg.select_tile(M, N, K, dt, CUS, workspace_bytes=ws_bytes)
+    if not res:
+        print(json.dumps({"sweep_summary": name, "selected": pick.name, "timed": 0}), flush=True)
+        return 0
+    if pick.name not in res:
+        print(json.dumps({"sweep_summary": name, "selected": pick.name, "timed": len(res)}), flush=True)
+        return 0
     best = min(res, key=res.get)
     print(json.dumps({"sweep_summary": name, "selected": pick.name, "selected_us": round(res[pick.name], 3),
                       "best": best, "best_us": round(res[best], 3),

@@ -1445,6 +1445,226 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
+// A+B kernel with whole-line A loads ("AB-line" kernel), 256 x 256 tiles with
+// one K step per 64-byte k-tile (e4m3 32 x 32 atoms).  The A+B kernel above
+// loads each k-tile of A as 16 rows x 64 bytes per LDS-DMA instruction: half
+// of every 128-byte line, the other half a k-tile later.  Here A is loaded in
+// k-tile pairs, 8 rows x 128 bytes (whole lines) per instruction, into NA = 3
+// pair stages of 128-byte rows (swizzled as the 128-byte k-tiles are); B keeps
+// its ST = 4 stages of 64-byte k-tiles.  Measured on MI355X, the operand
+// stream alone (no MFMAs) is 17 % faster this way for the e4m3 4096^3 tile
+// grid.  LDS: B stages [0, 64 KiB), A pair stages [64, 160 KiB).
+//
+// Phase t multiplies k-tile t and reads the fragments of k-tile t + 1, as in
+// k_loop, and issues half t % 2 of A pair t / 2 + 2 and all of B k-tile t + 3:
+// the same number of loads per wave and phase as the 64-byte kernel (NAL / 2 +
+// NBL), so the same wait counts hold.  Pair q's stage last held pair q - 3,
+// whose k-tile 2q - 5 was read in phase 2q - 6 and is past the barrier of
+// phase 2q - 5; pair q's loads go out after the barriers of phases 2q - 4 and
+// 2q - 3 and have landed at the barrier of phase 2q - 1, which reads k-tile
+// 2q (one phase of loads, NAL / 2 + NBL, may still be in flight).  Plain and
+// fused-epilogue launches only (split-K and stream-K use the A+B kernel).
+template <int DT, int R, int WM, int WN, bool EPI>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_ab_line_kernel(GemmArgs p)
+{
+    constexpr int TM = 256, TN = 256, ST = 4, NA = 3, KTB = 64;
+    using AT = Atom<DT, R>;
+    using acc_t = typename AT::acc_t;
+    constexpr int WAVES = WM * WN, MR = TM / WM / R, NR = TN / WN / R, P = AT::P;
+    constexpr int NAL = 32 / WAVES;                   // A loads per wave and pair
+    constexpr int NBL = 16 / WAVES;                   // B loads per wave and k-tile
+    constexpr int LOADS = NAL / 2 + NBL;              // loads per wave and phase
+    constexpr int B_STAGE = TN * KTB;                 // 16 KiB
+    constexpr int A_BASE = ST * B_STAGE;              // 64 KiB
+    constexpr int A_PSTAGE = TM * 128;                // 32 KiB
+    constexpr int LDS = A_BASE + NA * A_PSTAGE;       // 160 KiB
+    constexpr int WCOLS = TN / WN, SROW = WCOLS * 2 + 16;
+    constexpr int CH = fit_stage_rows(MR, WAVES, R, SROW, LDS);
+    constexpr int G = step_groups(MR * NR);
+    static_assert(AT::STEPS * KTB / 128 == 1, "one K step per 64-byte k-tile");
+    static_assert(WAVES % 2 == 0 && 32 % WAVES == 0 && NAL % 2 == 0, "A pair split");
+    static_assert(LDS <= 160 * 1024 && WAVES * CH * R * SROW <= LDS, "LDS budget");
+    static_assert(2 * LOADS <= 63, "pipeline depth vs vmcnt");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int wg, tm, tn;
+    split_slice<false>(p, wg);
+    tile_coords<DG_GROUP_M>(wg, p.tiles_m, p.tiles_n, tm, tn);
+    const KRange kr = k_range<KTB, false>(p, 0);
+    const int m0 = tm * TM, n0 = tn * TN;
+    const int rows = min(TM, p.M - m0);
+    const rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b,
+                                (uint32_t)((int64_t)(rows - 1) * p.lda_b + p.KA_b));
+    const int nb0 = n0 >> 4;
+    const int nbv = min(TN / 16, p.nblk - nb0);
+    const rsrc_t rb = make_rsrc(p.Bs + (int64_t)nb0 * p.KB * 1024,
+                                (uint32_t)nbv * (uint32_t)p.KB * 1024u);
+
+    // A pair chunk c = wave + WAVES i: rows 8c .. 8c + 7, 128 bytes each.  The
+    // swizzle key of row 8c + lane / 8 depends on c only through c % 2 = wave
+    // % 2, so chunk i sits 8 WAVES i rows below chunk 0.  The row goes in the
+    // per-lane offset, which the descriptor's range check sees (rows past M
+    // read zeros); the pair's K offset is scalar and stays inside the row
+    // unless the K-tail mask replaces the offset.
+    const ADma ad0 = a_dma_lane<128>(wave, lane, p.lda_b);
+    const uint32_t a_rows = 8u * WAVES * (uint32_t)p.lda_b;
+    const uint32_t b_goff0 = (uint32_t)wave * (uint32_t)p.KB * 1024u + lane * 16;
+    const uint32_t b_blocks = (uint32_t)WAVES * (uint32_t)p.KB * 1024u;
+
+    const int lr = lane % R;
+    const uint32_t swz = KTile<128>::key((uint32_t)(lane & 15));
+    const uint32_t row0 = (uint32_t)(wm * (TM / WM));
+    const uint32_t b_lds = (uint32_t)((wn * NR * (R / 16) + (lr >> 4)) * 1024 + (lane & 15) * 16);
+    // A fragment offsets for the first half of a 128-byte row; the second
+    // half reads chunk c + 4 where the first reads c < 4, i.e. the same
+    // offset with bit 6 flipped
+    uint32_t a_lane[P], b_lane[P], a_cur[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        a_lane[q] = (uint32_t)A_BASE + (row0 + (uint32_t)lr) * 128u +
+                    (((uint32_t)AT::a_chunk(0, lane, q) ^ swz) << 4);
+        b_lane[q] = b_lds + ((uint32_t)AT::b_group(0, lane, q) << 8);
+    }
+
+    i32x4 af[2][MR][P], bf[2][NR][P];
+    acc_t acc[MR][NR];
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[mi][j] = zero_acc<AT>();
+
+    // A loads of pair q, chunks [i0, i0 + n): op i - i0 + op0 of the phase
+    auto load_a = [&](int q, int i0, int n, int part, int nparts, int op0)
+                      __attribute__((always_inline)) {
+        uint8_t* base = lds + A_BASE + (q % NA) * A_PSTAGE;
+        const bool mask = 2 * q + 1 >= kr.last_full;
+#pragma unroll
+        for (int i = 0; i < NAL; ++i) {
+            if (i < i0 || i >= i0 + n || (op0 + i - i0) % nparts != part)
+                continue;
+            uint32_t off = ad0.goff + (uint32_t)i * a_rows;
+            if (mask && (int)((uint32_t)q * 128u + ad0.col) >= kr.ka_end)
+                off = kOOB;
+            dma16(ra, base + (wave + WAVES * i) * 1024, off, (uint32_t)q * 128u);
+        }
+    };
+    // B loads of k-tile kt into its stage: ops op0 ..
+    auto load_b = [&](int kt, int part, int nparts, int op0) __attribute__((always_inline)) {
+        const bool mask = kt >= kr.last_full;
+        uint8_t* base = lds + (kt % ST) * B_STAGE;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            if ((op0 + i) % nparts != part)
+                continue;
+            uint32_t off = b_goff0 + (uint32_t)i * b_blocks;
+            if (mask && kt >= kr.kb_end)
+                off = kOOB;
+            dma16(rb, base + (wave + WAVES * i) * 1024, off, (uint32_t)kt * 1024u);
+        }
+    };
+    // A read bases of k-tile kt, whose parity H is a constant here (trips of
+    // ST phases start at multiples of ST)
+    auto set_a = [&](int kt, auto hc) __attribute__((always_inline)) {
+        constexpr int H = decltype(hc)::value;
+        const uint32_t d = (uint32_t)((kt / 2) % NA) * A_PSTAGE;
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            a_cur[q] = (a_lane[q] ^ (uint32_t)(H * 64)) + d;
+    };
+    // group g of the fragment reads of the k-tile in B stage bstage (A from a_cur)
+    auto read = [&](int bstage, int set, int g) __attribute__((always_inline)) {
+        constexpr int NF = (MR + NR) * P;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f * G / NF != g)
+                continue;
+            if (f < NR * P) {
+                const int j = f / P, q = f % P;
+                bf[set][j][q] = *reinterpret_cast<const i32x4*>(
+                    lds + b_lane[q] + (uint32_t)(bstage * B_STAGE + j * (R / 16) * 1024));
+            } else {
+                const int mi = (f - NR * P) / P, q = (f - NR * P) % P;
+                af[set][mi][q] =
+                    *reinterpret_cast<const i32x4*>(lds + a_cur[q] + (uint32_t)(mi * R * 128));
+            }
+        }
+    };
+    auto mma = [&](int set, int g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < MR * NR; ++a) {
+            if (a * G / (MR * NR) != g)
+                continue;
+            const int mi = a / NR, j = a % NR;
+            acc[mi][j] = AT::mma(af[set][mi], bf[set][j], acc[mi][j]);
+        }
+    };
+
+    // prologue: A pairs 0 and 1, B k-tiles 0, 1, 2; the first group (pair 0,
+    // k-tile 0) has landed once at most the later 2 LOADS are in flight
+    load_a(0, 0, NAL, 0, 1, 0);
+    load_b(0, 0, 1, 0);
+    load_b(1, 0, 1, 0);
+    load_a(1, 0, NAL, 0, 1, 0);
+    load_b(2, 0, 1, 0);
+    DG_STAGE_BARRIER(2 * LOADS);
+    set_a(0, std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        read(0, 0, g);
+    auto phase = [&](int t, auto sc, auto tail) __attribute__((always_inline)) {
+        constexpr int si = decltype(sc)::value;
+        constexpr bool TAIL = decltype(tail)::value;
+        if constexpr (TAIL)
+            DG_STAGE_BARRIER(0);
+        else
+            DG_STAGE_BARRIER(LOADS);
+        set_a(t + 1, std::integral_constant<int, (si + 1) & 1>{});
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            read((si + 1) % ST, (si + 1) & 1, g);
+            mma(si & 1, g);
+            if constexpr (!TAIL) {
+                load_a(t / 2 + 2, (NAL / 2) * (t & 1), NAL / 2, g, G, 0);
+                load_b(t + ST - 1, g, G, NAL / 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    const int nkt = kr.n;
+    int kt = 0;
+    for (; kt + ST <= nkt; kt += ST) {
+        phase(kt, std::integral_constant<int, 0>{}, std::false_type{});
+        phase(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+        phase(kt + 2, std::integral_constant<int, 2>{}, std::false_type{});
+        phase(kt + 3, std::integral_constant<int, 3>{}, std::false_type{});
+    }
+    // the last nkt % ST phases only ever load k-tiles past K: no loads
+    if (kt < nkt)
+        phase(kt, std::integral_constant<int, 0>{}, std::true_type{});
+    if (kt + 1 < nkt)
+        phase(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    if (kt + 2 < nkt)
+        phase(kt + 2, std::integral_constant<int, 2>{}, std::true_type{});
+    // loads past nkt (zeros) still target LDS: drain them before the epilogue
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+
+    float scale_a = 1.f, scale_b = 1.f;
+    if constexpr (DT == DT_FP8) {
+        scale_a = *p.sa;
+        scale_b = *p.sb;
+    }
+    store_c_tile<DT, AT, MR, NR, CH, SROW, WCOLS, EPI>(p, acc, lds + wave * (CH * R * SROW), m0,
+                                                      rows, n0 + wn * WCOLS, (int)row0, lane,
+                                                      scale_a, scale_b);
+}
+
+// ---------------------------------------------------------------------------
 // A+B kernel with ping-pong wave groups ("PP" kernel).
 //
 // 8 waves in two groups of four; a workgroup's waves are spread round robin

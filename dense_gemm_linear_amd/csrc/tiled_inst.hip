@@ -44,11 +44,24 @@ hipError_t go(const GemmArgs& a, hipStream_t s)
     }
 }
 #else
+// The 4-wave 256 x 256 e4m3 rung with 32 x 32 atoms and four 64-byte stages
+// runs its plain and fused-epilogue launches on the kernel with whole-line A
+// loads (same results bit for bit: the same MFMAs in the same order).
+template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
+constexpr bool ab_line_rung()
+{
+    return DT == DT_FP8 && TM == 256 && TN == 256 && WM == 2 && WN == 2 && ST == 4 && R == 32 &&
+           KTB == 64 && (MODE == MODE_PLAIN || MODE == MODE_EPI);
+}
+
 template <int TM, int TN, int WM, int WN, int ST, int R, int KTB>
 hipError_t go_ab(const GemmArgs& a, hipStream_t s)
 {
     if constexpr ((MODE == MODE_SK && !sk_rung(TM, TN)) || !atom_fits<DT, R, KTB>()) {
         return hipErrorInvalidValue;
+    } else if constexpr (ab_line_rung<TM, TN, WM, WN, ST, R, KTB>()) {
+        return launch_args(&gemm_ab_line_kernel<DT, R, WM, WN, MODE == MODE_EPI>, grid_of(a),
+                           dim3(64 * WM * WN), a, s);
     } else {
         return launch_args(&gemm_ab_kernel<DT, TM, TN, WM, WN, ST, R, KTB, MODE>, grid_of(a),
                            dim3(ABShape<TM, TN, WM, WN, ST, R, KTB>::THREADS), a, s);
