@@ -165,7 +165,8 @@ def test_skinny(tile, act):
             check_epi_close("bf16", C, want, absprod, K, parts, 1.0, tile.name)
 
 
-FP8_TILES = [None, dg.tiled(128, 128, 4, 32), dg.tiled_ab(256, 256, 8, 32), dg.tiled_pp(256, 256),
+FP8_TILES = [None, dg.tiled(128, 128, 4, 32), dg.tiled_ab(256, 256, 8, 32),
+             dg.tiled_ab(256, 256, 4, 32, stages=4, tile_k=64), dg.tiled_pp(256, 256),
              dg.skinny(32, 16), dg.with_split(dg.tiled(64, 64), 2)]
 
 

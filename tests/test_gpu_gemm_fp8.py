@@ -89,6 +89,25 @@ def test_every_ladder_tile_short_k(tile):
             check_exact(C, ref, f"{tile.name} K={K} run {rep}")
 
 
+# The 4-wave 256 x 256 rung with 32 x 32 atoms and four 64-byte stages runs on
+# the kernel that loads A in k-tile pairs of whole 128-byte lines into three
+# pair stages: K counts whose last pair is half full or empty, a main loop
+# followed by 1-3 tail phases, partial row and column tiles, and repeated
+# runs (a stage reused too early shows up as stale data in some runs only).
+@pytest.mark.parametrize("M,N,K", [(300, 520, 448), (513, 264, 576), (256, 256, 1088),
+                                   (40, 300, 832), (257, 512, 64), (100, 300, 192),
+                                   (600, 700, 4160)],
+                         ids=lambda v: str(v))
+def test_whole_line_a_rung(M, N, K):
+    tile = dg.tiled_ab(256, 256, 4, 32, stages=4, tile_k=64)
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=M + N + K, smallint=True)
+    ref = oracle_full("fp8", A, B, 0.5, 2.0)
+    for rep in range(3):
+        C, ok = run("fp8", A, B, tile=tile, sa=0.5, sb=2.0)
+        assert ok, "guard band written"
+        check_exact(C, ref, f"{tile.name} {M}x{N}x{K} run {rep}")
+
+
 @pytest.mark.parametrize("tm,tn,w", dg.SKINNY_LADDER)
 def test_every_skinny_tile(tm, tn, w):
     M, N, K = tm - 3, 270, 320
