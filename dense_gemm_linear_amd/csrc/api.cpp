@@ -459,6 +459,24 @@ gemm_status run_gemm(int dt, const void* A, int64_t lda, const void* Bs, const f
         idx = ap.idx1;
         pl = ap.pl1;
         sk = ap.sk1;
+        // The fused-epilogue instance of the 4-wave e4m3 256 x 256 rung (the
+        // whole-line-A kernel) spills 3 VGPRs: with per-row and per-column
+        // scales on 4096^3 it measured 66-69 us on MI355X against 58-60 us for
+        // the 8-wave rung of the same tile (54-61 us for both without an
+        // epilogue).  A fused launch that the selector puts on it takes the
+        // 8-wave rung.  (Calibrated rung costs are for plain launches.)
+        if (ep.on && dt == DT_FP8 && ap.n1 == N && ap.m1 == M && t.kernel == GEMM_KERNEL_TILED_AB &&
+            t.tile_m == 256 && t.tile_n == 256 && t.waves == 4 && t.atom == 32 &&
+            t.lds_stages == 4 && t.tile_k == 64 && t.k_split <= 1) {
+            gemm_tile t8 = t;
+            t8.waves = 8;
+            int idx8 = -1;
+            if (resolve_tile(t8, M, e, &idx8)) {
+                t = t8;
+                idx = idx8;
+                pl = tile_split(t, idx, M, N, K, e);
+            }
+        }
         if (ap.n1 < N) {
             const int64_t n1 = ap.n1;
             const int64_t be = 64 * ((K * e + 63) / 64) * 16;   // Bs bytes per 16 columns

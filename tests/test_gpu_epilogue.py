@@ -188,6 +188,19 @@ def test_fp8_per_token_and_channel_scales(tile):
     check_epi_close("fp8", C, want, absprod, K, parts, sa * sb, str(tile))
 
 
+def test_fp8_scales_at_4096_cube_auto_plan():
+    """e4m3 4096^3 with per-row and per-column scales and no tile: the plan for
+    a plain launch is the 4-wave 256 x 256 rung, which a fused launch replaces
+    with the 8-wave one.  Every element against the oracle."""
+    M = N = K = 4096
+    assert dg.select_tile(M, N, K, "fp8", 256).name == "ab256x256w4a32s4k64"
+    A, B, _, _ = datagen.make_e4m3_pair(M, N, K, config=36, smallint=True)
+    parts = make_parts(M, N, True, 6, parts=("scale_m", "scale_n"))
+    C, ok = run_epi("fp8", A, B, parts, "none", None, sa=2.0 ** -3, sb=2.0 ** 2)
+    assert ok
+    check_exact(C, oracle_epi("fp8", A, B, parts, "none", 2.0 ** -3, 2.0 ** 2)[1], "auto 4096^3")
+
+
 @pytest.mark.parametrize("tile", [None, dg.tiled_pp(256, 256), dg.with_split(dg.tiled(64, 64), 2),
                                   dg.skinny(32, 16)], ids=lambda t: t.name if t else "auto")
 def test_mul_in_place(tile):
