@@ -440,7 +440,11 @@ gemm_status gemm_bf16_noalloc(const uint16_t* A, int64_t lda, const void* Bs, ui
  * one-pass launch: the one-pass time scaled by tiles / CUs and by 1.45 (a
  * stream-K unit measured that much slower than a one-pass one), plus about
  * 20 us for the fix-up of the cut tiles.  The launch with a fused epilogue
- * (gemm_*_ex with any part set) keeps the one-pass form.
+ * (gemm_*_ex with any part set) keeps the one-pass form.  It also runs on the
+ * 8-wave rung of the same tile when *first would be the 4-wave e4m3
+ * 256 x 256 rung with 32 x 32 atoms and four 64-byte stages, whose fused
+ * instance spills registers (measured on MI355X, e4m3 4096^3 with per-row
+ * and per-column scales: 66-69 us against 58-60 us).
  *
  * GEMM_ERR_INVALID_VALUE for a NULL output, M, N or K <= 0, num_cus <= 0 or
  * an unknown dtype.
